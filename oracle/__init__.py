@@ -1,0 +1,244 @@
+"""CPU oracle for the w8a8 scaled matrix multiply and its quantizers.
+
+TEST INFRASTRUCTURE ONLY: the plain, slow, obviously correct definition the
+HIP library is checked against. Only the tests, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this package. It shares
+no code with the HIP library and never imports it.
+
+The arithmetic lives in ``oracle.c`` (plain C, IEEE, no fast-math); this
+module builds it with gcc and marshals numpy arrays into it. Definitions and
+their sources on the reference pages are in the C file's header:
+
+* "[Kernel] Add w8a8 CUTLASS kernels" (PR description list): the scaled
+  product and its scale granularities; the per_tensor_quantize snippet:
+  divide, clamp to the e4m3 range, cast.
+* "Enable scaled FP8 (e4m3fn) KV cache on ROCm" ("Scaling semantics"):
+  scale = absmax/448, q = fp8(x/scale), x' = dequant(q)*scale.
+
+Parity pins: every function here is pinned in ``tests/test_oracle_*.py``
+against something other than itself (torch's CPU float8 cast, numpy's
+rounding, exact rational brute force, closed forms). None is unpinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+QT_INT8, QT_FP8 = 0, 1
+DT_BF16, DT_FP16, DT_F32, DT_I32 = 0, 1, 2, 3
+QTYPES = {"int8": QT_INT8, "fp8": QT_FP8}
+DTYPES = {"bf16": DT_BF16, "fp16": DT_FP16, "f32": DT_F32, "i32": DT_I32}
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-fno-fast-math", "-ffp-contract=off",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_int8_encode.restype = ctypes.c_int8
+        L.oracle_int8_encode.argtypes = [ctypes.c_float]
+        L.oracle_scale_from_absmax.restype = ctypes.c_float
+        L.oracle_scale_from_absmax.argtypes = [ctypes.c_float, I]
+        for name in ("oracle_e4m3_encode_n", "oracle_int8_encode_n", "oracle_e4m3_decode_n",
+                     "oracle_bf16_from_double_n", "oracle_fp16_from_double_n"):
+            getattr(L, name).restype = None
+            getattr(L, name).argtypes = [P, I64, P]
+        L.oracle_quant_per_token.restype = None
+        L.oracle_quant_per_token.argtypes = [P, I, I64, I64, I64, P, I, I64, P]
+        L.oracle_quant_per_tensor.restype = None
+        L.oracle_quant_per_tensor.argtypes = [P, I, I64, I64, I64, P, I, I64, P, I]
+        L.oracle_kv_quant.restype = None
+        L.oracle_kv_quant.argtypes = [P, I, I64, P, P, I]
+        L.oracle_kv_dequant.restype = None
+        L.oracle_kv_dequant.argtypes = [P, I64, P, P, I]
+        L.oracle_scaled_mm.restype = None
+        L.oracle_scaled_mm.argtypes = [P, I, I64, P, I64, P, I64, I, I64, I64, I64, P, I64, P, I64]
+        L.oracle_scaled_mm_rows.restype = None
+        L.oracle_scaled_mm_rows.argtypes = [P, I, I64, P, I64, P, I64, P, I64, I, I64, I64,
+                                            P, I64, P, I64]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _xtype_of(x: np.ndarray, xtype: str | None) -> int:
+    if x.dtype == np.float32:
+        return DT_F32
+    if x.dtype == np.uint16:
+        if xtype not in ("bf16", "fp16"):
+            raise ValueError("uint16 input needs xtype='bf16' or 'fp16'")
+        return DTYPES[xtype]
+    raise TypeError(f"unsupported input dtype {x.dtype}")
+
+
+# --------------------------------------------------------------------- codecs
+def e4m3_decode(codes) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().oracle_e4m3_decode_n(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def e4m3_encode(v) -> np.ndarray:
+    x = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().oracle_e4m3_encode_n(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def int8_encode(v) -> np.ndarray:
+    x = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(x.shape, np.int8)
+    lib().oracle_int8_encode_n(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def bf16_from_f64(v) -> np.ndarray:
+    x = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_bf16_from_double_n(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def fp16_from_f64(v) -> np.ndarray:
+    x = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_fp16_from_double_n(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def scale_from_absmax(absmax: float, qtype: str) -> np.float32:
+    return np.float32(lib().oracle_scale_from_absmax(float(absmax), QTYPES[qtype]))
+
+
+# ----------------------------------------------------------------- quantizers
+def quant_per_token(x: np.ndarray, qtype: str, xtype: str | None = None):
+    """x [M, K] (uint16 bf16/fp16 bits, or float32) -> (codes uint8 [M, K], scales float32 [M])."""
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    q = np.empty((M, K), np.uint8)
+    s = np.empty(M, np.float32)
+    lib().oracle_quant_per_token(_ptr(x), _xtype_of(x, xtype), M, K, K, _ptr(q),
+                                 QTYPES[qtype], K, _ptr(s))
+    return q, s
+
+
+def quant_per_tensor(x: np.ndarray, qtype: str, scale=None, dynamic: bool = False,
+                     xtype: str | None = None):
+    """Per-tensor quantisation; dynamic computes the scale, else ``scale`` (None = 1.0) is used."""
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    q = np.empty((M, K), np.uint8)
+    s = np.zeros(1, np.float32) if dynamic else (
+        None if scale is None else np.array([scale], np.float32))
+    lib().oracle_quant_per_tensor(_ptr(x), _xtype_of(x, xtype), M, K, K, _ptr(q),
+                                  QTYPES[qtype], K, _ptr(s), 1 if dynamic else 0)
+    return q, (np.float32(s[0]) if s is not None else np.float32(1.0))
+
+
+def kv_quant(x: np.ndarray, scale=None, dynamic: bool = True, xtype: str | None = None):
+    x = np.ascontiguousarray(x).reshape(-1)
+    q = np.empty(x.size, np.uint8)
+    s = np.zeros(1, np.float32) if dynamic else (
+        None if scale is None else np.array([scale], np.float32))
+    lib().oracle_kv_quant(_ptr(x), _xtype_of(x, xtype), x.size, _ptr(q), _ptr(s),
+                          1 if dynamic else 0)
+    return q, (np.float32(s[0]) if s is not None else np.float32(1.0))
+
+
+def kv_dequant(q: np.ndarray, scale, xtype: str = "bf16") -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8).reshape(-1)
+    s = None if scale is None else np.array([scale], np.float32)
+    out = np.empty(q.size, np.float32 if xtype == "f32" else np.uint16)
+    lib().oracle_kv_dequant(_ptr(q), q.size, _ptr(s), _ptr(out), DTYPES[xtype])
+    return out
+
+
+# -------------------------------------------------------------------- the GEMM
+def _scales(s, n):
+    if s is None:
+        return None, 1
+    s = np.ascontiguousarray(np.asarray(s, dtype=np.float32).reshape(-1))
+    if s.size not in (1, n):
+        raise ValueError("scale length must be 1 or the matching dimension")
+    return s, s.size
+
+
+def scaled_mm(a: np.ndarray, b: np.ndarray, qtype: str, a_scales=None, b_scales=None,
+              otype: str = "bf16") -> np.ndarray:
+    """D = a_scale (x) b_scale * (A . B^T) for codes a [M, K], b [N, K] (uint8 views).
+
+    Returns uint16 bit patterns for bf16/fp16, float32 for f32, int32 for i32.
+    """
+    a = np.ascontiguousarray(a).view(np.uint8)
+    b = np.ascontiguousarray(b).view(np.uint8)
+    M, K = a.shape
+    N, K2 = b.shape
+    assert K == K2
+    sa, n_a = _scales(a_scales, M)
+    sb, n_b = _scales(b_scales, N)
+    odt = {"bf16": np.uint16, "fp16": np.uint16, "f32": np.float32, "i32": np.int32}[otype]
+    out = np.empty((M, N), odt)
+    lib().oracle_scaled_mm(_ptr(out), DTYPES[otype], N, _ptr(a), K, _ptr(b), K, QTYPES[qtype],
+                           M, N, K, _ptr(sa), n_a, _ptr(sb), n_b)
+    return out
+
+
+def scaled_mm_rows(rows, a: np.ndarray, b: np.ndarray, qtype: str, a_scales=None,
+                   b_scales=None, otype: str = "bf16") -> np.ndarray:
+    """Rows ``rows`` of scaled_mm(a, b, ...), as an array [len(rows), N]."""
+    a = np.ascontiguousarray(a).view(np.uint8)
+    b = np.ascontiguousarray(b).view(np.uint8)
+    M, K = a.shape
+    N, _ = b.shape
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    assert r.size == 0 or (r.min() >= 0 and r.max() < M)
+    sa, n_a = _scales(a_scales, M)
+    sb, n_b = _scales(b_scales, N)
+    odt = {"bf16": np.uint16, "fp16": np.uint16, "f32": np.float32, "i32": np.int32}[otype]
+    out = np.empty((r.size, N), odt)
+    lib().oracle_scaled_mm_rows(_ptr(out), DTYPES[otype], N, _ptr(r), r.size, _ptr(a), K,
+                                _ptr(b), K, QTYPES[qtype], N, K, _ptr(sa), n_a, _ptr(sb), n_b)
+    return out
+
+
+def bf16_bits_to_f64(h) -> np.ndarray:
+    """Exact value of bf16 bit patterns (a shift into the fp32 encoding)."""
+    h = np.asarray(h, dtype=np.uint16)
+    return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def fp16_bits_to_f64(h) -> np.ndarray:
+    return np.asarray(h, dtype=np.uint16).view(np.float16).astype(np.float64)
