@@ -1,0 +1,163 @@
+/*
+ * w8a8.h -- C ABI of libw8a8: the w8a8 scaled matrix multiply for MI355X
+ * (gfx950) and the quantizers that feed it.
+ *
+ * Definitions come from the reference pages:
+ *  [P1] "[Kernel] Add w8a8 CUTLASS kernels" (vLLM issue/PR 4749): the
+ *       PR description's bullet list (symmetric int8 / fp8 e4m3 operands,
+ *       per-tensor or per-token activation scales, per-tensor or
+ *       per-output-channel weight scales, bf16 or fp16 output); the
+ *       misaligned-address report (B must be column-major, the
+ *       per_tensor_quantize recipe: divide, clamp, cast); the review
+ *       comments (check dims and layout, never crash on bad input,
+ *       submatrices with leading-dimension strides are allowed, the op must
+ *       work under graph capture).
+ *  [P2] "[Kernel] Support Fp8 Checkpoints (Dynamic + Static)" (vLLM PR
+ *       4332): static (calibrated) and dynamic activation scales.
+ *  [P3] "Enable scaled FP8 (e4m3fn) KV cache on ROCm" (vLLM issue 3290),
+ *       "Scaling semantics": scale = absmax / 448, q = fp8(x / scale),
+ *       x' = fp8_dequant(q) * scale; and its review answers: no scale means
+ *       scale 1.0.
+ *
+ * Conventions shared by every call
+ *  - All data pointers are DEVICE pointers on the current HIP device; scale
+ *    arrays are device float32 arrays. The caller owns and allocates every
+ *    buffer. The library never allocates, frees or synchronises, and keeps no
+ *    global state, so each call can be captured into a HIP graph. Work is
+ *    enqueued on `stream` (0 = the null stream) and runs asynchronously.
+ *  - Inputs are validated on the host from the arguments alone (device data
+ *    is never read). A bad argument returns an error status and never aborts
+ *    the process; w8a8_last_error() then holds a message (per thread).
+ *    Faults inside a kernel surface asynchronously, at a later HIP call.
+ *  - Matrices are row-major with a leading dimension (row stride, in
+ *    elements) >= the row length, so submatrices are accepted. Rows must be
+ *    16-byte aligned: data pointers 16-byte aligned, K and every leading
+ *    dimension a multiple of 16 (W8A8_ERR_ALIGNMENT otherwise).
+ *  - e4m3fn is the OCP fp8 E4M3 format (max 448, no infinities, 0x7F/0xFF
+ *    NaN). Quantisation is q = enc(x / s) with an IEEE binary32 division and
+ *    round-to-nearest-even; fp8 saturates at +-448 (NaN -> 0x7F), int8 is
+ *    symmetric, clamp(round_half_even(.), -127, 127) (NaN -> 0).
+ *  - A dynamic scale is absmax / Qmax with Qmax = 448 (fp8) or 127 (int8),
+ *    computed in binary32; an all-zero group gets scale 1.0.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum w8a8_status {
+    W8A8_OK = 0,
+    W8A8_ERR_INVALID_ARG = 1, /* NULL pointer, bad flag, scales where none are allowed */
+    W8A8_ERR_SHAPE = 2,       /* negative or incompatible sizes, bad scale length */
+    W8A8_ERR_LAYOUT = 3,      /* leading dimension smaller than the row (e.g. B not column-major) */
+    W8A8_ERR_ALIGNMENT = 4,   /* pointer, K or leading dimension not 16-byte aligned */
+    W8A8_ERR_DTYPE = 5,       /* unknown or unsupported element type combination */
+    W8A8_ERR_UNSUPPORTED = 6, /* valid request outside what the kernels handle (e.g. int8 K > 131072) */
+    W8A8_ERR_HIP = 7          /* a HIP runtime call (launch) failed */
+} w8a8_status;
+
+/* 8-bit code type of quantised operands. */
+typedef enum w8a8_qtype {
+    W8A8_Q_INT8 = 0,        /* symmetric int8, codes -127..127 */
+    W8A8_Q_FP8_E4M3FN = 1   /* OCP fp8 E4M3 */
+} w8a8_qtype;
+
+/* Element type of high-precision tensors (inputs of quantizers, outputs). */
+typedef enum w8a8_dtype {
+    W8A8_BF16 = 0,
+    W8A8_FP16 = 1,
+    W8A8_F32 = 2,   /* float32 */
+    W8A8_I32 = 3    /* int32: raw int8 accumulator output of w8a8_scaled_mm only */
+} w8a8_dtype;
+
+/*
+ * Dynamic per-token quantisation [P1 bullet list: per-token activations;
+ * P2: dynamic activation scales; scale rule of P3 "Scaling semantics"].
+ * For each row m of x [M, K] (row stride ldx elements, type xt in
+ * BF16/FP16/F32): scales[m] = absmax(x[m, :]) / Qmax (1.0 if the row is all
+ * zeros), q[m, k] = enc(x[m, k] / scales[m]) with row stride ldq bytes.
+ * Run on a weight [N, K] it gives per-output-channel weight quantisation.
+ * q: device, M*ldq bytes. scales: device float32 [M], written.
+ * M == 0 is a no-op. K == 0 writes scales of 1.0.
+ */
+w8a8_status w8a8_quant_per_token(const void* x, w8a8_dtype xt, int64_t M, int64_t K, int64_t ldx,
+                                 void* q, w8a8_qtype qt, int64_t ldq, float* scales,
+                                 hipStream_t stream);
+
+/*
+ * Per-tensor quantisation [P1 per_tensor_quantize recipe; P2 static
+ * act_scale and dynamic per-tensor scaling; P3 scale rule].
+ * dynamic == 0 (static, calibrated): s = *scale (scale == NULL means 1.0,
+ *   the pages' default); *scale is not written.
+ * dynamic == 1: s = absmax(x) / Qmax is computed and written to *scale
+ *   (scale must not be NULL). This takes four short kernels on `stream`;
+ *   *scale holds intermediate values until the last one ends.
+ * q[m, k] = enc(x[m, k] / s), row strides ldx (elements) and ldq (bytes).
+ */
+w8a8_status w8a8_quant_per_tensor(const void* x, w8a8_dtype xt, int64_t M, int64_t K, int64_t ldx,
+                                  void* q, w8a8_qtype qt, int64_t ldq, float* scale, int dynamic,
+                                  hipStream_t stream);
+
+/*
+ * The scaled matrix multiply [P1: cutlass_scaled_mm_dq, its bullet list and
+ * the layout rule from the misaligned-address report]:
+ *   D[m, n] = a_scale[m or 0] * b_scale[n or 0] * sum_k A[m, k] * B[k, n]
+ * A: codes [M, K] row-major, row stride lda bytes.
+ * B: codes K x N COLUMN-major, i.e. the bytes of a row-major [N, K] weight
+ *    (row n = output channel n), column stride ldb bytes (ldb >= K; a
+ *    smaller ldb means B is not column-major: W8A8_ERR_LAYOUT).
+ * A and B share the code type qt. Accumulation is int32 (exact) for int8 and
+ * float32 for fp8.
+ * a_scales: device float32, n_a == 1 (per tensor) or n_a == M (per token).
+ * b_scales: device float32, n_b == 1 (per tensor) or n_b == N (per channel).
+ * A NULL scale array means 1.0 (n_a / n_b are then ignored).
+ * out: [M, N] row-major, row stride ldo elements, type ot:
+ *   BF16 / FP16: the scaled result, rounded to nearest even;
+ *   F32: the scaled result in float32;
+ *   I32: the raw int32 accumulator (int8 only; both scale arrays must be NULL).
+ * M == 0 or N == 0 is a no-op; K == 0 writes zeros.
+ */
+w8a8_status w8a8_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* a, int64_t lda,
+                           const void* b, int64_t ldb, w8a8_qtype qt, int64_t M, int64_t N,
+                           int64_t K, const float* a_scales, int64_t n_a, const float* b_scales,
+                           int64_t n_b, hipStream_t stream);
+
+/*
+ * Scaled fp8 KV-cache quantisation of one flat, contiguous tensor of n
+ * elements (e.g. one layer's K or V cache) [P3 "Scaling semantics": per
+ * tensor scale = absmax / 448, q = fp8(x / scale)].
+ * dynamic == 1: *scale = absmax / 448 is computed and written (as in
+ * w8a8_quant_per_tensor). dynamic == 0: the given *scale is used (NULL: 1.0).
+ * q: device, n bytes of e4m3fn codes. n must be a multiple of 16.
+ */
+w8a8_status kv_fp8_scaled_quant(const void* x, w8a8_dtype xt, int64_t n, uint8_t* q, float* scale,
+                                int dynamic, hipStream_t stream);
+
+/*
+ * Scaled fp8 KV-cache dequantisation [P3: x' = fp8_dequant(q) * scale]:
+ * x[i] = round(e4m3_value(q[i]) * s) with the product in float32, then
+ * rounded to nearest even into xt (BF16/FP16/F32). s = *scale, NULL: 1.0.
+ * n must be a multiple of 16.
+ */
+w8a8_status kv_fp8_scaled_dequant(const uint8_t* q, int64_t n, const float* scale, void* x,
+                                  w8a8_dtype xt, hipStream_t stream);
+
+/* Name of a status code (static string). */
+const char* w8a8_status_string(w8a8_status s);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* w8a8_last_error(void);
+
+/* Library version string. */
+const char* w8a8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

@@ -1,0 +1,251 @@
+"""Python binding of libw8a8, the MI355X (gfx950) w8a8 scaled-GEMM library.
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libw8a8.so`` through its C ABI (``include/w8a8.h``). PyTorch supplies
+device memory and the current stream. There is no fallback: without the
+built library every call raises.
+
+Functions carry the C names:
+
+* ``w8a8_quant_per_token(x, qtype)`` -> ``(q, scales)``
+* ``w8a8_quant_per_tensor(x, qtype, scale=None, dynamic=False)`` -> ``(q, scale)``
+* ``w8a8_scaled_mm(a, b, a_scales, b_scales, out_dtype)`` -> ``out``
+* ``kv_fp8_scaled_quant(x, scale=None, dynamic=True)`` -> ``(q, scale)``
+* ``kv_fp8_scaled_dequant(q, scale, out_dtype)`` -> ``x``
+
+plus ``scaled_mm(a, b, scale_a, scale_b, out_dtype)``, the call shape of
+``cutlass_scaled_mm_dq`` in "[Kernel] Add w8a8 CUTLASS kernels" (the usage
+snippet of its misaligned-address report), where ``b`` is a K x N
+column-major view such as ``weight.t()``.
+
+Codes are torch.int8 (int8) or torch.float8_e4m3fn (fp8) tensors; scales are
+float32 device tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw8a8.so")
+
+# Enum values of include/w8a8.h.
+W8A8_OK = 0
+STATUS_NAMES = {0: "W8A8_OK", 1: "W8A8_ERR_INVALID_ARG", 2: "W8A8_ERR_SHAPE",
+                3: "W8A8_ERR_LAYOUT", 4: "W8A8_ERR_ALIGNMENT", 5: "W8A8_ERR_DTYPE",
+                6: "W8A8_ERR_UNSUPPORTED", 7: "W8A8_ERR_HIP"}
+Q_INT8, Q_FP8 = 0, 1
+D_BF16, D_FP16, D_F32, D_I32 = 0, 1, 2, 3
+
+QTYPE_OF = {"int8": Q_INT8, "fp8": Q_FP8, torch.int8: Q_INT8, torch.float8_e4m3fn: Q_FP8}
+CODE_DTYPE = {Q_INT8: torch.int8, Q_FP8: torch.float8_e4m3fn}
+DTYPE_OF = {torch.bfloat16: D_BF16, torch.float16: D_FP16, torch.float32: D_F32,
+            torch.int32: D_I32}
+
+# C ABI signatures (name -> argtypes); every function returns w8a8_status.
+_P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+SIGNATURES = {
+    "w8a8_quant_per_token": [_P, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _P],
+    "w8a8_quant_per_tensor": [_P, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _I, _P],
+    "w8a8_scaled_mm": [_P, _I, _I64, _P, _I64, _P, _I64, _I, _I64, _I64, _I64, _P, _I64, _P,
+                       _I64, _P],
+    "kv_fp8_scaled_quant": [_P, _I, _I64, _P, _P, _I, _P],
+    "kv_fp8_scaled_dequant": [_P, _I64, _P, _P, _I, _P],
+}
+
+
+class W8A8Error(RuntimeError):
+    """A libw8a8 call returned an error status."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        self.status = status
+        self.status_name = STATUS_NAMES.get(status, str(status))
+        super().__init__(f"{fn}: {self.status_name}: {message}")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libw8a8.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libw8a8 is not built ({path} missing): run "
+                          f"`python -m int8_scaled_gemm_amd.build` first")
+    lib = ctypes.CDLL(path)
+    for name, argtypes in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = ctypes.c_int
+    lib.w8a8_status_string.argtypes = [ctypes.c_int]
+    lib.w8a8_status_string.restype = ctypes.c_char_p
+    lib.w8a8_last_error.argtypes = []
+    lib.w8a8_last_error.restype = ctypes.c_char_p
+    lib.w8a8_version.argtypes = []
+    lib.w8a8_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _call(name: str, *args) -> None:
+    lib = load_library()
+    st = getattr(lib, name)(*args)
+    if st != W8A8_OK:
+        raise W8A8Error(name, st, lib.w8a8_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libw8a8 operates on GPU tensors only")
+
+
+def _rows(t: torch.Tensor, what: str):
+    """(rows, cols, leading dimension) of a 2-D tensor with unit column stride."""
+    if t.dim() != 2:
+        raise ValueError(f"{what} must be 2-D, got shape {tuple(t.shape)}")
+    if t.size(1) > 1 and t.stride(1) != 1:
+        raise ValueError(f"{what} must have unit stride along its last dimension")
+    ld = t.stride(0) if t.size(0) > 1 else max(t.size(1), t.stride(0))
+    return t.size(0), t.size(1), ld
+
+
+def _qtype(qtype) -> int:
+    try:
+        return QTYPE_OF[qtype]
+    except KeyError:
+        raise ValueError(f"qtype must be 'int8' or 'fp8', got {qtype!r}") from None
+
+
+def _dtype(dt) -> int:
+    try:
+        return DTYPE_OF[dt]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {dt}") from None
+
+
+# ------------------------------------------------------------------ quantizers
+def w8a8_quant_per_token(x: torch.Tensor, qtype="fp8", q: torch.Tensor | None = None,
+                         scales: torch.Tensor | None = None):
+    """Dynamic per-token quantisation of x [M, K] -> (codes [M, K], scales fp32 [M])."""
+    _check_cuda(x, q, scales)
+    qt = _qtype(qtype)
+    M, K, ldx = _rows(x, "x")
+    if q is None:
+        q = torch.empty((M, K), dtype=CODE_DTYPE[qt], device=x.device)
+    if scales is None:
+        scales = torch.empty(M, dtype=torch.float32, device=x.device)
+    _, _, ldq = _rows(q, "q")
+    _call("w8a8_quant_per_token", _ptr(x), _dtype(x.dtype), M, K, ldx, _ptr(q), qt, ldq,
+          _ptr(scales), _stream(x))
+    return q, scales
+
+
+def w8a8_quant_per_tensor(x: torch.Tensor, qtype="fp8", scale: torch.Tensor | None = None,
+                          dynamic: bool = False, q: torch.Tensor | None = None):
+    """Per-tensor quantisation. Static (dynamic=False) uses ``scale`` (None means 1.0);
+    dynamic computes absmax/Qmax into ``scale`` (allocated when None)."""
+    _check_cuda(x, q, scale)
+    qt = _qtype(qtype)
+    M, K, ldx = _rows(x, "x")
+    if q is None:
+        q = torch.empty((M, K), dtype=CODE_DTYPE[qt], device=x.device)
+    if dynamic and scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _, _, ldq = _rows(q, "q")
+    _call("w8a8_quant_per_tensor", _ptr(x), _dtype(x.dtype), M, K, ldx, _ptr(q), qt, ldq,
+          _ptr(scale), 1 if dynamic else 0, _stream(x))
+    return q, scale
+
+
+def kv_fp8_scaled_quant(x: torch.Tensor, scale: torch.Tensor | None = None,
+                        dynamic: bool = True, q: torch.Tensor | None = None):
+    """Scaled fp8 KV-cache quantisation of a contiguous tensor (any shape)."""
+    _check_cuda(x, q, scale)
+    if not x.is_contiguous():
+        raise ValueError("kv_fp8_scaled_quant needs a contiguous tensor")
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    if dynamic and scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _call("kv_fp8_scaled_quant", _ptr(x), _dtype(x.dtype), x.numel(), _ptr(q), _ptr(scale),
+          1 if dynamic else 0, _stream(x))
+    return q, scale
+
+
+def kv_fp8_scaled_dequant(q: torch.Tensor, scale: torch.Tensor | None,
+                          out_dtype=torch.bfloat16, out: torch.Tensor | None = None):
+    """x' = dequant(q) * scale, rounded into out_dtype."""
+    _check_cuda(q, scale, out)
+    if not q.is_contiguous():
+        raise ValueError("kv_fp8_scaled_dequant needs a contiguous tensor")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _call("kv_fp8_scaled_dequant", _ptr(q), q.numel(), _ptr(scale), _ptr(out),
+          _dtype(out.dtype), _stream(q))
+    return out
+
+
+# ---------------------------------------------------------------------- GEMM
+def w8a8_scaled_mm(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | None,
+                   b_scales: torch.Tensor | None, out_dtype=torch.bfloat16,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """D = a_scales (x) b_scales * (a @ b).
+
+    a: codes [M, K] with unit column stride. b: codes K x N, COLUMN-major
+    (b.stride(0) == 1), e.g. ``weight.t()`` for a row-major [N, K] weight.
+    a_scales: fp32 [1] or [M] (or [M, 1]); b_scales: fp32 [1] or [N] (or [1, N]).
+    None means 1.0. out_dtype: bfloat16, float16, float32, or int32 (the raw
+    int8 accumulator, scales must be None).
+    """
+    _check_cuda(a, b, a_scales, b_scales, out)
+    qt = _qtype(a.dtype)
+    if b.dtype != a.dtype:
+        raise ValueError(f"a and b must share a code type, got {a.dtype} and {b.dtype}")
+    M, K, lda = _rows(a, "a")
+    if b.dim() != 2 or b.size(0) != K:
+        raise ValueError(f"b must be K x N with K={K}, got shape {tuple(b.shape)}")
+    N = b.size(1)
+    if b.size(0) > 1 and b.stride(0) != 1:
+        raise ValueError("b must be column-major (K x N with stride(0) == 1), e.g. weight.t()")
+    ldb = b.stride(1) if N > 1 else max(K, b.stride(1))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _, _, ldo = _rows(out, "out")
+    sa = None if a_scales is None else a_scales.reshape(-1)
+    sb = None if b_scales is None else b_scales.reshape(-1)
+    for s, what in ((sa, "a_scales"), (sb, "b_scales")):
+        if s is not None and (s.dtype != torch.float32 or not s.is_contiguous()):
+            raise ValueError(f"{what} must be a contiguous float32 tensor")
+    _call("w8a8_scaled_mm", _ptr(out), _dtype(out.dtype), ldo, _ptr(a), lda, _ptr(b), ldb, qt,
+          M, N, K, _ptr(sa), 0 if sa is None else sa.numel(), _ptr(sb),
+          0 if sb is None else sb.numel(), _stream(a))
+    return out
+
+
+def scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor | None,
+              scale_b: torch.Tensor | None, out_dtype=torch.bfloat16,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """The cutlass_scaled_mm_dq call shape: a [M, K], b K x N column-major."""
+    return w8a8_scaled_mm(a, b, scale_a, scale_b, out_dtype, out)
+
+
+def version() -> str:
+    return load_library().w8a8_version().decode()
+
+
+__all__ = ["w8a8_quant_per_token", "w8a8_quant_per_tensor", "w8a8_scaled_mm",
+           "kv_fp8_scaled_quant", "kv_fp8_scaled_dequant", "scaled_mm", "W8A8Error",
+           "load_library", "version", "LIB_PATH", "SIGNATURES"]

@@ -1,0 +1,197 @@
+// api.cpp -- the C ABI of libw8a8 (declared in include/w8a8.h).
+//
+// Every argument is checked here, on the host, before anything is enqueued:
+// a bad call returns a status and a per-thread message and never aborts
+// (the review of "[Kernel] Add w8a8 CUTLASS kernels" asks that input
+// validation never crash the caller and that dims and layout be checked,
+// e.g. a B that is not column-major, the cause of its misaligned-address
+// report). Nothing here allocates, frees or synchronises, so the calls can
+// be captured into a HIP graph (the graph-capture failure reported on the
+// same page).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/w8a8.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+w8a8_status fail(w8a8_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+w8a8_status ok() {
+    g_msg[0] = '\0';
+    return W8A8_OK;
+}
+
+w8a8_status from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(W8A8_ERR_HIP, "%s: HIP error %d (%s)", what, static_cast<int>(e), hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(w8a8_dtype t) { return t == W8A8_BF16 || t == W8A8_FP16 ? 2 : 4; }
+
+bool valid_qtype(w8a8_qtype q) { return q == W8A8_Q_INT8 || q == W8A8_Q_FP8_E4M3FN; }
+
+bool valid_in_dtype(w8a8_dtype t) { return t == W8A8_BF16 || t == W8A8_FP16 || t == W8A8_F32; }
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+
+// Shared checks of an [M, K] high-precision input and its [M, K] codes.
+w8a8_status check_quant_io(const char* fn, const void* x, w8a8_dtype xt, int64_t M, int64_t K,
+                           int64_t ldx, const void* q, w8a8_qtype qt, int64_t ldq) {
+    if (!valid_in_dtype(xt)) return fail(W8A8_ERR_DTYPE, "%s: input type %d is not BF16, FP16 or F32", fn, xt);
+    if (!valid_qtype(qt)) return fail(W8A8_ERR_DTYPE, "%s: code type %d is not INT8 or FP8_E4M3FN", fn, qt);
+    if (M < 0 || K < 0) return fail(W8A8_ERR_SHAPE, "%s: negative size M=%lld K=%lld", fn, (long long)M, (long long)K);
+    if (M > kMaxDim || K > kMaxDim) return fail(W8A8_ERR_UNSUPPORTED, "%s: M or K above 2^31-1", fn);
+    if (ldx < K || ldq < K) return fail(W8A8_ERR_LAYOUT, "%s: leading dimensions ldx=%lld ldq=%lld must be >= K=%lld", fn, (long long)ldx, (long long)ldq, (long long)K);
+    if (M == 0 || K == 0) return W8A8_OK;  // no element is read or written
+    if (K % 16 || ldx % 16 || ldq % 16)
+        return fail(W8A8_ERR_ALIGNMENT, "%s: K, ldx and ldq must be multiples of 16 (K=%lld ldx=%lld ldq=%lld)", fn, (long long)K, (long long)ldx, (long long)ldq);
+    if (!x || !q) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL x or q", fn);
+    if (!aligned16(x) || !aligned16(q)) return fail(W8A8_ERR_ALIGNMENT, "%s: x and q must be 16-byte aligned", fn);
+    if (xt == W8A8_F32 && (reinterpret_cast<uintptr_t>(x) & 31u))
+        return fail(W8A8_ERR_ALIGNMENT, "%s: float32 input must be 32-byte aligned", fn);
+    const uint64_t units = static_cast<uint64_t>(M) * static_cast<uint64_t>((K + 2047) / 2048);
+    if (units >= (uint64_t{1} << 31)) return fail(W8A8_ERR_UNSUPPORTED, "%s: tensor too large", fn);
+    return W8A8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w8a8_version(void) { return "libw8a8 0.1 (gfx950)"; }
+
+const char* w8a8_last_error(void) { return g_msg; }
+
+const char* w8a8_status_string(w8a8_status s) {
+    switch (s) {
+        case W8A8_OK: return "W8A8_OK";
+        case W8A8_ERR_INVALID_ARG: return "W8A8_ERR_INVALID_ARG";
+        case W8A8_ERR_SHAPE: return "W8A8_ERR_SHAPE";
+        case W8A8_ERR_LAYOUT: return "W8A8_ERR_LAYOUT";
+        case W8A8_ERR_ALIGNMENT: return "W8A8_ERR_ALIGNMENT";
+        case W8A8_ERR_DTYPE: return "W8A8_ERR_DTYPE";
+        case W8A8_ERR_UNSUPPORTED: return "W8A8_ERR_UNSUPPORTED";
+        case W8A8_ERR_HIP: return "W8A8_ERR_HIP";
+    }
+    return "W8A8_UNKNOWN_STATUS";
+}
+
+w8a8_status w8a8_quant_per_token(const void* x, w8a8_dtype xt, int64_t M, int64_t K, int64_t ldx,
+                                 void* q, w8a8_qtype qt, int64_t ldq, float* scales,
+                                 hipStream_t stream) {
+    const char* fn = "w8a8_quant_per_token";
+    w8a8_status s = check_quant_io(fn, x, xt, M, K, ldx, q, qt, ldq);
+    if (s != W8A8_OK) return s;
+    if (M == 0) return ok();
+    if (!scales) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL scales", fn);
+    if (reinterpret_cast<uintptr_t>(scales) & 3u) return fail(W8A8_ERR_ALIGNMENT, "%s: scales must be 4-byte aligned", fn);
+    return from_hip(w8a8::launch_quant_per_token(xt, x, M, K, ldx, static_cast<uint8_t*>(q), qt, ldq, scales, stream), fn);
+}
+
+w8a8_status w8a8_quant_per_tensor(const void* x, w8a8_dtype xt, int64_t M, int64_t K, int64_t ldx,
+                                  void* q, w8a8_qtype qt, int64_t ldq, float* scale, int dynamic,
+                                  hipStream_t stream) {
+    const char* fn = "w8a8_quant_per_tensor";
+    if (dynamic != 0 && dynamic != 1) return fail(W8A8_ERR_INVALID_ARG, "%s: dynamic must be 0 or 1", fn);
+    w8a8_status s = check_quant_io(fn, x, xt, M, K, ldx, q, qt, ldq);
+    if (s != W8A8_OK) return s;
+    if (dynamic && !scale) return fail(W8A8_ERR_INVALID_ARG, "%s: dynamic scaling needs a scale buffer", fn);
+    if (scale && (reinterpret_cast<uintptr_t>(scale) & 3u)) return fail(W8A8_ERR_ALIGNMENT, "%s: scale must be 4-byte aligned", fn);
+    if (M == 0 && !dynamic) return ok();
+    return from_hip(w8a8::launch_quant_per_tensor(xt, x, M, K, ldx, static_cast<uint8_t*>(q), qt, ldq, scale, dynamic != 0, stream), fn);
+}
+
+w8a8_status w8a8_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* a, int64_t lda,
+                           const void* b, int64_t ldb, w8a8_qtype qt, int64_t M, int64_t N,
+                           int64_t K, const float* a_scales, int64_t n_a, const float* b_scales,
+                           int64_t n_b, hipStream_t stream) {
+    const char* fn = "w8a8_scaled_mm";
+    if (!valid_qtype(qt)) return fail(W8A8_ERR_DTYPE, "%s: code type %d is not INT8 or FP8_E4M3FN", fn, qt);
+    if (ot != W8A8_BF16 && ot != W8A8_FP16 && ot != W8A8_F32 && ot != W8A8_I32)
+        return fail(W8A8_ERR_DTYPE, "%s: output type %d unknown", fn, ot);
+    if (ot == W8A8_I32 && qt != W8A8_Q_INT8)
+        return fail(W8A8_ERR_DTYPE, "%s: I32 output (raw accumulator) exists for int8 only", fn);
+    if (ot == W8A8_I32 && (a_scales || b_scales))
+        return fail(W8A8_ERR_INVALID_ARG, "%s: I32 output is the raw accumulator; scales must be NULL", fn);
+    if (M < 0 || N < 0 || K < 0)
+        return fail(W8A8_ERR_SHAPE, "%s: negative size M=%lld N=%lld K=%lld", fn, (long long)M, (long long)N, (long long)K);
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(W8A8_ERR_UNSUPPORTED, "%s: a size is above 2^31-1", fn);
+    if (lda < K) return fail(W8A8_ERR_LAYOUT, "%s: lda=%lld < K=%lld", fn, (long long)lda, (long long)K);
+    if (ldb < K)
+        return fail(W8A8_ERR_LAYOUT, "%s: ldb=%lld < K=%lld: B must be K x N column-major (rows of an [N, K] weight)", fn, (long long)ldb, (long long)K);
+    if (ldo < N) return fail(W8A8_ERR_LAYOUT, "%s: ldo=%lld < N=%lld", fn, (long long)ldo, (long long)N);
+    if (a_scales && n_a != 1 && n_a != M)
+        return fail(W8A8_ERR_SHAPE, "%s: a_scales has %lld entries; need 1 (per tensor) or M=%lld (per token)", fn, (long long)n_a, (long long)M);
+    if (b_scales && n_b != 1 && n_b != N)
+        return fail(W8A8_ERR_SHAPE, "%s: b_scales has %lld entries; need 1 (per tensor) or N=%lld (per channel)", fn, (long long)n_b, (long long)N);
+    if (qt == W8A8_Q_INT8 && K > 131072)
+        return fail(W8A8_ERR_UNSUPPORTED, "%s: int8 K=%lld could overflow the int32 accumulator (max 131072)", fn, (long long)K);
+    if (M == 0 || N == 0) return ok();
+    if (!out) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL out", fn);
+    if (K > 0 && (!a || !b)) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL a or b", fn);
+    if (K % 16 || (K > 0 && (lda % 16 || ldb % 16)))
+        return fail(W8A8_ERR_ALIGNMENT, "%s: K, lda and ldb must be multiples of 16 (K=%lld lda=%lld ldb=%lld)", fn, (long long)K, (long long)lda, (long long)ldb);
+    if ((a && !aligned16(a)) || (b && !aligned16(b))) return fail(W8A8_ERR_ALIGNMENT, "%s: a and b must be 16-byte aligned", fn);
+    if (reinterpret_cast<uintptr_t>(out) % elem_size(ot)) return fail(W8A8_ERR_ALIGNMENT, "%s: out is not aligned to its element size", fn);
+    if ((a_scales && (reinterpret_cast<uintptr_t>(a_scales) & 3u)) || (b_scales && (reinterpret_cast<uintptr_t>(b_scales) & 3u)))
+        return fail(W8A8_ERR_ALIGNMENT, "%s: scale arrays must be 4-byte aligned", fn);
+    w8a8::GemmProblem p;
+    p.out = out;
+    p.ot = ot;
+    p.ldo = ldo;
+    p.a = static_cast<const uint8_t*>(a);
+    p.lda = lda;
+    p.b = static_cast<const uint8_t*>(b);
+    p.ldb = ldb;
+    p.qt = qt;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.sa = a_scales;
+    p.sa_per_row = a_scales && n_a == M && M != 1;
+    p.sb = b_scales;
+    p.sb_per_col = b_scales && n_b == N && N != 1;
+    return from_hip(w8a8::launch_scaled_mm(p, stream), fn);
+}
+
+w8a8_status kv_fp8_scaled_quant(const void* x, w8a8_dtype xt, int64_t n, uint8_t* q, float* scale,
+                                int dynamic, hipStream_t stream) {
+    const char* fn = "kv_fp8_scaled_quant";
+    if (dynamic != 0 && dynamic != 1) return fail(W8A8_ERR_INVALID_ARG, "%s: dynamic must be 0 or 1", fn);
+    if (n < 0) return fail(W8A8_ERR_SHAPE, "%s: negative n", fn);
+    if (n % 16) return fail(W8A8_ERR_ALIGNMENT, "%s: n=%lld must be a multiple of 16", fn, (long long)n);
+    // A flat tensor is one row of n elements.
+    w8a8_status s = check_quant_io(fn, x, xt, n > 0 ? 1 : 0, n, n, q, W8A8_Q_FP8_E4M3FN, n);
+    if (s != W8A8_OK) return s;
+    if (dynamic && !scale) return fail(W8A8_ERR_INVALID_ARG, "%s: dynamic scaling needs a scale buffer", fn);
+    if (scale && (reinterpret_cast<uintptr_t>(scale) & 3u)) return fail(W8A8_ERR_ALIGNMENT, "%s: scale must be 4-byte aligned", fn);
+    if (n == 0 && !dynamic) return ok();
+    return from_hip(w8a8::launch_quant_per_tensor(xt, x, n > 0 ? 1 : 0, n, n, q, W8A8_Q_FP8_E4M3FN, n, scale, dynamic != 0, stream), fn);
+}
+
+w8a8_status kv_fp8_scaled_dequant(const uint8_t* q, int64_t n, const float* scale, void* x,
+                                  w8a8_dtype xt, hipStream_t stream) {
+    const char* fn = "kv_fp8_scaled_dequant";
+    if (!valid_in_dtype(xt)) return fail(W8A8_ERR_DTYPE, "%s: output type %d is not BF16, FP16 or F32", fn, xt);
+    if (n < 0) return fail(W8A8_ERR_SHAPE, "%s: negative n", fn);
+    if (n % 16) return fail(W8A8_ERR_ALIGNMENT, "%s: n=%lld must be a multiple of 16", fn, (long long)n);
+    if (n == 0) return ok();
+    if (!q || !x) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL q or x", fn);
+    if (!aligned16(q) || !aligned16(x)) return fail(W8A8_ERR_ALIGNMENT, "%s: q and x must be 16-byte aligned", fn);
+    if (scale && (reinterpret_cast<uintptr_t>(scale) & 3u)) return fail(W8A8_ERR_ALIGNMENT, "%s: scale must be 4-byte aligned", fn);
+    return from_hip(w8a8::launch_kv_dequant(q, n, scale, x, xt, stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// launch.hpp -- host-side launchers of the libw8a8 kernels. Arguments are
+// validated by the C ABI layer (api.cpp) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+hipError_t launch_quant_per_token(int xt, const void* x, int64_t M, int64_t K, int64_t ldx,
+                                  uint8_t* q, int qt, int64_t ldq, float* scales, hipStream_t st);
+
+hipError_t launch_quant_per_tensor(int xt, const void* x, int64_t M, int64_t K, int64_t ldx,
+                                   uint8_t* q, int qt, int64_t ldq, float* scale, bool dynamic,
+                                   hipStream_t st);
+
+hipError_t launch_kv_dequant(const uint8_t* q, int64_t n, const float* scale, void* x, int xt,
+                             hipStream_t st);
+
+struct GemmProblem {
+    void* out;
+    int ot;
+    int64_t ldo;
+    const uint8_t* a;
+    int64_t lda;
+    const uint8_t* b;
+    int64_t ldb;
+    int qt;
+    int64_t M, N, K;
+    const float* sa;  // NULL: 1.0
+    bool sa_per_row;
+    const float* sb;  // NULL: 1.0
+    bool sb_per_col;
+};
+
+hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st);
+
+}  // namespace w8a8

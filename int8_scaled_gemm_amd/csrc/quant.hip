@@ -1,0 +1,361 @@
+// quant.hip -- the quantizers that feed the scaled matrix multiply, and the
+// scaled fp8 KV-cache quant/dequant, for gfx950.
+//
+// Definitions: "Enable scaled FP8 (e4m3fn) KV cache on ROCm", "Scaling
+// semantics" (scale = absmax / 448, q = fp8(x / scale), x' = dequant(q) *
+// scale); "[Kernel] Add w8a8 CUTLASS kernels", per_tensor_quantize snippet
+// (divide, clamp to the e4m3 range, cast) and the PR's list of scale
+// granularities (per token, per tensor); "[Kernel] Support Fp8 Checkpoints
+// (Dynamic + Static)" (static calibrated vs dynamic activation scales).
+//
+// All of these are HBM-bound streams: 2 bytes in and 1 byte out per element
+// (bf16 -> code), plus a 2-byte read pass for a dynamic per-tensor scale.
+// Loads and stores are 16-byte vectors per lane; a row's absmax is reduced
+// across the wavefront with lane shuffles, and across waves through LDS.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace w8a8 {
+
+namespace {
+
+constexpr int kBlock = 256;
+
+// ------------------------------------------------------------------------
+// Per-token (per-row) dynamic quantisation, row held in registers.
+// TPR threads share one row (64: one wavefront, 256: the whole block); each
+// thread holds VPT vectors of 8 elements. One HBM read, one HBM write.
+// ------------------------------------------------------------------------
+template <int XT, int QT, int TPR, int VPT>
+__global__ __launch_bounds__(kBlock) void quant_rows_kernel(const void* __restrict__ x, int64_t ldx,
+                                                            uint8_t* __restrict__ q, int64_t ldq,
+                                                            float* __restrict__ scales, int64_t M,
+                                                            int64_t K) {
+    constexpr int RPB = kBlock / TPR;
+    const int t = threadIdx.x % TPR;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
+    const bool active = row < M;
+
+    float v[VPT][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int64_t k = static_cast<int64_t>(t + i * TPR) * 8;
+        if (active && k < K) {
+            load8<XT>(x, row * ldx + k, v[i]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+    }
+    amax = wave_max(amax);
+    if constexpr (TPR > 64) {
+        __shared__ float part[kBlock / 64];
+        if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; ++w) amax = fmaxf(amax, part[w]);
+    }
+    if (!active) return;
+
+    const float s = scale_from_absmax<QT>(amax);
+    const double r = 1.0 / static_cast<double>(s);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int64_t k = static_cast<int64_t>(t + i * TPR) * 8;
+        if (k < K) *reinterpret_cast<u32x2*>(q + row * ldq + k) = quant8<QT>(v[i], r);
+    }
+    if (t == 0) scales[row] = s;
+}
+
+// Rows too long for registers: one block per row, absmax pass then a
+// quantise pass that re-reads the row (from L2).
+template <int XT, int QT>
+__global__ __launch_bounds__(kBlock) void quant_rows_2pass_kernel(const void* __restrict__ x,
+                                                                  int64_t ldx,
+                                                                  uint8_t* __restrict__ q,
+                                                                  int64_t ldq,
+                                                                  float* __restrict__ scales,
+                                                                  int64_t M, int64_t K) {
+    const int64_t row = blockIdx.x;
+    float amax = 0.0f;
+    for (int64_t k = static_cast<int64_t>(threadIdx.x) * 8; k < K; k += kBlock * 8) {
+        float v[8];
+        load8<XT>(x, row * ldx + k, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    }
+    amax = wave_max(amax);
+    __shared__ float part[kBlock / 64];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) amax = fmaxf(amax, part[w]);
+
+    const float s = scale_from_absmax<QT>(amax);
+    const double r = 1.0 / static_cast<double>(s);
+    for (int64_t k = static_cast<int64_t>(threadIdx.x) * 8; k < K; k += kBlock * 8) {
+        float v[8];
+        load8<XT>(x, row * ldx + k, v);
+        *reinterpret_cast<u32x2*>(q + row * ldq + k) = quant8<QT>(v, r);
+    }
+    if (threadIdx.x == 0) scales[row] = s;
+}
+
+// ------------------------------------------------------------------------
+// Per-tensor passes over an [M, K] tensor with a row stride. Work is cut in
+// units of one row x 2048 elements (256 lanes x 8); each block takes kUnroll
+// units per step so that every lane keeps kUnroll 16-byte loads in flight.
+// ------------------------------------------------------------------------
+constexpr int kUnroll = 4;
+constexpr int kUnitElems = kBlock * 8;
+
+struct Units {
+    uint32_t per_row;  // units per row
+    uint32_t total;
+};
+
+__device__ __forceinline__ bool unit_coords(const Units& u, uint32_t id, int64_t K, int64_t& row,
+                                            int64_t& k) {
+    if (id >= u.total) return false;
+    const uint32_t r = id / u.per_row;
+    row = r;
+    k = static_cast<int64_t>(id - r * u.per_row) * kUnitElems + threadIdx.x * 8;
+    return k < K;
+}
+
+// Writes v into *p (a float). Used to reset the absmax slot, as a kernel so
+// that a captured graph holds no memset node.
+__global__ void fill_f32_kernel(float* p, float v) { *p = v; }
+
+// absmax over the tensor, merged into *amax_slot (float bits; every value is
+// >= 0, so unsigned integer order is float order).
+template <int XT>
+__global__ __launch_bounds__(kBlock) void absmax_kernel(const void* __restrict__ x, int64_t ldx,
+                                                        Units u, int64_t K,
+                                                        float* __restrict__ amax_slot) {
+    float amax = 0.0f;
+    for (uint32_t base = blockIdx.x * kUnroll; base < u.total; base += gridDim.x * kUnroll) {
+        float v[kUnroll][8];
+        bool ok[kUnroll];
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+            int64_t row, k;
+            ok[j] = unit_coords(u, base + j, K, row, k);
+            if (ok[j]) load8<XT>(x, row * ldx + k, v[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j)
+            if (ok[j])
+#pragma unroll
+                for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
+    }
+    amax = wave_max(amax);
+    __shared__ float part[kBlock / 64];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; ++w) amax = fmaxf(amax, part[w]);
+        atomicMax(reinterpret_cast<unsigned int*>(amax_slot), __float_as_uint(amax));
+    }
+}
+
+// Quantise with one scale for the whole tensor. FROM_AMAX: *scale holds the
+// tensor's absmax (bits) and the scale is derived here; otherwise *scale is
+// the scale itself, NULL meaning 1.0.
+template <int XT, int QT, bool FROM_AMAX>
+__global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const void* __restrict__ x,
+                                                              int64_t ldx,
+                                                              uint8_t* __restrict__ q, int64_t ldq,
+                                                              const float* __restrict__ scale,
+                                                              Units u, int64_t K) {
+    float s;
+    if constexpr (FROM_AMAX) s = scale_from_absmax<QT>(*scale);
+    else s = scale ? *scale : 1.0f;
+    const double r = 1.0 / static_cast<double>(s);
+    for (uint32_t base = blockIdx.x * kUnroll; base < u.total; base += gridDim.x * kUnroll) {
+        float v[kUnroll][8];
+        bool ok[kUnroll];
+        int64_t row[kUnroll], k[kUnroll];
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+            ok[j] = unit_coords(u, base + j, K, row[j], k[j]);
+            if (ok[j]) load8<XT>(x, row[j] * ldx + k[j], v[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j)
+            if (ok[j]) *reinterpret_cast<u32x2*>(q + row[j] * ldq + k[j]) = quant8<QT>(v[j], r);
+    }
+}
+
+// absmax (bits, in *scale) -> scale, in place. Runs after the quantise pass.
+template <int QT>
+__global__ void finalize_scale_kernel(float* scale) { *scale = scale_from_absmax<QT>(*scale); }
+
+// ------------------------------------------------------------------------
+// KV dequant: 16 codes per lane (one 16-byte load), product in float32,
+// rounded once into the output type.
+// ------------------------------------------------------------------------
+template <int XT>
+__global__ __launch_bounds__(kBlock) void kv_dequant_kernel(const uint8_t* __restrict__ q,
+                                                            int64_t n,
+                                                            const float* __restrict__ scale,
+                                                            void* __restrict__ x) {
+    const float s = scale ? *scale : 1.0f;
+    const int64_t nvec = n / 16;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * kUnroll + threadIdx.x;
+         base < nvec; base += static_cast<int64_t>(gridDim.x) * kBlock * kUnroll) {
+        u32x4 c[kUnroll];
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+            const int64_t i = base + j * kBlock;
+            if (i < nvec) c[j] = reinterpret_cast<const u32x4*>(q)[i];
+        }
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+            const int64_t i = base + j * kBlock;
+            if (i >= nvec) continue;
+            float f[16];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                f[4 * w + 0] = __builtin_amdgcn_cvt_f32_fp8(c[j][w], 0) * s;
+                f[4 * w + 1] = __builtin_amdgcn_cvt_f32_fp8(c[j][w], 1) * s;
+                f[4 * w + 2] = __builtin_amdgcn_cvt_f32_fp8(c[j][w], 2) * s;
+                f[4 * w + 3] = __builtin_amdgcn_cvt_f32_fp8(c[j][w], 3) * s;
+            }
+            if constexpr (XT == D_F32) {
+                f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(x) + i * 16);
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    o[w] = f32x4{f[4 * w], f[4 * w + 1], f[4 * w + 2], f[4 * w + 3]};
+            } else {
+                u32x4 o[2];
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {
+                    uint32_t lo, hi;
+                    if constexpr (XT == D_BF16) {
+                        lo = to_bf16_bits(f[2 * w]);
+                        hi = to_bf16_bits(f[2 * w + 1]);
+                    } else {
+                        lo = to_fp16_bits(f[2 * w]);
+                        hi = to_fp16_bits(f[2 * w + 1]);
+                    }
+                    o[w / 4][w % 4] = lo | (hi << 16);
+                }
+                u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(x) + i * 16);
+                dst[0] = o[0];
+                dst[1] = o[1];
+            }
+        }
+    }
+}
+
+int grid_for(uint64_t work_items, uint64_t per_block) {
+    uint64_t g = (work_items + per_block - 1) / per_block;
+    if (g > 8192) g = 8192;
+    if (g < 1) g = 1;
+    return static_cast<int>(g);
+}
+
+Units make_units(int64_t M, int64_t K) {
+    Units u;
+    u.per_row = static_cast<uint32_t>((K + kUnitElems - 1) / kUnitElems);
+    u.total = static_cast<uint32_t>(M) * u.per_row;
+    return u;
+}
+
+template <int XT, int QT>
+hipError_t per_token_typed(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                           int64_t ldq, float* scales, hipStream_t st) {
+    // Fit the row in registers when possible: one wave per row up to 8192
+    // elements, one 256-lane block per row up to 32768, else two passes.
+    if (K <= 8192) {
+        const int g = static_cast<int>((M + 3) / 4);
+        if (K <= 1024)
+            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 64, 2>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
+        else if (K <= 2048)
+            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 64, 4>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
+        else if (K <= 4096)
+            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 64, 8>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
+        else
+            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 64, 16>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
+    } else if (K <= 32768) {
+        const int g = static_cast<int>(M);
+        if (K <= 16384)
+            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 256, 8>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
+        else
+            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 256, 16>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
+    } else {
+        hipLaunchKernelGGL((quant_rows_2pass_kernel<XT, QT>), dim3(static_cast<int>(M)), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
+    }
+    return hipGetLastError();
+}
+
+template <int XT, int QT>
+hipError_t per_tensor_typed(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                            int64_t ldq, float* scale, bool dynamic, hipStream_t st) {
+    const Units u = make_units(M, K);
+    const int g = grid_for(u.total, kUnroll);
+    if (dynamic) {
+        hipLaunchKernelGGL(fill_f32_kernel, dim3(1), dim3(1), 0, st, scale, 0.0f);
+        hipLaunchKernelGGL((absmax_kernel<XT>), dim3(g), dim3(kBlock), 0, st, x, ldx, u, K, scale);
+        hipLaunchKernelGGL((quant_tensor_kernel<XT, QT, true>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, static_cast<const float*>(scale), u, K);
+        hipLaunchKernelGGL((finalize_scale_kernel<QT>), dim3(1), dim3(1), 0, st, scale);
+    } else {
+        hipLaunchKernelGGL((quant_tensor_kernel<XT, QT, false>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, static_cast<const float*>(scale), u, K);
+    }
+    return hipGetLastError();
+}
+
+template <int QT>
+hipError_t per_token_q(int xt, const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                       int64_t ldq, float* scales, hipStream_t st) {
+    switch (xt) {
+        case D_BF16: return per_token_typed<D_BF16, QT>(x, M, K, ldx, q, ldq, scales, st);
+        case D_FP16: return per_token_typed<D_FP16, QT>(x, M, K, ldx, q, ldq, scales, st);
+        default: return per_token_typed<D_F32, QT>(x, M, K, ldx, q, ldq, scales, st);
+    }
+}
+
+template <int QT>
+hipError_t per_tensor_q(int xt, const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                        int64_t ldq, float* scale, bool dynamic, hipStream_t st) {
+    switch (xt) {
+        case D_BF16: return per_tensor_typed<D_BF16, QT>(x, M, K, ldx, q, ldq, scale, dynamic, st);
+        case D_FP16: return per_tensor_typed<D_FP16, QT>(x, M, K, ldx, q, ldq, scale, dynamic, st);
+        default: return per_tensor_typed<D_F32, QT>(x, M, K, ldx, q, ldq, scale, dynamic, st);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quant_per_token(int xt, const void* x, int64_t M, int64_t K, int64_t ldx,
+                                  uint8_t* q, int qt, int64_t ldq, float* scales, hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    if (qt == Q_FP8) return per_token_q<Q_FP8>(xt, x, M, K, ldx, q, ldq, scales, st);
+    return per_token_q<Q_INT8>(xt, x, M, K, ldx, q, ldq, scales, st);
+}
+
+hipError_t launch_quant_per_tensor(int xt, const void* x, int64_t M, int64_t K, int64_t ldx,
+                                   uint8_t* q, int qt, int64_t ldq, float* scale, bool dynamic,
+                                   hipStream_t st) {
+    if (qt == Q_FP8) return per_tensor_q<Q_FP8>(xt, x, M, K, ldx, q, ldq, scale, dynamic, st);
+    return per_tensor_q<Q_INT8>(xt, x, M, K, ldx, q, ldq, scale, dynamic, st);
+}
+
+hipError_t launch_kv_dequant(const uint8_t* q, int64_t n, const float* scale, void* x, int xt,
+                             hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int g = grid_for(static_cast<uint64_t>(n / 16), static_cast<uint64_t>(kBlock) * kUnroll);
+    switch (xt) {
+        case D_BF16: hipLaunchKernelGGL((kv_dequant_kernel<D_BF16>), dim3(g), dim3(kBlock), 0, st, q, n, scale, x); break;
+        case D_FP16: hipLaunchKernelGGL((kv_dequant_kernel<D_FP16>), dim3(g), dim3(kBlock), 0, st, q, n, scale, x); break;
+        default: hipLaunchKernelGGL((kv_dequant_kernel<D_F32>), dim3(g), dim3(kBlock), 0, st, q, n, scale, x); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace w8a8

@@ -32,9 +32,11 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 QT_INT8, QT_FP8 = 0, 1
-DT_BF16, DT_FP16, DT_F32, DT_I32 = 0, 1, 2, 3
+DT_BF16, DT_FP16, DT_F32, DT_I32, DT_F64 = 0, 1, 2, 3, 4
 QTYPES = {"int8": QT_INT8, "fp8": QT_FP8}
-DTYPES = {"bf16": DT_BF16, "fp16": DT_FP16, "f32": DT_F32, "i32": DT_I32}
+DTYPES = {"bf16": DT_BF16, "fp16": DT_FP16, "f32": DT_F32, "i32": DT_I32, "f64": DT_F64}
+_OUT_NP = {"bf16": np.uint16, "fp16": np.uint16, "f32": np.float32, "i32": np.int32,
+           "f64": np.float64}
 
 
 def build(force: bool = True) -> str:
@@ -200,7 +202,8 @@ def scaled_mm(a: np.ndarray, b: np.ndarray, qtype: str, a_scales=None, b_scales=
               otype: str = "bf16") -> np.ndarray:
     """D = a_scale (x) b_scale * (A . B^T) for codes a [M, K], b [N, K] (uint8 views).
 
-    Returns uint16 bit patterns for bf16/fp16, float32 for f32, int32 for i32.
+    Returns uint16 bit patterns for bf16/fp16, float32 for f32, int32 for i32,
+    float64 for f64 (the value before the final rounding).
     """
     a = np.ascontiguousarray(a).view(np.uint8)
     b = np.ascontiguousarray(b).view(np.uint8)
@@ -209,8 +212,7 @@ def scaled_mm(a: np.ndarray, b: np.ndarray, qtype: str, a_scales=None, b_scales=
     assert K == K2
     sa, n_a = _scales(a_scales, M)
     sb, n_b = _scales(b_scales, N)
-    odt = {"bf16": np.uint16, "fp16": np.uint16, "f32": np.float32, "i32": np.int32}[otype]
-    out = np.empty((M, N), odt)
+    out = np.empty((M, N), _OUT_NP[otype])
     lib().oracle_scaled_mm(_ptr(out), DTYPES[otype], N, _ptr(a), K, _ptr(b), K, QTYPES[qtype],
                            M, N, K, _ptr(sa), n_a, _ptr(sb), n_b)
     return out
@@ -227,8 +229,7 @@ def scaled_mm_rows(rows, a: np.ndarray, b: np.ndarray, qtype: str, a_scales=None
     assert r.size == 0 or (r.min() >= 0 and r.max() < M)
     sa, n_a = _scales(a_scales, M)
     sb, n_b = _scales(b_scales, N)
-    odt = {"bf16": np.uint16, "fp16": np.uint16, "f32": np.float32, "i32": np.int32}[otype]
-    out = np.empty((r.size, N), odt)
+    out = np.empty((r.size, N), _OUT_NP[otype])
     lib().oracle_scaled_mm_rows(_ptr(out), DTYPES[otype], N, _ptr(r), r.size, _ptr(a), K,
                                 _ptr(b), K, QTYPES[qtype], N, K, _ptr(sa), n_a, _ptr(sb), n_b)
     return out

@@ -42,6 +42,7 @@
 #define DT_FP16 1
 #define DT_F32 2
 #define DT_I32 3
+#define DT_F64 4
 
 /* ---------------------------------------------------------------------- */
 /* Rounding a non-negative double onto a binary floating-point grid.       */
@@ -273,8 +274,8 @@ void oracle_kv_dequant(const uint8_t* q, int64_t n, const float* scale, void* x,
 /* the sum stays exact while K < 2^17).                                     */
 /* D[m, n] = acc * a_scale[m or 0] * b_scale[n or 0] in fp64, then rounded */
 /* once to bf16 or fp16. A NULL scale array means 1.0.                     */
-/* otype DT_F32 stores the fp64 value rounded to binary32; DT_I32 (int8    */
-/* only) stores the raw accumulator.                                       */
+/* otype DT_F32 stores the fp64 value rounded to binary32, DT_F64 the fp64 */
+/* value itself; DT_I32 (int8 only) stores the raw accumulator.            */
 /* ---------------------------------------------------------------------- */
 static void mm_one(void* out, int otype, int64_t ldo, int64_t orow, const uint8_t* a, int64_t lda,
                    const uint8_t* b, int64_t ldb, int qtype, int64_t m, int64_t n, int64_t K,
@@ -301,6 +302,7 @@ static void mm_one(void* out, int otype, int64_t ldo, int64_t orow, const uint8_
     double d = acc * s_a * s_b;
     if (otype == DT_BF16) ((uint16_t*)out)[orow * ldo + n] = oracle_bf16_from_double(d);
     else if (otype == DT_FP16) ((uint16_t*)out)[orow * ldo + n] = oracle_fp16_from_double(d);
+    else if (otype == DT_F64) ((double*)out)[orow * ldo + n] = d;
     else ((float*)out)[orow * ldo + n] = (float)d;
 }
 

@@ -1,0 +1,120 @@
+"""The C ABI library: it loads, exports every function include/w8a8.h
+declares, and rejects bad arguments on the host with a status (never a
+crash), as the review on "[Kernel] Add w8a8 CUTLASS kernels" asks of input
+validation. No call here reaches the GPU: each one fails validation first.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import int8_scaled_gemm_amd as w8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8a8.h")
+
+# status codes (include/w8a8.h)
+OK, INVALID, SHAPE, LAYOUT, ALIGN, DTYPE, UNSUP = 0, 1, 2, 3, 4, 5, 6
+FAKE = 0x10000  # a 16-byte-aligned non-NULL address; never dereferenced by failing calls
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(w8a8_\w+|kv_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return w8.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared()
+    assert set(names) >= {"w8a8_quant_per_token", "w8a8_quant_per_tensor", "w8a8_scaled_mm",
+                          "kv_fp8_scaled_quant", "kv_fp8_scaled_dequant",
+                          "w8a8_status_string", "w8a8_last_error"}
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", w8.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)", out))
+    assert set(names) <= exported
+
+
+def test_header_compiles_as_c(tmp_path):
+    c = tmp_path / "t.c"
+    c.write_text('#include "w8a8.h"\nint main(void){return (int)w8a8_status_string(W8A8_OK)[0];}\n')
+    subprocess.run(["gcc", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    "-I" + os.path.dirname(HEADER), str(c)], check=True)
+
+
+def test_status_strings(lib):
+    for code, name in w8.STATUS_NAMES.items():
+        assert lib.w8a8_status_string(code).decode() == name
+    assert lib.w8a8_version().decode().startswith("libw8a8")
+
+
+def mm(lib, out=FAKE, ot=0, ldo=64, a=FAKE, lda=128, b=FAKE, ldb=128, qt=1, M=16, N=64, K=128,
+       sa=None, n_a=1, sb=None, n_b=1):
+    return lib.w8a8_scaled_mm(out, ot, ldo, a, lda, b, ldb, qt, M, N, K, sa, n_a, sb, n_b, None)
+
+
+def test_scaled_mm_validation(lib):
+    assert mm(lib, ldb=64) == LAYOUT          # B not column-major (ldb < K)
+    assert "column-major" in lib.w8a8_last_error().decode()
+    assert mm(lib, lda=100) == LAYOUT
+    assert mm(lib, ldo=32) == LAYOUT
+    assert mm(lib, M=-1) == SHAPE
+    assert mm(lib, K=120, lda=128, ldb=128) == ALIGN   # K not a multiple of 16
+    assert mm(lib, lda=136) == ALIGN
+    assert mm(lib, a=FAKE + 8) == ALIGN
+    assert mm(lib, out=FAKE + 1) == ALIGN              # bf16 out must be 2-byte aligned
+    assert mm(lib, qt=7) == DTYPE
+    assert mm(lib, ot=9) == DTYPE
+    assert mm(lib, ot=3, qt=1) == DTYPE                 # raw int32 only for int8
+    assert mm(lib, ot=3, qt=0, sa=FAKE) == INVALID      # raw accumulator takes no scales
+    assert mm(lib, sa=FAKE, n_a=5) == SHAPE             # neither 1 nor M
+    assert mm(lib, sb=FAKE, n_b=63) == SHAPE
+    assert mm(lib, out=None) == INVALID
+    assert mm(lib, a=None) == INVALID
+    assert mm(lib, qt=0, K=131088, lda=131088, ldb=131088) == UNSUP
+    assert mm(lib, M=2**31) == UNSUP
+    # empty problems are accepted without touching memory
+    assert mm(lib, M=0, out=None, a=None, b=None) == OK
+    assert mm(lib, N=0, out=None, a=None, b=None) == OK
+
+
+def test_quant_validation(lib):
+    f = lib.w8a8_quant_per_token
+    assert f(FAKE, 0, 4, 100, 112, FAKE, 1, 112, FAKE, None) == ALIGN
+    assert f(FAKE, 0, 4, 128, 64, FAKE, 1, 128, FAKE, None) == LAYOUT
+    assert f(FAKE, 5, 4, 128, 128, FAKE, 1, 128, FAKE, None) == DTYPE
+    assert f(FAKE, 0, 4, 128, 128, FAKE, 3, 128, FAKE, None) == DTYPE
+    assert f(FAKE, 0, 4, 128, 128, FAKE, 1, 128, None, None) == INVALID
+    assert f(None, 0, 4, 128, 128, FAKE, 1, 128, FAKE, None) == INVALID
+    assert f(FAKE, 0, -4, 128, 128, FAKE, 1, 128, FAKE, None) == SHAPE
+    assert f(None, 0, 0, 128, 128, None, 1, 128, None, None) == OK
+    g = lib.w8a8_quant_per_tensor
+    assert g(FAKE, 0, 4, 128, 128, FAKE, 1, 128, None, 1, None) == INVALID  # dynamic needs a slot
+    assert g(FAKE, 0, 4, 128, 128, FAKE, 1, 128, FAKE, 2, None) == INVALID
+    assert g(FAKE + 4, 0, 4, 128, 128, FAKE, 1, 128, None, 0, None) == ALIGN
+    k = lib.kv_fp8_scaled_quant
+    assert k(FAKE, 0, 100, FAKE, FAKE, 1, None) == ALIGN
+    assert k(FAKE, 0, 128, FAKE, None, 1, None) == INVALID
+    assert k(FAKE, 0, -16, FAKE, FAKE, 1, None) == SHAPE
+    d = lib.kv_fp8_scaled_dequant
+    assert d(FAKE, 100, FAKE, FAKE, 0, None) == ALIGN
+    assert d(FAKE, 128, FAKE, FAKE, 3, None) == DTYPE
+    assert d(None, 128, FAKE, FAKE, 0, None) == INVALID
+    assert d(None, 0, None, None, 0, None) == OK
+
+
+def test_binding_layout_errors_are_python_errors():
+    import torch
+    # the binding refuses host tensors and wrong layouts before calling the library
+    a = torch.zeros(4, 128, dtype=torch.float8_e4m3fn)
+    with pytest.raises(ValueError):
+        w8.w8a8_scaled_mm(a, a.t(), None, None)

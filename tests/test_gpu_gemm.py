@@ -1,0 +1,218 @@
+"""GPU parity of the scaled matrix multiply against the oracle.
+
+D = a_scale (x) b_scale * (A_q . B_q) with B column-major ("[Kernel] Add w8a8
+CUTLASS kernels": PR description list, misaligned-address report, and the
+review's unit test on submatrices of A and B). int8 accumulators are
+compared bit for bit; outputs within the tolerance in tests/gpu_util.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import int8_scaled_gemm_amd as w8
+import oracle
+import workloads
+from tests.gpu_util import DEV, TORCH_OF, bits, check_scaled_mm, codes_to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _quantized(M, N, K, qtype, seed):
+    """Llama-like data quantised by the oracle: activations per token,
+    weights per output channel."""
+    x = workloads.activations(M, K, seed=seed)
+    w = workloads.weights(N, K, seed=seed + 1)
+    a, sa = oracle.quant_per_token(x.view(torch.int16).numpy().view(np.uint16), qtype, xtype="bf16")
+    b, sb = oracle.quant_per_token(w.view(torch.int16).numpy().view(np.uint16), qtype, xtype="bf16")
+    return a, sa, b, sb
+
+
+def _run(a, b, qtype, sa, sb, otype):
+    ad = codes_to_dev(a, qtype)
+    bd = codes_to_dev(b, qtype)  # [N, K] row-major: its transpose is K x N column-major
+    sad = None if sa is None else torch.from_numpy(np.asarray(sa, np.float32)).to(DEV)
+    sbd = None if sb is None else torch.from_numpy(np.asarray(sb, np.float32)).to(DEV)
+    out = w8.w8a8_scaled_mm(ad, bd.t(), sad, sbd, TORCH_OF[otype])
+    torch.cuda.synchronize()
+    return out
+
+
+SHAPES = [
+    # decode path (M <= 64): ragged N, K with a 16-byte tail past a 128-byte slice
+    (1, 48, 4096), (1, 4096, 4096), (5, 100, 272), (16, 64, 128), (17, 200, 1040),
+    (33, 1000, 144), (64, 6144, 512), (2, 16, 16),
+    # tiled path: several tiles and ragged tails in M, N, K
+    (65, 130, 128), (200, 384, 1040), (256, 256, 4096), (300, 520, 272), (777, 1111, 528),
+    (1024, 768, 2048),
+]
+
+
+@pytest.mark.parametrize("qtype", ["fp8", "int8"])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_scaled_mm_parity(qtype, M, N, K):
+    a, sa, b, sb = _quantized(M, N, K, qtype, seed=M + N + K)
+    info = check_scaled_mm(_run(a, b, qtype, sa, sb, "bf16"), a, b, qtype, sa, sb, "bf16")
+    assert info["exact_frac"] > 0.9, info
+
+
+@pytest.mark.parametrize("qtype", ["fp8", "int8"])
+@pytest.mark.parametrize("otype", ["bf16", "fp16", "f32"])
+@pytest.mark.parametrize("gran", ["tensor-tensor", "token-tensor", "tensor-channel", "none"])
+@pytest.mark.parametrize("M", [8, 160])
+def test_scale_granularities_and_outputs(qtype, otype, gran, M):
+    N, K = 272, 384
+    a, sa, b, sb = _quantized(M, N, K, qtype, seed=7 * M)
+    if gran == "tensor-tensor":
+        sa, sb = sa[:1], sb[:1]
+    elif gran == "token-tensor":
+        sb = sb[:1]
+    elif gran == "tensor-channel":
+        sa = sa[:1]
+    else:
+        sa = sb = None
+        if otype == "fp16":  # raw accumulators overflow fp16
+            sa = np.array([2.0 ** -10], np.float32)
+    check_scaled_mm(_run(a, b, qtype, sa, sb, otype), a, b, qtype, sa, sb, otype)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (16, 64, 128), (40, 100, 4096), (300, 300, 1024),
+                                   (64, 28672 // 8, 4096)])
+def test_int8_raw_accumulator_bit_exact(M, N, K):
+    a = workloads.random_codes((M, K), "int8", seed=1).numpy()
+    b = workloads.random_codes((N, K), "int8", seed=2).numpy()
+    check_scaled_mm(_run(a, b, "int8", None, None, "i32"), a, b, "int8", None, None, "i32")
+
+
+def test_int8_extreme_accumulator():
+    """All 127 x all -127 over K = 28672: -462,450,688 in every element."""
+    K = 28672
+    a = np.full((3, K), 127, np.int8).view(np.uint8)
+    b = np.full((20, K), -127, np.int8).view(np.uint8)
+    out = _run(a, b, "int8", None, None, "i32").cpu().numpy()
+    assert (out == -462450688).all()
+
+
+def test_fp8_uniform_random_codes():
+    """Every finite e4m3 code, including subnormals and +-448, in the operands."""
+    M, N, K = 96, 160, 1024
+    a = workloads.random_codes((M, K), "fp8", seed=3).numpy()
+    b = workloads.random_codes((N, K), "fp8", seed=4).numpy()
+    sa = np.float32(1e-4) * np.ones(M, np.float32)
+    sb = np.linspace(1e-3, 2e-3, N).astype(np.float32)
+    check_scaled_mm(_run(a, b, "fp8", sa, sb, "bf16"), a, b, "fp8", sa, sb, "bf16")
+    a1 = a[:7]
+    check_scaled_mm(_run(a1, b, "fp8", sa[:7], sb, "f32"), a1, b, "fp8", sa[:7], sb, "f32")
+
+
+def test_tiny_int8_case_end_to_end():
+    """The tiny int8 case, every step on the GPU: per-tensor dynamic int8
+    quantisation of A [16,128] and W [64,128], int32 accumulate, bf16 out."""
+    x, w = workloads.tiny_int8_inputs()
+    xh = x.view(torch.int16).numpy().view(np.uint16)
+    wh = w.view(torch.int16).numpy().view(np.uint16)
+    qa_ref, sa_ref = oracle.quant_per_tensor(xh, "int8", dynamic=True, xtype="bf16")
+    qw_ref, sw_ref = oracle.quant_per_tensor(wh, "int8", dynamic=True, xtype="bf16")
+    d_ref = oracle.scaled_mm(qa_ref, qw_ref, "int8", [sa_ref], [sw_ref], "bf16")
+    qa, sa = w8.w8a8_quant_per_tensor(x.to(DEV), "int8", dynamic=True)
+    qw, sw = w8.w8a8_quant_per_tensor(w.to(DEV), "int8", dynamic=True)
+    d = w8.scaled_mm(qa, qw.t(), sa, sw, torch.bfloat16)
+    raw = w8.w8a8_scaled_mm(qa, qw.t(), None, None, torch.int32)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(qa), qa_ref) and np.array_equal(bits(qw), qw_ref)
+    assert np.array_equal(raw.cpu().numpy(), oracle.scaled_mm(qa_ref, qw_ref, "int8", None, None, "i32"))
+    check_scaled_mm(d, qa_ref, qw_ref, "int8", [sa_ref], [sw_ref], "bf16")
+    assert np.mean(bits(d) == d_ref) > 0.99
+
+
+@pytest.mark.parametrize("M", [7, 150])
+def test_submatrices_and_output_padding(M):
+    """A and B as column windows of wider matrices (leading dimensions larger
+    than K), output into a window of a wider buffer: padding untouched."""
+    N, K = 96, 256
+    qtype = "fp8"
+    abig = workloads.random_codes((M, K + 64), qtype, seed=5).numpy()
+    bbig = workloads.random_codes((N + 8, K + 32), qtype, seed=6).numpy()
+    a = np.ascontiguousarray(abig[:, 32:32 + K])
+    b = np.ascontiguousarray(bbig[4:4 + N, 16:16 + K])
+    sa = np.full(M, 1e-3, np.float32)
+    sb = np.full(N, 2e-3, np.float32)
+    ad = codes_to_dev(abig, qtype)[:, 32:32 + K]
+    bd = codes_to_dev(bbig, qtype)[4:4 + N, 16:16 + K]
+    obig = torch.full((M, N + 40), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = obig[:, 24:24 + N]
+    w8.w8a8_scaled_mm(ad, bd.t(), torch.from_numpy(sa).to(DEV), torch.from_numpy(sb).to(DEV),
+                      torch.bfloat16, out=out)
+    torch.cuda.synchronize()
+    check_scaled_mm(out, a, b, qtype, sa, sb, "bf16")
+    ob = obig.float().cpu().numpy()
+    assert (ob[:, :24] == 7.0).all() and (ob[:, 24 + N:] == 7.0).all()
+
+
+def test_k_zero_writes_zeros_and_empty_is_noop():
+    a = torch.empty(5, 0, dtype=torch.int8, device=DEV)
+    b = torch.empty(0, 9, dtype=torch.int8, device=DEV)
+    out = torch.full((5, 9), 3.0, dtype=torch.bfloat16, device=DEV)
+    w8.w8a8_scaled_mm(a, b, None, None, torch.bfloat16, out=out)
+    torch.cuda.synchronize()
+    assert (out.float().cpu() == 0).all()
+    e = w8.w8a8_scaled_mm(torch.empty(0, 64, dtype=torch.int8, device=DEV),
+                          torch.empty(64, 32, dtype=torch.int8, device=DEV).t().contiguous().t(),
+                          None, None)
+    assert e.shape == (0, 32)
+
+
+def test_wrong_b_layout_is_an_error_not_a_crash():
+    """The misaligned-address report: B passed row-major K x N instead of
+    column-major. Here it is refused before any launch."""
+    a = torch.zeros(8, 4096, dtype=torch.float8_e4m3fn, device=DEV)
+    b = torch.zeros(4096, 8192, dtype=torch.float8_e4m3fn, device=DEV)  # row-major K x N
+    with pytest.raises(ValueError, match="column-major"):
+        w8.w8a8_scaled_mm(a, b, None, None, torch.float16)
+    lib = w8.load_library()
+    st = lib.w8a8_scaled_mm(None, 0, 8192, a.data_ptr(), 4096, b.data_ptr(), 8192 - 8192, 1,
+                            8, 8192, 4096, None, 1, None, 1, None)
+    assert st == 3  # W8A8_ERR_LAYOUT
+
+
+def test_graph_capture_and_replay():
+    """The quantizers and the GEMM capture into a HIP graph (they allocate and
+    synchronise nothing) and every replay matches the eager result."""
+    M, N, K = 16, 512, 1024
+    x = workloads.activations(M, K, seed=31).to(DEV)
+    w = workloads.weights(N, K, seed=32).to(DEV)
+    qw, sw = w8.w8a8_quant_per_token(w, "fp8")
+    q_eager, s_eager = w8.w8a8_quant_per_token(x, "fp8")
+    d_eager = w8.w8a8_scaled_mm(q_eager, qw.t(), s_eager, sw, torch.bfloat16)
+    kv = workloads.kv_tensor(1, "k", shape=(64, 8, 128)).to(DEV)
+    kq_eager, ks_eager = w8.kv_fp8_scaled_quant(kv)
+    torch.cuda.synchronize()
+    q = torch.empty_like(q_eager)
+    s = torch.empty_like(s_eager)
+    d = torch.empty_like(d_eager)
+    kq = torch.empty_like(kq_eager)
+    ks = torch.empty_like(ks_eager)
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            w8.w8a8_quant_per_token(x, "fp8", q=q, scales=s)
+            w8.w8a8_scaled_mm(q, qw.t(), s, sw, torch.bfloat16, out=d)
+            w8.kv_fp8_scaled_quant(kv, scale=ks, dynamic=True, q=kq)
+    torch.cuda.synchronize()
+    for i in range(3):
+        d.zero_()
+        kq.zero_()
+        ks.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits_t(d), bits_t(d_eager)), i
+        assert torch.equal(kq.view(torch.uint8), kq_eager.view(torch.uint8)), i
+        assert torch.equal(ks, ks_eager), i
+        # eager work between replays
+        w8.w8a8_quant_per_token(kv.view(-1, 128)[:64], "int8")
+        torch.cuda.synchronize()
+
+
+def bits_t(t):
+    return t.view(torch.int16)

@@ -164,3 +164,13 @@ def test_rows_variant_matches_full(orc):
     full = orc.scaled_mm(a, b, "int8", sa, sb, "bf16")
     rows = [0, 5, 36, 17]
     assert np.array_equal(orc.scaled_mm_rows(rows, a, b, "int8", sa, sb, "bf16"), full[rows])
+
+
+def test_f64_output_is_exact_product_of_scales(orc):
+    a = _codes((4, 96), "fp8", 17)
+    b = _codes((6, 96), "fp8", 18)
+    sa = np.array([0.5, 0.25, 2.0, 1.0], np.float32)
+    sb = np.array([1, 2, 4, 8, 0.5, 0.125], np.float32)  # powers of two: products exact
+    acc, den = _exact_acc(a, b, "fp8")
+    want = acc / den * sa[:, None].astype(np.float64) * sb[None, :].astype(np.float64)
+    assert np.array_equal(orc.scaled_mm(a, b, "fp8", sa, sb, "f64"), want)
