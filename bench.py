@@ -1,0 +1,384 @@
+"""Benchmark of the w8a8 scaled-GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+One step is one pass of the hot path over one batch of synthetic input,
+captured in a HIP graph and replayed (the library allocates and synchronises
+nothing, so a whole step captures). Workloads:
+
+  decode  (default) fp8 e4m3 decode GEMMs of the four Llama-3-8B linear
+          layers (QKV 6144x4096, O 4096x4096, gate_up 28672x4096, down
+          4096x14336) at M = 1, 16, 64: for each, dynamic per-token fp8
+          quantisation of the bf16 activations, then the scaled GEMM with
+          per-channel fp8 weights, bf16 out.
+  prefill the same layers at M = 512, 2048, 8192 with a static per-tensor
+          activation scale (calibrated on a seeded [512, K] batch), bf16 out.
+  int8    Llama-3-70B layers (QKV 10240x8192, O 8192x8192, gate_up
+          57344x8192, down 8192x28672) at M = 1, 64, 4096: per-token int8
+          activations, per-channel int8 weights, int32 accumulate, bf16 out.
+  kv      scaled fp8 KV cache: per-tensor dynamic quant + dequant of 32
+          layers of K and V [32768, 8, 128] bf16, plus the standalone
+          per-token fp8 quantisation of [8192, 4096] bf16.
+
+Weights are quantised once before timing (offline preparation). Every
+(M, layer) GEMM has its own weight copy, so one step streams 0.65 GB (decode)
+and the 256 MB last-level cache holds no weight from one use to the next.
+
+Prints one JSON line: the workload's throughput, a roofline entry for the
+dominant kernel (its launches timed with HIP events inside the replayed
+graph) and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import int8_scaled_gemm_amd as w8  # noqa: E402
+import workloads  # noqa: E402
+
+METRIC = "scaled_mm TFLOP/s (fp8/int8) at Llama-3-8B shapes; % of MFMA / HBM roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "int8": 5000.0}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------
+# Workloads: each builds device buffers and returns a list of launches. A
+# launch is (kind, fn, units) where fn() enqueues one library call, kind
+# names the kernel family, and units are its algorithmic flops and bytes.
+# --------------------------------------------------------------------------
+class Launch:
+    def __init__(self, kind, fn, flops, nbytes, label):
+        self.kind, self.fn, self.flops, self.nbytes, self.label = kind, fn, flops, nbytes, label
+
+
+def _gemm_bytes(M, N, K, n_sa, n_sb, out_bytes=2):
+    return M * K + N * K + 4 * n_sa + 4 * n_sb + out_bytes * M * N
+
+
+def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
+    launches, keep = [], []
+    code_dtype = torch.float8_e4m3fn if qtype == "fp8" else torch.int8
+    seed = 1000
+    for M in Ms:
+        for name, N, K in layers:
+            seed += 1
+            w = workloads.weights(N, K, seed=seed, device=dev)
+            wq, ws = w8.w8a8_quant_per_token(w, qtype)   # offline: per-channel weights
+            del w
+            x = workloads.activations(M, K, seed=seed + 500, device=dev)
+            q = torch.empty((M, K), dtype=code_dtype, device=dev)
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            if act_scheme == "per_token":
+                s = torch.empty(M, dtype=torch.float32, device=dev)
+                qf = (lambda x=x, q=q, s=s: w8.w8a8_quant_per_token(x, qtype, q=q, scales=s))
+                n_sa = M
+                qbytes = 3 * M * K + 4 * M
+            else:  # static per-tensor scale from a seeded calibration batch
+                calib = workloads.activations(workloads.CALIBRATION_ROWS, K,
+                                              seed=workloads.CALIBRATION_SEED, device=dev)
+                _, s = w8.w8a8_quant_per_tensor(calib, qtype, dynamic=True)
+                del calib
+                qf = (lambda x=x, q=q, s=s: w8.w8a8_quant_per_tensor(x, qtype, scale=s, q=q))
+                n_sa = 1
+                qbytes = 3 * M * K + 4
+            mf = (lambda q=q, wq=wq, s=s, ws=ws, out=out:
+                  w8.w8a8_scaled_mm(q, wq.t(), s, ws, torch.bfloat16, out=out))
+            launches.append(Launch("quant", qf, 0, qbytes, f"quant M={M} {name}"))
+            launches.append(Launch("gemm", mf, 2 * M * N * K, _gemm_bytes(M, N, K, n_sa, N),
+                                   f"gemm M={M} {name} {N}x{K}"))
+            keep += [wq, ws, x, q, s, out]
+    return launches, keep
+
+
+def build_kv_workload(dev, layers=workloads.KV_LAYERS):
+    launches, keep = [], []
+    n = 1
+    for d in workloads.KV_SHAPE:
+        n *= d
+    for layer in range(layers):
+        for which in ("k", "v"):
+            x = workloads.kv_tensor(layer, which, device=dev)
+            q = torch.empty(workloads.KV_SHAPE, dtype=torch.float8_e4m3fn, device=dev)
+            s = torch.empty(1, dtype=torch.float32, device=dev)
+            y = torch.empty(workloads.KV_SHAPE, dtype=torch.bfloat16, device=dev)
+            launches.append(Launch("kv_quant",
+                                   lambda x=x, q=q, s=s: w8.kv_fp8_scaled_quant(x, scale=s, q=q),
+                                   0, 2 * n + n + 2 * n, f"kv quant L{layer}{which}"))
+            launches.append(Launch("kv_dequant",
+                                   lambda q=q, s=s, y=y: w8.kv_fp8_scaled_dequant(q, s, out=y),
+                                   0, n + 2 * n, f"kv dequant L{layer}{which}"))
+            keep += [x, q, s, y]
+    M, K = workloads.PER_TOKEN_STANDALONE
+    x = workloads.activations(M, K, seed=0, device=dev)
+    q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    s = torch.empty(M, dtype=torch.float32, device=dev)
+    launches.append(Launch("quant", lambda: w8.w8a8_quant_per_token(x, "fp8", q=q, scales=s),
+                           0, 3 * M * K + 4 * M, "per-token quant 8192x4096"))
+    keep += [x, q, s]
+    return launches, keep
+
+
+WORKLOADS = {
+    "decode": dict(desc="fp8 e4m3 decode GEMMs, Llama-3-8B QKV/O/gate_up/down at M=1,16,64: "
+                        "dynamic per-token activation quant + scaled_mm, per-channel weights, "
+                        "bf16 out",
+                   layers=workloads.LLAMA3_8B_LAYERS, Ms=workloads.FP8_DECODE_M, qtype="fp8",
+                   act="per_token", dominant="gemm", bound="hbm"),
+    "prefill": dict(desc="fp8 e4m3 prefill GEMMs, Llama-3-8B QKV/O/gate_up/down at "
+                         "M=512,2048,8192: static per-tensor activation quant + scaled_mm, "
+                         "per-channel weights, bf16 out",
+                    layers=workloads.LLAMA3_8B_LAYERS, Ms=workloads.FP8_PREFILL_M, qtype="fp8",
+                    act="per_tensor_static", dominant="gemm", bound="mfma"),
+    "int8": dict(desc="int8 w8a8 GEMMs, Llama-3-70B unsharded QKV/O/gate_up/down at "
+                      "M=1,64,4096: per-token int8 activations + scaled_mm, per-channel int8 "
+                      "weights, int32 accumulate, bf16 out",
+                 layers=workloads.LLAMA3_70B_LAYERS, Ms=workloads.INT8_70B_M, qtype="int8",
+                 act="per_token", dominant="gemm", bound="mfma"),
+    "kv": dict(desc="scaled fp8 KV cache: per-tensor dynamic quant + dequant of 32 layers of "
+                    "K and V [32768,8,128] bf16, plus per-token fp8 quant of [8192,4096]",
+               dominant="kv_quant", bound="hbm"),
+}
+
+
+# --------------------------------------------------------------------------
+def capture(launches, stream, timed_kind=None):
+    """Capture every launch into one graph. With timed_kind, each launch of
+    that kind is bracketed by a pair of externally recorded timing events."""
+    g = torch.cuda.CUDAGraph()
+    pairs = []
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for L in launches:
+                if timed_kind is not None and L.kind == timed_kind:
+                    e0 = torch.cuda.Event(enable_timing=True, external=True)
+                    e1 = torch.cuda.Event(enable_timing=True, external=True)
+                    e0.record(stream)
+                    L.fn()
+                    e1.record(stream)
+                    pairs.append((L, e0, e1))
+                else:
+                    L.fn()
+    return g, pairs
+
+
+def cpu_baseline(spec, launches_meta, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    cores = oracle.num_threads()
+    if spec.get("layers") is None:   # kv: quant + dequant of a slice of one layer tensor
+        x = workloads.kv_tensor(0, "k")
+        xh = workloads.as_u16(x).reshape(-1)
+        n = xh.size // 8
+        t0 = time.perf_counter()
+        q, s = oracle.kv_quant(xh[:n], xtype="bf16")
+        oracle.kv_dequant(q, s, "bf16")
+        dt = time.perf_counter() - t0
+        return {"value": round(5 * n / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+                "kind": "oracle",
+                "sample": f"KV quant+dequant of the first {n} elements of layer 0 K (1/8 tensor)"}
+    frac = 8
+    flops = 0
+    t0 = time.perf_counter()
+    done = 0
+    for M in spec["Ms"]:
+        for name, N, K in spec["layers"]:
+            Ms = min(M, 64)
+            Ns = max(16, N // frac)
+            x = workloads.as_u16(workloads.activations(Ms, K, seed=7))
+            w = workloads.as_u16(workloads.weights(Ns, K, seed=8))
+            if spec["act"] == "per_token":
+                a, sa = oracle.quant_per_token(x, spec["qtype"], xtype="bf16")
+            else:
+                a, sa = oracle.quant_per_tensor(x, spec["qtype"], scale=np.float32(0.05),
+                                                xtype="bf16")
+                sa = np.array([sa], np.float32)
+            b, sb = oracle.quant_per_token(w, spec["qtype"], xtype="bf16")
+            oracle.scaled_mm(a, b, spec["qtype"], sa, sb, "bf16")
+            flops += 2 * Ms * Ns * K
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{done} of the step's (M, layer) GEMMs with their activation quant, "
+                      f"on the first N/{frac} weight rows and at most 64 rows of M "
+                      f"({flops / 1e9:.2f} GFLOP, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle time for the CPU baseline (0: skip)")
+    ap.add_argument("--detail", action="store_true", help="per-launch times on stderr")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(collectives and sharding are out of scope); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    spec = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    w8.load_library()
+    log(f"[bench] workload {args.workload}: building inputs")
+    if args.workload == "kv":
+        launches, keep = build_kv_workload(dev)
+    else:
+        launches, keep = build_gemm_workload(spec["layers"], spec["Ms"], spec["qtype"],
+                                             spec["act"], dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+
+    # eager warm-up of every launch (also validates arguments before capture)
+    with torch.cuda.stream(stream):
+        for L in launches:
+            L.fn()
+    torch.cuda.synchronize()
+
+    dominant = spec["dominant"]
+    try:
+        graph, pairs = capture(launches, stream, timed_kind=dominant)
+        timed_in_graph = True
+    except Exception as e:  # event nodes unsupported: time the dominant launches separately
+        log(f"[bench] timing events inside the graph unavailable ({e}); falling back")
+        torch.cuda.synchronize()
+        graph, pairs = capture(launches, stream)
+        timed_in_graph = False
+
+    # Every replay and every timing event below goes to `stream` (a graph
+    # replays on the current stream).
+    stream_ctx = torch.cuda.stream(stream)
+    stream_ctx.__enter__()
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    step_ms = start.elapsed_time(end) / args.steps
+
+    if timed_in_graph:
+        # the event pairs hold the dominant launches of the last timed replay
+        dom_ms = sum(e0.elapsed_time(e1) for _, e0, e1 in pairs)
+        dom_n = len(pairs)
+    else:
+        dl = [L for L in launches if L.kind == dominant]
+        g2, _ = capture(dl, stream)
+        g2.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            g2.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dom_ms = e0.elapsed_time(e1)
+        dom_n = args.steps * len(dl)
+
+    per_step_flops = sum(L.flops for L in launches)
+    per_step_bytes = sum(L.nbytes for L in launches)
+    dl = [L for L in launches if L.kind == dominant]
+    dom_avg_s = dom_ms / 1e3 / dom_n
+    dom_bytes = sum(L.nbytes for L in dl) / len(dl)
+    dom_flops = sum(L.flops for L in dl) / len(dl)
+
+    if args.workload == "kv":
+        value = per_step_bytes / (step_ms / 1e3) / 1e9
+        metric, unit = "scaled fp8 KV cache quant+dequant GB/s (algorithmic bytes)", "GB/s"
+        dtype = "fp8e4m3"
+    else:
+        value = per_step_flops / (step_ms / 1e3) / 1e12
+        metric, unit = METRIC, "TFLOP/s"
+        dtype = "fp8e4m3" if spec["qtype"] == "fp8" else "int8"
+
+    if spec["bound"] == "hbm":
+        achieved = dom_bytes / dom_avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = dom_flops / dom_avg_s / 1e12
+        peak = MFMA_PEAK_TFLOPS[spec["qtype"]]
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+    roof["kernel"] = ("w8a8_scaled_mm" if dominant == "gemm" else "kv_fp8_scaled_quant")
+    roof["launches_per_step"] = len(dl)
+    roof["avg_launch_us"] = round(dom_avg_s * 1e6, 3)
+    roof["timing"] = "events in graph" if timed_in_graph else "graph of dominant launches"
+
+    if args.detail:
+        # per-launch times: each launch alone, graph of 10 back-to-back copies
+        for L in launches:
+            g3, _ = capture([L] * 10, stream)
+            g3.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(5):
+                g3.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / 50
+            log(f"[bench]   {L.label:40s} {us:9.2f} us  {L.nbytes / us / 1e3:8.1f} GB/s  "
+                f"{L.flops / us / 1e6:9.1f} TFLOP/s")
+
+    result = {
+        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic (seeded; Llama-3 layer shapes, bf16 N(0,1) activations with 1% "
+                "outlier channels x20, N(0,0.02) weights)" if args.workload != "kv" else
+                "synthetic (seeded; N(0,1) K/V with 0.1% outliers x10)",
+        "config": {"workload": spec["desc"], "mode": "hip-graph replay, inputs resident in HBM",
+                   "step_bytes": per_step_bytes, "step_flops": per_step_flops,
+                   "launches_per_step": len(launches), "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if args.cpu_budget > 0:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(spec, launches, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    stream_ctx.__exit__(None, None, None)
+    log(f"[bench] wall {wall:.3f}s for the timed loop")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

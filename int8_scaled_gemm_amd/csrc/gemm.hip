@@ -222,12 +222,16 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs p) {
         }
 }
 
-// M <= 16*TM rows; one workgroup per 16 columns; WAVES waves split the
-// 128-byte K slices round-robin (neighbouring waves read neighbouring
-// slices of the same weight rows); U slices per wave per step in flight.
-template <int QT, int OT, int TM, int WAVES, int U>
+// M <= 64 rows in up to 4 row-tiles of 16 (p.tiles_m of them, a runtime
+// value so that one kernel serves every decode batch size); one workgroup
+// per 16 columns; WAVES waves split the 128-byte K slices round-robin
+// (neighbouring waves read neighbouring slices of the same weight rows);
+// U slices per wave per step in flight.
+template <int QT, int OT, int WAVES, int U>
 __global__ __launch_bounds__(WAVES * 64) void gemm_decode_kernel(GemmArgs p) {
     typedef typename AccOf<QT>::type Acc;
+    constexpr int TM = 4;
+    const int mt = p.tiles_m;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n0 = blockIdx.x * 16;
     const int nrow = n0 + (lane & 15);
@@ -250,6 +254,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_decode_kernel(GemmArgs p) {
             bf[u] = join(lo ? load16(bp + k) : z, hi ? load16(bp + k + 16) : z);
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
+                if (i >= mt) break;
                 const int m = i * 16 + (lane & 15);
                 const uint8_t* ap = p.a + static_cast<int64_t>(m) * p.lda + k;
                 const bool mv = m < p.M;
@@ -259,15 +264,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_decode_kernel(GemmArgs p) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int i = 0; i < TM; ++i) mma<QT>(acc[i], af[u][i], bf[u]);
+            for (int i = 0; i < TM; ++i) {
+                if (i >= mt) break;
+                mma<QT>(acc[i], af[u][i], bf[u]);
+            }
     }
 
     // Add the waves' partial sums (fixed order), then the fused epilogue.
     __shared__ Acc red[WAVES][TM][64];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) red[wave][i][lane] = acc[i];
+    for (int i = 0; i < TM; ++i)
+        if (i < mt) red[wave][i][lane] = acc[i];
     __syncthreads();
-    for (int i = wave; i < TM; i += WAVES) {
+    for (int i = wave; i < mt; i += WAVES) {
         Acc s = red[0][i][lane];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) s += red[w][i][lane];
@@ -290,20 +299,18 @@ hipError_t run_tile(GemmArgs a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int QT, int OT, int TM>
+template <int QT, int OT>
 hipError_t run_decode(GemmArgs a, hipStream_t st) {
     constexpr int kWaves = 4, kU = 4;
+    a.tiles_m = (a.M + 15) / 16;
     const int grid = (a.N + 15) / 16;
-    hipLaunchKernelGGL((gemm_decode_kernel<QT, OT, TM, kWaves, kU>), dim3(grid), dim3(kWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((gemm_decode_kernel<QT, OT, kWaves, kU>), dim3(grid), dim3(kWaves * 64), 0, st, a);
     return hipGetLastError();
 }
 
 template <int QT, int OT>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
-    if (a.M <= 16) return run_decode<QT, OT, 1>(a, st);
-    if (a.M <= 32) return run_decode<QT, OT, 2>(a, st);
-    if (a.M <= 48) return run_decode<QT, OT, 3>(a, st);
-    if (a.M <= 64) return run_decode<QT, OT, 4>(a, st);
+    if (a.M <= 64) return run_decode<QT, OT>(a, st);
     // Enough 128 x 128 tiles to cover the 256 CUs, else halve the row tile.
     const int64_t big = ((a.M + 127) / 128) * ((a.N + 127) / 128);
     if (big >= 256) return run_tile<QT, OT, 128, 128>(a, st);

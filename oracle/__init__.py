@@ -84,11 +84,18 @@ def lib():
         L.oracle_kv_dequant.argtypes = [P, I64, P, P, I]
         L.oracle_scaled_mm.restype = None
         L.oracle_scaled_mm.argtypes = [P, I, I64, P, I64, P, I64, I, I64, I64, I64, P, I64, P, I64]
+        L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_num_threads.argtypes = []
         L.oracle_scaled_mm_rows.restype = None
         L.oracle_scaled_mm_rows.argtypes = [P, I, I64, P, I64, P, I64, P, I64, I, I64, I64,
                                             P, I64, P, I64]
         _lib = L
     return _lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(lib().oracle_num_threads())
 
 
 def _ptr(a):

@@ -32,6 +32,7 @@
  * float operation below must be IEEE).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -326,6 +327,9 @@ void oracle_scaled_mm_rows(void* out, int otype, int64_t ldo, const int64_t* row
         for (int64_t n = 0; n < N; ++n)
             mm_one(out, otype, ldo, i, a, lda, b, ldb, qtype, rows[i], n, K, sa, n_a, sb, n_b);
 }
+
+/* Threads the OpenMP loops above use. */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* Vector helpers for the tests. */
 void oracle_e4m3_encode_n(const float* v, int64_t n, uint8_t* q) {
