@@ -138,6 +138,8 @@ w8a8_status w8a8_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* a,
         return fail(W8A8_ERR_SHAPE, "%s: b_scales has %lld entries; need 1 (per tensor) or N=%lld (per channel)", fn, (long long)n_b, (long long)N);
     if (qt == W8A8_Q_INT8 && K > 131072)
         return fail(W8A8_ERR_UNSUPPORTED, "%s: int8 K=%lld could overflow the int32 accumulator (max 131072)", fn, (long long)K);
+    if (K > 0 && (lda > (int64_t{1} << 23) || ldb > (int64_t{1} << 23)))
+        return fail(W8A8_ERR_UNSUPPORTED, "%s: lda and ldb are limited to 2^23 bytes", fn);
     if (M == 0 || N == 0) return ok();
     if (!out) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL out", fn);
     if (K > 0 && (!a || !b)) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL a or b", fn);

@@ -51,6 +51,7 @@ struct GemmArgs {
     const float* sb;
     int sb_per_col;
     int tiles_m, tiles_n;
+    int vec_out;  // out and ldo allow 4-element vector stores
 };
 
 template <int QT>
@@ -121,54 +122,186 @@ __device__ __forceinline__ bool tile_coords(int pid, int tiles_m, int tiles_n, i
     return true;
 }
 
-constexpr int kBK = 128;            // K bytes per slice (one MFMA depth for fp8)
-constexpr int kLdsRow = kBK + 16;   // padded LDS row
+constexpr int kBK = 128;  // K bytes per slice (one MFMA depth for fp8)
 
-template <int QT, int OT, int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs p) {
-    typedef typename AccOf<QT>::type Acc;
-    constexpr int WM = BM / 2, WN = BN / 2;  // 2 x 2 waves
-    constexpr int TM = WM / 16, TN = WN / 16;
-    constexpr int AV = BM * kBK / 16 / 256;  // 16-byte vectors per lane per slice
-    constexpr int BV = BN * kBK / 16 / 256;
-    constexpr int kStage = (BM + BN) * kLdsRow;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+// ---------------------------------------------------------------------------
+// Direct global -> LDS loads (buffer_load_dwordx4 ... lds): lane q of the
+// issuing wave writes its 16 bytes at lds + 16 * q; an offset at or beyond the
+// resource's byte count reads as zero, which masks the tile edges.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) uint32_t* lds_u32p;
+__device__ void raw_buffer_load_lds(i32x4 rsrc, lds_u32p lds, int size, int voffset, int soffset,
+                                    int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+constexpr int kOutOfRange = 0x7FFFFFF0;
+
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t nbytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = static_cast<int>(static_cast<uint32_t>(a));
+    r[1] = static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu);  // stride 0
+    r[2] = static_cast<int>(nbytes);
+    r[3] = 0x00020000;  // raw buffer, 32-bit data format
+    return r;
+}
+
+// LDS layout of one 32-row x 128-byte operand group (4 KB), in the order the
+// 32 x 32 MFMAs consume it: half h (2 KB, K bytes 64h .. 64h+63) holds two
+// 1 KB sub-blocks s; entry p (16 bytes) of sub-block s is row p % 32 at K
+// bytes 64h + 32s + 16 (p / 32). One wave-wide direct load fills one
+// sub-block from 32 rows x 32 contiguous bytes, and a lane's reads of
+// 16-byte words at 16 * lane are bank-conflict free.
+//  - fp8 (v_mfma_f32_32x32x64_f8f6f4, 64 K per op): lane l's fragment for
+//    half h is sub-block 0 word l followed by sub-block 1 word l;
+//  - int8 (v_mfma_i32_32x32x32_i8, 32 K per op): sub-block s alone is the
+//    fragment of one op.
+// The K order inside a fragment differs from memory order; A and B use the
+// same order, so the sum is the same, and every run of 8 consecutive k stays
+// one input group of the fp8 matrix core.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+template <int QT>
+struct Acc32Of;
+template <>
+struct Acc32Of<Q_FP8> {
+    typedef f32x16 type;
+};
+template <>
+struct Acc32Of<Q_INT8> {
+    typedef i32x16 type;
+};
+
+// c += W_frag . X_frag over one 64-byte K half: the weight fragment is the
+// first operand, so the result's 32 x 32 tile has output columns (n) along
+// its rows and output rows (m) along lanes.
+template <int QT>
+__device__ __forceinline__ void mma32_half(typename Acc32Of<QT>::type& c, const uint8_t* wb,
+                                           const uint8_t* xb, int lane) {
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(wb + 16 * lane);
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(wb + 1024 + 16 * lane);
+    const u32x4 x0 = *reinterpret_cast<const u32x4*>(xb + 16 * lane);
+    const u32x4 x1 = *reinterpret_cast<const u32x4*>(xb + 1024 + 16 * lane);
+    if constexpr (QT == Q_FP8) {
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(join(w0, w1), join(x0, x1), c, 0, 0, 0,
+                                                            0, 0, 0);
+    } else {
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+            i32x4{static_cast<int>(w0[0]), static_cast<int>(w0[1]), static_cast<int>(w0[2]),
+                  static_cast<int>(w0[3])},
+            i32x4{static_cast<int>(x0[0]), static_cast<int>(x0[1]), static_cast<int>(x0[2]),
+                  static_cast<int>(x0[3])},
+            c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+            i32x4{static_cast<int>(w1[0]), static_cast<int>(w1[1]), static_cast<int>(w1[2]),
+                  static_cast<int>(w1[3])},
+            i32x4{static_cast<int>(x1[0]), static_cast<int>(x1[1]), static_cast<int>(x1[2]),
+                  static_cast<int>(x1[3])},
+            c, 0, 0, 0);
+    }
+}
+
+// Scale, round and store the 4 consecutive columns n..n+3 of row m.
+template <int OT, typename Acc>
+__device__ __forceinline__ void store4(const GemmArgs& p, int m, int n, const Acc& acc, int base,
+                                       bool vec) {
+    if (m >= p.M) return;
+    if constexpr (OT == D_I32) {
+        int32_t* o = static_cast<int32_t*>(p.out) + static_cast<int64_t>(m) * p.ldo + n;
+        if (vec && n + 3 < p.N) {
+            *reinterpret_cast<i32x4*>(o) =
+                i32x4{static_cast<int>(acc[base]), static_cast<int>(acc[base + 1]),
+                      static_cast<int>(acc[base + 2]), static_cast<int>(acc[base + 3])};
+        } else {
+            for (int r = 0; r < 4; ++r)
+                if (n + r < p.N) o[r] = static_cast<int32_t>(acc[base + r]);
+        }
+    } else {
+        const float sa = p.sa ? p.sa[p.sa_per_row ? m : 0] : 1.0f;
+        float d[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float sb = p.sb ? p.sb[p.sb_per_col ? min(n + r, p.N - 1) : 0] : 1.0f;
+            d[r] = static_cast<float>(acc[base + r]) * sa * sb;
+        }
+        const int64_t o = static_cast<int64_t>(m) * p.ldo + n;
+        if constexpr (OT == D_F32) {
+            float* out = static_cast<float*>(p.out) + o;
+            if (vec && n + 3 < p.N) {
+                *reinterpret_cast<f32x4*>(out) = f32x4{d[0], d[1], d[2], d[3]};
+            } else {
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < p.N) out[r] = d[r];
+            }
+        } else {
+            uint16_t h[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                h[r] = (OT == D_BF16) ? to_bf16_bits(d[r]) : to_fp16_bits(d[r]);
+            uint16_t* out = static_cast<uint16_t*>(p.out) + o;
+            if (vec && n + 3 < p.N) {
+                *reinterpret_cast<u32x2*>(out) = u32x2{h[0] | (static_cast<uint32_t>(h[1]) << 16),
+                                                       h[2] | (static_cast<uint32_t>(h[3]) << 16)};
+            } else {
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < p.N) out[r] = h[r];
+            }
+        }
+    }
+}
+
+// BM x BN block tile; WGM x WGN waves, each owning a (BM/WGM) x (BN/WGN)
+// wave tile of 32 x 32 MFMA tiles. K is walked in 128-byte slices through two
+// LDS stages filled by direct loads: the loads of slice k+1 are in flight
+// while the MFMAs consume slice k, with one barrier per slice.
+template <int QT, int OT, int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
+    typedef typename Acc32Of<QT>::type Acc;
+    constexpr int NW = WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int kStage = (BM + BN) * kBK;
+    constexpr int kLoads = (BM + BN) / 8;  // 1 KB wave-wide loads per stage
+    static_assert(TM >= 1 && TN >= 1 && kLoads % NW == 0, "tile shape");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
 
     int tm, tn;
     if (!tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn)) return;
     const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
 
-    u32x4 ra[AV], rb[BV];
-    auto gload = [&](int kt) {
-        const int k0 = kt * kBK;
+    const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
+    const i32x4 ra = buffer_rsrc(p.a + static_cast<int64_t>(m0) * p.lda,
+                                 static_cast<uint32_t>((rows_a - 1) * p.lda + p.K));
+    const i32x4 rb = buffer_rsrc(p.b + static_cast<int64_t>(n0) * p.ldb,
+                                 static_cast<uint32_t>((rows_b - 1) * p.ldb + p.K));
+    const int q_row = lane & 31, q_k = 16 * (lane >> 5);
+
+    // Per load: this lane's byte offset within the slice (or out of range).
+    int base_off[kLoads / NW];
 #pragma unroll
-        for (int j = 0; j < AV; ++j) {
-            const int v = tid + 256 * j, r = v >> 3, k = k0 + (v & 7) * 16;
-            const int gm = m0 + r;
-            ra[j] = (gm < p.M && k < p.K) ? load16(p.a + static_cast<int64_t>(gm) * p.lda + k)
-                                          : u32x4{0, 0, 0, 0};
-        }
+    for (int j = 0; j < kLoads / NW; ++j) {
+        const int i = wave + NW * j;
+        const bool is_a = i < BM / 8;
+        const int ii = is_a ? i : i - BM / 8;
+        const int row = 32 * (ii >> 2) + q_row;
+        base_off[j] = (row < (is_a ? rows_a : rows_b))
+                          ? row * static_cast<int>(is_a ? p.lda : p.ldb) + 32 * (ii & 3) + q_k
+                          : kOutOfRange;
+    }
+    auto issue = [&](int kt, int buf) {
+        uint8_t* st = smem + buf * kStage;
 #pragma unroll
-        for (int j = 0; j < BV; ++j) {
-            const int v = tid + 256 * j, r = v >> 3, k = k0 + (v & 7) * 16;
-            const int gn = n0 + r;
-            rb[j] = (gn < p.N && k < p.K) ? load16(p.b + static_cast<int64_t>(gn) * p.ldb + k)
-                                          : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto swrite = [&](int buf) {
-        uint8_t* s = smem + buf * kStage;
-#pragma unroll
-        for (int j = 0; j < AV; ++j) {
-            const int v = tid + 256 * j;
-            *reinterpret_cast<u32x4*>(s + (v >> 3) * kLdsRow + (v & 7) * 16) = ra[j];
-        }
-#pragma unroll
-        for (int j = 0; j < BV; ++j) {
-            const int v = tid + 256 * j;
-            *reinterpret_cast<u32x4*>(s + (BM + (v >> 3)) * kLdsRow + (v & 7) * 16) = rb[j];
+        for (int j = 0; j < kLoads / NW; ++j) {
+            const int i = wave + NW * j;
+            const bool is_a = i < BM / 8;
+            const int ii = is_a ? i : i - BM / 8;
+            const bool ok = base_off[j] != kOutOfRange && kt * kBK + 32 * (ii & 3) + q_k < p.K;
+            const int off = ok ? base_off[j] + kt * kBK : kOutOfRange;
+            uint8_t* dst = st + (is_a ? 0 : BM * kBK) + (ii >> 2) * 4096 + (ii & 3) * 1024;
+            raw_buffer_load_lds(is_a ? ra : rb, (lds_u32p)(dst), 16, off, 0, 0, 0);
         }
     };
 
@@ -176,50 +309,43 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
     const int KT = (p.K + kBK - 1) / kBK;
-    if (KT > 0) {
-        gload(0);
-        swrite(0);
-    }
-    __syncthreads();
-    const int frag_row = lane & 15, frag_k = (lane >> 4) * 32;
+    if (KT > 0) issue(0, 0);
     for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < KT) gload(kt + 1);
-        const uint8_t* s = smem + cur * kStage;
-        i32x8 af[TM], bf[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const uint8_t* q = s + (wm * WM + i * 16 + frag_row) * kLdsRow + frag_k;
-            af[i] = join(load16(q), load16(q + 16));
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const uint8_t* q = s + (BM + wn * WN + j * 16 + frag_row) * kLdsRow + frag_k;
-            bf[j] = join(load16(q), load16(q + 16));
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) mma<QT>(acc[i][j], af[i], bf[j]);
-        if (kt + 1 < KT) swrite(cur ^ 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        if (kt + 1 < KT) issue(kt + 1, cur ^ 1);
+        const uint8_t* sa = smem + cur * kStage;
+        const uint8_t* sb = sa + BM * kBK;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    mma32_half<QT>(acc[i][j], sb + (wn * TN + j) * 4096 + h * 2048,
+                                   sa + (wm * TM + i) * 4096 + h * 2048, lane);
     }
 
-    // Fused epilogue.
+    // Fused epilogue. In a 32 x 32 tile lane l holds, for q = 0..3, output
+    // row m = l % 32 and the 4 consecutive columns n = 8q + 4 (l / 32) + 0..3.
+    const bool vec = p.vec_out;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm * WM + i * 32 + (lane & 31);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = n0 + wn * WN + j * 16 + (lane & 15);
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + r;
-                if (m < p.M && n < p.N) store_out<OT>(p, m, n, acc[i][j][r]);
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+                if (n < p.N) store4<OT>(p, m, n, acc[i][j], 4 * q, vec);
             }
-        }
+    }
 }
 
 // M <= 64 rows in up to 4 row-tiles of 16 (p.tiles_m of them, a runtime
@@ -289,13 +415,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_decode_kernel(GemmArgs p) {
     }
 }
 
-template <int QT, int OT, int BM, int BN>
+template <int QT, int OT, int BM, int BN, int WGM, int WGN>
 hipError_t run_tile(GemmArgs a, hipStream_t st) {
     a.tiles_m = (a.M + BM - 1) / BM;
     a.tiles_n = (a.N + BN - 1) / BN;
     const int total = a.tiles_m * a.tiles_n;
     const int grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((gemm_tile_kernel<QT, OT, BM, BN>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_tile_kernel<QT, OT, BM, BN, WGM, WGN>), dim3(grid),
+                       dim3(WGM * WGN * 64), 0, st, a);
     return hipGetLastError();
 }
 
@@ -311,10 +438,14 @@ hipError_t run_decode(GemmArgs a, hipStream_t st) {
 template <int QT, int OT>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
     if (a.M <= 64) return run_decode<QT, OT>(a, st);
-    // Enough 128 x 128 tiles to cover the 256 CUs, else halve the row tile.
-    const int64_t big = ((a.M + 127) / 128) * ((a.N + 127) / 128);
-    if (big >= 256) return run_tile<QT, OT, 128, 128>(a, st);
-    return run_tile<QT, OT, 64, 128>(a, st);
+    // The largest tile that still gives every CU a block, else the smallest.
+    auto tiles = [&](int bm, int bn) {
+        return static_cast<int64_t>((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+    };
+    if (tiles(256, 256) >= 256) return run_tile<QT, OT, 256, 256, 2, 4>(a, st);
+    if (tiles(256, 128) >= 256) return run_tile<QT, OT, 256, 128, 4, 2>(a, st);
+    if (tiles(128, 128) >= 256) return run_tile<QT, OT, 128, 128, 2, 2>(a, st);
+    return run_tile<QT, OT, 64, 64, 2, 2>(a, st);
 }
 
 template <int QT>
@@ -348,6 +479,8 @@ hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st) {
     a.sb = p.sb;
     a.sb_per_col = p.sb_per_col ? 1 : 0;
     a.tiles_m = a.tiles_n = 0;
+    const int esz = (p.ot == D_BF16 || p.ot == D_FP16) ? 2 : 4;
+    a.vec_out = (reinterpret_cast<uintptr_t>(p.out) % (4 * esz) == 0) && (p.ldo % 4 == 0);
     if (p.qt == Q_FP8) return dispatch_ot<Q_FP8>(p.ot, a, st);
     return dispatch_ot<Q_INT8>(p.ot, a, st);
 }

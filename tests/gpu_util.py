@@ -76,6 +76,16 @@ def fp8_group_bound(a: np.ndarray, b: np.ndarray, group: int = 8) -> np.ndarray:
 FP8_GROUP_REL = 2.0 ** -10
 
 
+def check_scaled_mm_rows(got: torch.Tensor, rows, a: np.ndarray, b: np.ndarray, qtype: str,
+                         sa, sb, otype: str) -> dict:
+    """check_scaled_mm on a sample of output rows (for sizes where the full
+    oracle product would take too long)."""
+    rows = np.asarray(sorted(set(int(r) for r in rows)), np.int64)
+    sa_rows = sa if (sa is None or np.size(sa) == 1) else np.asarray(sa)[rows]
+    return check_scaled_mm(got[torch.from_numpy(rows).to(got.device)], a[rows], b, qtype,
+                           sa_rows, sb, otype)
+
+
 def check_scaled_mm(got: torch.Tensor, a: np.ndarray, b: np.ndarray, qtype: str, sa, sb,
                     otype: str, max_abs_rel: float = 1e-2) -> dict:
     """Compare a HIP scaled_mm output with the oracle.

@@ -12,7 +12,8 @@ import torch
 import int8_scaled_gemm_amd as w8
 import oracle
 import workloads
-from tests.gpu_util import DEV, TORCH_OF, bits, check_scaled_mm, codes_to_dev
+from tests.gpu_util import (DEV, TORCH_OF, bits, check_scaled_mm, check_scaled_mm_rows,
+                            codes_to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,6 +53,24 @@ SHAPES = [
 def test_scaled_mm_parity(qtype, M, N, K):
     a, sa, b, sb = _quantized(M, N, K, qtype, seed=M + N + K)
     info = check_scaled_mm(_run(a, b, qtype, sa, sb, "bf16"), a, b, qtype, sa, sb, "bf16")
+    assert info["exact_frac"] > 0.9, info
+
+
+# Shapes that select each block tile of the tiled kernel (256x256, 256x128,
+# 128x128, 64x128), with ragged M, N and K tails; checked on sampled rows.
+TILE_SHAPES = [(4096 + 37, 4096 + 48, 384 + 16), (2048, 4096 + 16, 272), (1024 + 5, 4096, 144),
+               (200, 300, 1040)]
+
+
+@pytest.mark.parametrize("qtype", ["fp8", "int8"])
+@pytest.mark.parametrize("M,N,K", TILE_SHAPES)
+def test_tile_configs_sampled_rows(qtype, M, N, K):
+    a, sa, b, sb = _quantized(M, N, K, qtype, seed=M + 2 * N + K)
+    got = _run(a, b, qtype, sa, sb, "bf16")
+    rng = np.random.default_rng(M)
+    rows = [0, 1, 15, 16, 255, 256, M - 1, M - 2] + list(rng.integers(0, M, 40))
+    rows = [r for r in rows if r < M]
+    info = check_scaled_mm_rows(got, rows, a, b, qtype, sa, sb, "bf16")
     assert info["exact_frac"] > 0.9, info
 
 
