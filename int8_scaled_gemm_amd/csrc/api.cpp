@@ -66,6 +66,72 @@ w8a8_status check_quant_io(const char* fn, const void* x, w8a8_dtype xt, int64_t
     return W8A8_OK;
 }
 
+static w8a8_status scaled_mm_impl(const char* fn, void* out, w8a8_dtype ot, int64_t ldo, const void* a,
+                                  int64_t lda, const void* b, int64_t ldb, w8a8_qtype qt, int64_t M,
+                                  int64_t N, int64_t K, const float* a_scales, int64_t n_a,
+                                  const float* b_scales, int64_t n_b, void* workspace,
+                                  int64_t workspace_bytes, bool with_ws, hipStream_t stream) {
+    if (!valid_qtype(qt)) return fail(W8A8_ERR_DTYPE, "%s: code type %d is not INT8 or FP8_E4M3FN", fn, qt);
+    if (ot != W8A8_BF16 && ot != W8A8_FP16 && ot != W8A8_F32 && ot != W8A8_I32)
+        return fail(W8A8_ERR_DTYPE, "%s: output type %d unknown", fn, ot);
+    if (ot == W8A8_I32 && qt != W8A8_Q_INT8)
+        return fail(W8A8_ERR_DTYPE, "%s: I32 output (raw accumulator) exists for int8 only", fn);
+    if (ot == W8A8_I32 && (a_scales || b_scales))
+        return fail(W8A8_ERR_INVALID_ARG, "%s: I32 output is the raw accumulator; scales must be NULL", fn);
+    if (M < 0 || N < 0 || K < 0)
+        return fail(W8A8_ERR_SHAPE, "%s: negative size M=%lld N=%lld K=%lld", fn, (long long)M, (long long)N, (long long)K);
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(W8A8_ERR_UNSUPPORTED, "%s: a size is above 2^31-1", fn);
+    if (lda < K) return fail(W8A8_ERR_LAYOUT, "%s: lda=%lld < K=%lld", fn, (long long)lda, (long long)K);
+    if (ldb < K)
+        return fail(W8A8_ERR_LAYOUT, "%s: ldb=%lld < K=%lld: B must be K x N column-major (rows of an [N, K] weight)", fn, (long long)ldb, (long long)K);
+    if (ldo < N) return fail(W8A8_ERR_LAYOUT, "%s: ldo=%lld < N=%lld", fn, (long long)ldo, (long long)N);
+    if (a_scales && n_a != 1 && n_a != M)
+        return fail(W8A8_ERR_SHAPE, "%s: a_scales has %lld entries; need 1 (per tensor) or M=%lld (per token)", fn, (long long)n_a, (long long)M);
+    if (b_scales && n_b != 1 && n_b != N)
+        return fail(W8A8_ERR_SHAPE, "%s: b_scales has %lld entries; need 1 (per tensor) or N=%lld (per channel)", fn, (long long)n_b, (long long)N);
+    if (qt == W8A8_Q_INT8 && K > 131072)
+        return fail(W8A8_ERR_UNSUPPORTED, "%s: int8 K=%lld could overflow the int32 accumulator (max 131072)", fn, (long long)K);
+    if (K > 0 && (lda > (int64_t{1} << 23) || ldb > (int64_t{1} << 23)))
+        return fail(W8A8_ERR_UNSUPPORTED, "%s: lda and ldb are limited to 2^23 bytes", fn);
+    if (M == 0 || N == 0) return ok();
+    if (!out) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL out", fn);
+    if (K > 0 && (!a || !b)) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL a or b", fn);
+    if (K % 16 || (K > 0 && (lda % 16 || ldb % 16)))
+        return fail(W8A8_ERR_ALIGNMENT, "%s: K, lda and ldb must be multiples of 16 (K=%lld lda=%lld ldb=%lld)", fn, (long long)K, (long long)lda, (long long)ldb);
+    if ((a && !aligned16(a)) || (b && !aligned16(b))) return fail(W8A8_ERR_ALIGNMENT, "%s: a and b must be 16-byte aligned", fn);
+    if (reinterpret_cast<uintptr_t>(out) % elem_size(ot)) return fail(W8A8_ERR_ALIGNMENT, "%s: out is not aligned to its element size", fn);
+    if ((a_scales && (reinterpret_cast<uintptr_t>(a_scales) & 3u)) || (b_scales && (reinterpret_cast<uintptr_t>(b_scales) & 3u)))
+        return fail(W8A8_ERR_ALIGNMENT, "%s: scale arrays must be 4-byte aligned", fn);
+    if (with_ws) {
+        const w8a8::DecodePlan d = w8a8::plan_decode(M, N, K);
+        if (d.workspace_bytes > 0) {
+            if (!workspace) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL workspace (%lld bytes needed)", fn, (long long)d.workspace_bytes);
+            if (workspace_bytes < d.workspace_bytes)
+                return fail(W8A8_ERR_INVALID_ARG, "%s: workspace of %lld bytes, %lld needed", fn, (long long)workspace_bytes, (long long)d.workspace_bytes);
+            if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(W8A8_ERR_ALIGNMENT, "%s: workspace must be 256-byte aligned", fn);
+        }
+    }
+    w8a8::GemmProblem p;
+    p.out = out;
+    p.ot = ot;
+    p.ldo = ldo;
+    p.a = static_cast<const uint8_t*>(a);
+    p.lda = lda;
+    p.b = static_cast<const uint8_t*>(b);
+    p.ldb = ldb;
+    p.qt = qt;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.sa = a_scales;
+    p.sa_per_row = a_scales && n_a == M && M != 1;
+    p.sb = b_scales;
+    p.sb_per_col = b_scales && n_b == N && N != 1;
+    p.splitk = with_ws;
+    p.workspace = with_ws ? workspace : nullptr;
+    return from_hip(w8a8::launch_scaled_mm(p, stream), fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -117,55 +183,27 @@ w8a8_status w8a8_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* a,
                            const void* b, int64_t ldb, w8a8_qtype qt, int64_t M, int64_t N,
                            int64_t K, const float* a_scales, int64_t n_a, const float* b_scales,
                            int64_t n_b, hipStream_t stream) {
-    const char* fn = "w8a8_scaled_mm";
+    return scaled_mm_impl("w8a8_scaled_mm", out, ot, ldo, a, lda, b, ldb, qt, M, N, K, a_scales, n_a,
+                          b_scales, n_b, nullptr, 0, false, stream);
+}
+
+w8a8_status w8a8_scaled_mm_workspace_size(w8a8_qtype qt, int64_t M, int64_t N, int64_t K,
+                                          int64_t* bytes) {
+    const char* fn = "w8a8_scaled_mm_workspace_size";
     if (!valid_qtype(qt)) return fail(W8A8_ERR_DTYPE, "%s: code type %d is not INT8 or FP8_E4M3FN", fn, qt);
-    if (ot != W8A8_BF16 && ot != W8A8_FP16 && ot != W8A8_F32 && ot != W8A8_I32)
-        return fail(W8A8_ERR_DTYPE, "%s: output type %d unknown", fn, ot);
-    if (ot == W8A8_I32 && qt != W8A8_Q_INT8)
-        return fail(W8A8_ERR_DTYPE, "%s: I32 output (raw accumulator) exists for int8 only", fn);
-    if (ot == W8A8_I32 && (a_scales || b_scales))
-        return fail(W8A8_ERR_INVALID_ARG, "%s: I32 output is the raw accumulator; scales must be NULL", fn);
-    if (M < 0 || N < 0 || K < 0)
-        return fail(W8A8_ERR_SHAPE, "%s: negative size M=%lld N=%lld K=%lld", fn, (long long)M, (long long)N, (long long)K);
-    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(W8A8_ERR_UNSUPPORTED, "%s: a size is above 2^31-1", fn);
-    if (lda < K) return fail(W8A8_ERR_LAYOUT, "%s: lda=%lld < K=%lld", fn, (long long)lda, (long long)K);
-    if (ldb < K)
-        return fail(W8A8_ERR_LAYOUT, "%s: ldb=%lld < K=%lld: B must be K x N column-major (rows of an [N, K] weight)", fn, (long long)ldb, (long long)K);
-    if (ldo < N) return fail(W8A8_ERR_LAYOUT, "%s: ldo=%lld < N=%lld", fn, (long long)ldo, (long long)N);
-    if (a_scales && n_a != 1 && n_a != M)
-        return fail(W8A8_ERR_SHAPE, "%s: a_scales has %lld entries; need 1 (per tensor) or M=%lld (per token)", fn, (long long)n_a, (long long)M);
-    if (b_scales && n_b != 1 && n_b != N)
-        return fail(W8A8_ERR_SHAPE, "%s: b_scales has %lld entries; need 1 (per tensor) or N=%lld (per channel)", fn, (long long)n_b, (long long)N);
-    if (qt == W8A8_Q_INT8 && K > 131072)
-        return fail(W8A8_ERR_UNSUPPORTED, "%s: int8 K=%lld could overflow the int32 accumulator (max 131072)", fn, (long long)K);
-    if (K > 0 && (lda > (int64_t{1} << 23) || ldb > (int64_t{1} << 23)))
-        return fail(W8A8_ERR_UNSUPPORTED, "%s: lda and ldb are limited to 2^23 bytes", fn);
-    if (M == 0 || N == 0) return ok();
-    if (!out) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL out", fn);
-    if (K > 0 && (!a || !b)) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL a or b", fn);
-    if (K % 16 || (K > 0 && (lda % 16 || ldb % 16)))
-        return fail(W8A8_ERR_ALIGNMENT, "%s: K, lda and ldb must be multiples of 16 (K=%lld lda=%lld ldb=%lld)", fn, (long long)K, (long long)lda, (long long)ldb);
-    if ((a && !aligned16(a)) || (b && !aligned16(b))) return fail(W8A8_ERR_ALIGNMENT, "%s: a and b must be 16-byte aligned", fn);
-    if (reinterpret_cast<uintptr_t>(out) % elem_size(ot)) return fail(W8A8_ERR_ALIGNMENT, "%s: out is not aligned to its element size", fn);
-    if ((a_scales && (reinterpret_cast<uintptr_t>(a_scales) & 3u)) || (b_scales && (reinterpret_cast<uintptr_t>(b_scales) & 3u)))
-        return fail(W8A8_ERR_ALIGNMENT, "%s: scale arrays must be 4-byte aligned", fn);
-    w8a8::GemmProblem p;
-    p.out = out;
-    p.ot = ot;
-    p.ldo = ldo;
-    p.a = static_cast<const uint8_t*>(a);
-    p.lda = lda;
-    p.b = static_cast<const uint8_t*>(b);
-    p.ldb = ldb;
-    p.qt = qt;
-    p.M = M;
-    p.N = N;
-    p.K = K;
-    p.sa = a_scales;
-    p.sa_per_row = a_scales && n_a == M && M != 1;
-    p.sb = b_scales;
-    p.sb_per_col = b_scales && n_b == N && N != 1;
-    return from_hip(w8a8::launch_scaled_mm(p, stream), fn);
+    if (!bytes) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL bytes", fn);
+    if (M < 0 || N < 0 || K < 0) return fail(W8A8_ERR_SHAPE, "%s: negative size", fn);
+    *bytes = w8a8::plan_decode(M, N, K).workspace_bytes;
+    return ok();
+}
+
+w8a8_status w8a8_scaled_mm_ws(void* out, w8a8_dtype ot, int64_t ldo, const void* a, int64_t lda,
+                              const void* b, int64_t ldb, w8a8_qtype qt, int64_t M, int64_t N,
+                              int64_t K, const float* a_scales, int64_t n_a, const float* b_scales,
+                              int64_t n_b, void* workspace, int64_t workspace_bytes,
+                              hipStream_t stream) {
+    return scaled_mm_impl("w8a8_scaled_mm_ws", out, ot, ldo, a, lda, b, ldb, qt, M, N, K, a_scales,
+                          n_a, b_scales, n_b, workspace, workspace_bytes, true, stream);
 }
 
 w8a8_status kv_fp8_scaled_quant(const void* x, w8a8_dtype xt, int64_t n, uint8_t* q, float* scale,

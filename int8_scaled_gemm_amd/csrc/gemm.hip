@@ -31,6 +31,9 @@
 //    added through LDS before the epilogue.
 // The epilogue is fused: scales applied in fp32 and the result rounded to
 // nearest even into bf16/fp16 in registers, then stored once.
+#include <algorithm>
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -52,6 +55,11 @@ struct GemmArgs {
     int sb_per_col;
     int tiles_m, tiles_n;
     int vec_out;  // out and ldo allow 4-element vector stores
+    // split-K decode: partial sums [splits][M][N] and one arrival counter per
+    // 64-column tile, both in the caller's workspace
+    void* ws_part;
+    uint32_t* ws_count;
+    int splits, slices_per_split;
 };
 
 template <int QT>
@@ -415,6 +423,146 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_decode_kernel(GemmArgs p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Split-K decode kernel, M <= 16*MT rows. A block owns 64 output columns (one
+// 16-column tile per wave) and a range of K slices. The 4 waves share the
+// activation rows, staged through LDS one 1 KB K-chunk at a time with
+// row-contiguous direct loads (row stride padded by 16 bytes, so the 16-row
+// fragment reads spread over the banks); each wave streams its own weight
+// rows straight from HBM with non-temporal loads, the whole chunk (8 slices,
+// 16 loads per lane) in flight at once. With splits > 1 every block writes
+// its fp32 (int32 for int8) partial tile to the workspace; the last block to
+// arrive on a column tile adds the partials in split order (deterministic),
+// applies the fused epilogue and resets the tile's counter to zero.
+// ---------------------------------------------------------------------------
+constexpr int kDecChunk = 1024;
+constexpr int kDecRow = kDecChunk + 16;
+
+__device__ __forceinline__ u32x4 load16_nt(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+template <int QT, int OT, int MT>
+__global__ __launch_bounds__(256) void gemm_decode_sk_kernel(GemmArgs p) {
+    typedef typename AccOf<QT>::type Acc;
+    __shared__ __attribute__((aligned(16))) uint8_t sa_lds[MT * 16 * kDecRow];
+    __shared__ int last_block;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = p.splits;
+    const int ct = blockIdx.x / S, sp = blockIdx.x % S;
+    const int n0 = ct * 64 + wave * 16;
+    const int KS = (p.K + kBK - 1) / kBK;
+    const int s0 = sp * p.slices_per_split, s1 = min(KS, s0 + p.slices_per_split);
+    const int kbeg = s0 * kBK, kend = min(p.K, s1 * kBK);
+    const int mt = p.tiles_m;  // 16-row tiles of A, <= MT
+    const int g = lane >> 4;
+
+    const i32x4 ra = buffer_rsrc(p.a, static_cast<uint32_t>((p.M - 1) * p.lda + p.K));
+    const int nrow = n0 + (lane & 15);
+    const uint8_t* bp = p.b + static_cast<int64_t>(nrow < p.N ? nrow : p.N - 1) * p.ldb + 16 * g;
+    const bool nvalid = nrow < p.N;
+
+    Acc acc[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[i] = Acc{0, 0, 0, 0};
+
+    const u32x4 z = {0, 0, 0, 0};
+    for (int kc = kbeg; kc < kend; kc += kDecChunk) {
+        // A chunk -> LDS: one wave-wide 1 KB load per row
+        for (int r = wave; r < 16 * mt; r += 4) {
+            const int k = kc + 16 * lane;
+            const int off = (r < p.M && k < kend) ? r * static_cast<int>(p.lda) + k : kOutOfRange;
+            raw_buffer_load_lds(ra, (lds_u32p)(sa_lds + r * kDecRow), 16, off, 0, 0, 0);
+        }
+        // this wave's weight fragments for the chunk: lane group g takes K
+        // bytes 16g..16g+15 and 64+16g..64+16g+15 of each 128-byte slice
+        constexpr int U = kDecChunk / kBK;
+        i32x8 wf[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = kc + u * kBK;
+            const bool lo = nvalid && k + 16 * g < kend, hi = nvalid && k + 64 + 16 * g < kend;
+            wf[u] = join(lo ? load16_nt(bp + k) : z, hi ? load16_nt(bp + k + 64) : z);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                if (i >= mt) break;
+                const uint8_t* ar = sa_lds + (16 * i + (lane & 15)) * kDecRow + u * kBK + 16 * g;
+                const i32x8 af = join(*reinterpret_cast<const u32x4*>(ar),
+                                      *reinterpret_cast<const u32x4*>(ar + 64));
+                mma<QT>(acc[i], af, wf[u]);
+            }
+        }
+        __syncthreads();  // the next chunk overwrites the staged rows
+    }
+
+    const int n = n0 + (lane & 15);
+    if (S == 1) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            if (i >= mt) break;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 16 * i + 4 * g + r;
+                if (m < p.M && n < p.N) store_out<OT>(p, m, n, acc[i][r]);
+            }
+        }
+        return;
+    }
+
+    // Partial tile -> workspace, then the last arriving block reduces. The
+    // partials travel with agent-coherent (L2 write-through / L2-bypassing)
+    // atomic stores and loads, and each block waits for its stores to be
+    // acknowledged before it counts itself in, so no cache-wide write-back or
+    // invalidate (an agent-scope fence) is needed.
+    typedef typename std::conditional<QT == Q_FP8, float, int32_t>::type Part;
+    Part* part = static_cast<Part*>(p.ws_part);
+    const int64_t plane = static_cast<int64_t>(p.M) * p.N;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        if (i >= mt) break;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 16 * i + 4 * g + r;
+            if (m < p.M && n < p.N)
+                __hip_atomic_store(part + sp * plane + static_cast<int64_t>(m) * p.N + n,
+                                   static_cast<Part>(acc[i][r]), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        last_block = __hip_atomic_fetch_add(p.ws_count + ct, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(S - 1);
+    __syncthreads();
+    if (!last_block) return;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        if (i >= mt) break;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 16 * i + 4 * g + r;
+            if (m < p.M && n < p.N) {
+                const int64_t o = static_cast<int64_t>(m) * p.N + n;
+                Part sum = __hip_atomic_load(part + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int q = 1; q < S; ++q)
+                    sum += __hip_atomic_load(part + q * plane + o, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+                store_out<OT>(p, m, n, sum);
+            }
+        }
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(p.ws_count + ct, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int QT, int OT, int BM, int BN, int WGM, int WGN>
 hipError_t run_tile(GemmArgs a, hipStream_t st) {
     a.tiles_m = (a.M + BM - 1) / BM;
@@ -436,7 +584,21 @@ hipError_t run_decode(GemmArgs a, hipStream_t st) {
 }
 
 template <int QT, int OT>
+hipError_t run_decode_sk(GemmArgs a, hipStream_t st) {
+    a.tiles_m = (a.M + 15) / 16;
+    const int grid = ((a.N + 63) / 64) * a.splits;
+    if (a.tiles_m <= 1)
+        hipLaunchKernelGGL((gemm_decode_sk_kernel<QT, OT, 1>), dim3(grid), dim3(256), 0, st, a);
+    else if (a.tiles_m <= 2)
+        hipLaunchKernelGGL((gemm_decode_sk_kernel<QT, OT, 2>), dim3(grid), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((gemm_decode_sk_kernel<QT, OT, 4>), dim3(grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int QT, int OT>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
+    if (a.M <= 64 && a.splits > 0) return run_decode_sk<QT, OT>(a, st);
     if (a.M <= 64) return run_decode<QT, OT>(a, st);
     // The largest tile that still gives every CU a block, else the smallest.
     auto tiles = [&](int bm, int bn) {
@@ -462,6 +624,30 @@ hipError_t dispatch_ot(int ot, const GemmArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// The workspace starts with a fixed region of tile counters, so that the
+// partial sums of one call never land where another call keeps its counters.
+constexpr int64_t kCounterBytes = 65536;
+
+DecodePlan plan_decode(int64_t M, int64_t N, int64_t K) {
+    DecodePlan d{0, 0, 0};
+    if (M < 1 || M > 64 || N < 1) return d;
+    const int64_t tiles = (N + 63) / 64;
+    const int64_t slices = (K + kBK - 1) / kBK;
+    // Measured on MI355X (Llama-3-8B decode shapes, M = 1..64): the 64-column
+    // split-K kernel wins once N gives at least 256 column tiles (gate_up,
+    // 28672 wide), where two splits keep ~900 workgroups in flight; on
+    // narrower N its partial-sum traffic (splits x M x N x 4 bytes each way)
+    // costs more than it saves, and the 16-column kernel without a workspace
+    // is faster. splits == 0 selects that kernel.
+    if (tiles < 256 || tiles * 4 > kCounterBytes) return d;
+    const int64_t splits = std::max<int64_t>(1, std::min<int64_t>(2, slices / 4));
+    d.splits = static_cast<int>(splits);
+    d.slices_per_split = static_cast<int>((slices + splits - 1) / splits);
+    if (d.slices_per_split == 0) d.slices_per_split = 1;
+    if (splits > 1) d.workspace_bytes = kCounterBytes + splits * M * N * 4;
+    return d;
+}
+
 hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     GemmArgs a;
@@ -481,6 +667,17 @@ hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st) {
     a.tiles_m = a.tiles_n = 0;
     const int esz = (p.ot == D_BF16 || p.ot == D_FP16) ? 2 : 4;
     a.vec_out = (reinterpret_cast<uintptr_t>(p.out) % (4 * esz) == 0) && (p.ldo % 4 == 0);
+    a.ws_part = nullptr;
+    a.ws_count = nullptr;
+    a.splits = 0;
+    a.slices_per_split = 0;
+    if (p.splitk && p.M <= 64) {
+        const DecodePlan d = plan_decode(p.M, p.N, p.K);  // splits == 0: plain decode kernel
+        a.splits = d.splits;
+        a.slices_per_split = d.slices_per_split;
+        a.ws_count = static_cast<uint32_t*>(p.workspace);
+        a.ws_part = static_cast<uint8_t*>(p.workspace) + kCounterBytes;
+    }
     if (p.qt == Q_FP8) return dispatch_ot<Q_FP8>(p.ot, a, st);
     return dispatch_ot<Q_INT8>(p.ot, a, st);
 }
