@@ -177,6 +177,14 @@ w8a8_status kv_fp8_scaled_quant(const void* x, w8a8_dtype xt, int64_t n, uint8_t
 w8a8_status kv_fp8_scaled_dequant(const uint8_t* q, int64_t n, const float* scale, void* x,
                                   w8a8_dtype xt, hipStream_t stream);
 
+/*
+ * Name of the kernel configuration that w8a8_scaled_mm (with_workspace = 0)
+ * or w8a8_scaled_mm_ws (1) runs for an M x N x K problem, such as
+ * "gemm_decode_kernel" or "gemm_tile_kernel<256x256>" (static string, ""
+ * for negative sizes), so that profiles can be matched to calls.
+ */
+const char* w8a8_scaled_mm_kernel(int64_t M, int64_t N, int64_t K, int with_workspace);
+
 /* Name of a status code (static string). */
 const char* w8a8_status_string(w8a8_status s);
 

@@ -90,6 +90,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.w8a8_last_error.restype = ctypes.c_char_p
     lib.w8a8_version.argtypes = []
     lib.w8a8_version.restype = ctypes.c_char_p
+    lib.w8a8_scaled_mm_kernel.argtypes = [_I64, _I64, _I64, _I]
+    lib.w8a8_scaled_mm_kernel.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -291,11 +293,16 @@ def scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor | None,
     return w8a8_scaled_mm(a, b, scale_a, scale_b, out_dtype, out)
 
 
+def w8a8_scaled_mm_kernel(M: int, N: int, K: int, with_workspace: bool = True) -> str:
+    """Kernel configuration the library runs for an M x N x K problem."""
+    return load_library().w8a8_scaled_mm_kernel(M, N, K, 1 if with_workspace else 0).decode()
+
+
 def version() -> str:
     return load_library().w8a8_version().decode()
 
 
 __all__ = ["w8a8_quant_per_token", "w8a8_quant_per_tensor", "w8a8_scaled_mm",
-           "w8a8_scaled_mm_workspace_size", "workspace_for",
+           "w8a8_scaled_mm_workspace_size", "w8a8_scaled_mm_kernel", "workspace_for",
            "kv_fp8_scaled_quant", "kv_fp8_scaled_dequant", "scaled_mm", "W8A8Error",
            "load_library", "version", "LIB_PATH", "SIGNATURES"]

@@ -187,6 +187,11 @@ w8a8_status w8a8_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* a,
                           b_scales, n_b, nullptr, 0, false, stream);
 }
 
+const char* w8a8_scaled_mm_kernel(int64_t M, int64_t N, int64_t K, int with_workspace) {
+    if (M < 0 || N < 0 || K < 0) return "";
+    return w8a8::scaled_mm_kernel_name(M, N, K, with_workspace != 0);
+}
+
 w8a8_status w8a8_scaled_mm_workspace_size(w8a8_qtype qt, int64_t M, int64_t N, int64_t K,
                                           int64_t* bytes) {
     const char* fn = "w8a8_scaled_mm_workspace_size";

@@ -596,18 +596,45 @@ hipError_t run_decode_sk(GemmArgs a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// The kernel configuration a problem runs with (shared by the launch and by
+// scaled_mm_kernel_name, so that profiles can be matched to launches).
+enum Config {
+    kDecode,         // gemm_decode_kernel: 16 columns per workgroup, K split over its waves
+    kDecodeSplit1,   // gemm_decode_sk_kernel<MT = 1>
+    kDecodeSplit2,   // gemm_decode_sk_kernel<MT = 2>
+    kDecodeSplit4,   // gemm_decode_sk_kernel<MT = 4>
+    kTile256x256,    // gemm_tile_kernel 256 x 256, 8 waves
+    kTile256x128,    // gemm_tile_kernel 256 x 128, 8 waves
+    kTile128x128,    // gemm_tile_kernel 128 x 128, 4 waves
+    kTile64x64,      // gemm_tile_kernel 64 x 64, 4 waves
+};
+
+Config select_config(int64_t M, int64_t N, bool splitk_planned) {
+    if (M <= 64) {
+        if (!splitk_planned) return kDecode;
+        const int64_t mt = (M + 15) / 16;
+        return mt <= 1 ? kDecodeSplit1 : (mt <= 2 ? kDecodeSplit2 : kDecodeSplit4);
+    }
+    // The largest tile that still gives every CU a block, else the smallest.
+    auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (tiles(256, 256) >= 256) return kTile256x256;
+    if (tiles(256, 128) >= 256) return kTile256x128;
+    if (tiles(128, 128) >= 256) return kTile128x128;
+    return kTile64x64;
+}
+
 template <int QT, int OT>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
-    if (a.M <= 64 && a.splits > 0) return run_decode_sk<QT, OT>(a, st);
-    if (a.M <= 64) return run_decode<QT, OT>(a, st);
-    // The largest tile that still gives every CU a block, else the smallest.
-    auto tiles = [&](int bm, int bn) {
-        return static_cast<int64_t>((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
-    };
-    if (tiles(256, 256) >= 256) return run_tile<QT, OT, 256, 256, 2, 4>(a, st);
-    if (tiles(256, 128) >= 256) return run_tile<QT, OT, 256, 128, 4, 2>(a, st);
-    if (tiles(128, 128) >= 256) return run_tile<QT, OT, 128, 128, 2, 2>(a, st);
-    return run_tile<QT, OT, 64, 64, 2, 2>(a, st);
+    switch (select_config(a.M, a.N, a.splits > 0)) {
+        case kDecode: return run_decode<QT, OT>(a, st);
+        case kDecodeSplit1:
+        case kDecodeSplit2:
+        case kDecodeSplit4: return run_decode_sk<QT, OT>(a, st);
+        case kTile256x256: return run_tile<QT, OT, 256, 256, 2, 4>(a, st);
+        case kTile256x128: return run_tile<QT, OT, 256, 128, 4, 2>(a, st);
+        case kTile128x128: return run_tile<QT, OT, 128, 128, 2, 2>(a, st);
+        default: return run_tile<QT, OT, 64, 64, 2, 2>(a, st);
+    }
 }
 
 template <int QT>
@@ -680,6 +707,20 @@ hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st) {
     }
     if (p.qt == Q_FP8) return dispatch_ot<Q_FP8>(p.ot, a, st);
     return dispatch_ot<Q_INT8>(p.ot, a, st);
+}
+
+const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K, bool splitk) {
+    const bool planned = splitk && M <= 64 && plan_decode(M, N, K).splits > 0;
+    switch (select_config(M, N, planned)) {
+        case kDecode: return "gemm_decode_kernel";
+        case kDecodeSplit1: return "gemm_decode_sk_kernel<MT=1>";
+        case kDecodeSplit2: return "gemm_decode_sk_kernel<MT=2>";
+        case kDecodeSplit4: return "gemm_decode_sk_kernel<MT=4>";
+        case kTile256x256: return "gemm_tile_kernel<256x256>";
+        case kTile256x128: return "gemm_tile_kernel<256x128>";
+        case kTile128x128: return "gemm_tile_kernel<128x128>";
+        default: return "gemm_tile_kernel<64x64>";
+    }
 }
 
 }  // namespace w8a8

@@ -46,4 +46,7 @@ DecodePlan plan_decode(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st);
 
+// Name of the kernel configuration a problem runs with.
+const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K, bool splitk);
+
 }  // namespace w8a8

@@ -300,8 +300,11 @@ hipError_t per_tensor_typed(const void* x, int64_t M, int64_t K, int64_t ldx, ui
     const Units u = make_units(M, K);
     const int g = grid_for(u.total, kUnroll);
     if (dynamic) {
+        // Every absmax workgroup merges its result with one atomic on the
+        // same word: keep them few (two per CU), each striding over the data.
+        const int ga = g < 512 ? g : 512;
         hipLaunchKernelGGL(fill_f32_kernel, dim3(1), dim3(1), 0, st, scale, 0.0f);
-        hipLaunchKernelGGL((absmax_kernel<XT>), dim3(g), dim3(kBlock), 0, st, x, ldx, u, K, scale);
+        hipLaunchKernelGGL((absmax_kernel<XT>), dim3(ga), dim3(kBlock), 0, st, x, ldx, u, K, scale);
         hipLaunchKernelGGL((quant_tensor_kernel<XT, QT, true>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, static_cast<const float*>(scale), u, K);
         hipLaunchKernelGGL((finalize_scale_kernel<QT>), dim3(1), dim3(1), 0, st, scale);
     } else {
