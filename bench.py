@@ -25,8 +25,17 @@ Weights are quantised once before timing (offline preparation). Every
 and the 256 MB last-level cache holds no weight from one use to the next.
 
 Prints one JSON line: the workload's throughput, a roofline entry for the
-dominant kernel (its launches timed with HIP events inside the replayed
-graph) and the CPU oracle timed on a bounded sample of the same workload.
+kernel that takes the most time per step (the step's launches of that kernel
+captured alone and replayed, timed with HIP events on the launch stream), the
+same figures for every kernel, and the CPU oracle timed on a bounded sample of
+the same workload. The roofline's `traffic` is the HBM traffic per launch from
+the rocprofv3 FETCH_SIZE / WRITE_SIZE record under profiles/, when that record
+was taken from the current kernel sources (else null).
+
+    python bench.py --copy-calibration
+
+runs only a plain device copy of 256 MiB, four times: the FETCH_SIZE and
+WRITE_SIZE counters read for it calibrate those of the kernels.
 """
 from __future__ import annotations
 
@@ -60,8 +69,14 @@ def log(*a):
 # names the kernel family, and units are its algorithmic flops and bytes.
 # --------------------------------------------------------------------------
 class Launch:
-    def __init__(self, kind, fn, flops, nbytes, label):
-        self.kind, self.fn, self.flops, self.nbytes, self.label = kind, fn, flops, nbytes, label
+    """One library call of a step. `kernel` names the kernel configuration it
+    runs (several calls of one step can share it); `flops` and `nbytes` are
+    its algorithmic work: 2*M*N*K, and every operand, scale and output byte
+    read or written once."""
+
+    def __init__(self, kind, fn, flops, nbytes, label, kernel):
+        self.kind, self.fn, self.flops, self.nbytes = kind, fn, flops, nbytes
+        self.label, self.kernel = label, kernel
 
 
 def _gemm_bytes(M, N, K, n_sa, n_sb, out_bytes=2):
@@ -96,11 +111,18 @@ def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
                 qbytes = 3 * M * K + 4
             mf = (lambda q=q, wq=wq, s=s, ws=ws, out=out:
                   w8.w8a8_scaled_mm(q, wq.t(), s, ws, torch.bfloat16, out=out))
-            launches.append(Launch("quant", qf, 0, qbytes, f"quant M={M} {name}"))
+            qkern = ("quant_rows_kernel" if act_scheme == "per_token" else "quant_tensor_kernel")
+            launches.append(Launch("quant", qf, 0, qbytes, f"quant M={M} {name}", qkern))
             launches.append(Launch("gemm", mf, 2 * M * N * K, _gemm_bytes(M, N, K, n_sa, N),
-                                   f"gemm M={M} {name} {N}x{K}"))
+                                   f"gemm M={M} {name} {N}x{K}",
+                                   w8.w8a8_scaled_mm_kernel(M, N, K, with_workspace=True)))
             keep += [wq, ws, x, q, s, out]
     return launches, keep
+
+
+# A dynamic per-tensor quantisation is one library call of four kernels: zero
+# the max, the absmax reduction, the quantisation, and max -> scale.
+KV_QUANT_KERNELS = "fill_f32_kernel+absmax_kernel+quant_tensor_kernel+finalize_scale_kernel"
 
 
 def build_kv_workload(dev, layers=workloads.KV_LAYERS):
@@ -116,17 +138,20 @@ def build_kv_workload(dev, layers=workloads.KV_LAYERS):
             y = torch.empty(workloads.KV_SHAPE, dtype=torch.bfloat16, device=dev)
             launches.append(Launch("kv_quant",
                                    lambda x=x, q=q, s=s: w8.kv_fp8_scaled_quant(x, scale=s, q=q),
-                                   0, 2 * n + n + 2 * n, f"kv quant L{layer}{which}"))
+                                   0, 2 * n + n + 2 * n, f"kv quant L{layer}{which}",
+                                   KV_QUANT_KERNELS))
             launches.append(Launch("kv_dequant",
                                    lambda q=q, s=s, y=y: w8.kv_fp8_scaled_dequant(q, s, out=y),
-                                   0, n + 2 * n, f"kv dequant L{layer}{which}"))
+                                   0, n + 2 * n, f"kv dequant L{layer}{which}",
+                                   "kv_dequant_kernel"))
             keep += [x, q, s, y]
     M, K = workloads.PER_TOKEN_STANDALONE
     x = workloads.activations(M, K, seed=0, device=dev)
     q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
     s = torch.empty(M, dtype=torch.float32, device=dev)
     launches.append(Launch("quant", lambda: w8.w8a8_quant_per_token(x, "fp8", q=q, scales=s),
-                           0, 3 * M * K + 4 * M, "per-token quant 8192x4096"))
+                           0, 3 * M * K + 4 * M, "per-token quant 8192x4096",
+                           "quant_rows_kernel"))
     keep += [x, q, s]
     return launches, keep
 
@@ -136,42 +161,104 @@ WORKLOADS = {
                         "dynamic per-token activation quant + scaled_mm, per-channel weights, "
                         "bf16 out",
                    layers=workloads.LLAMA3_8B_LAYERS, Ms=workloads.FP8_DECODE_M, qtype="fp8",
-                   act="per_token", dominant="gemm", bound="hbm"),
+                   act="per_token", cpu_n_frac=1),
     "prefill": dict(desc="fp8 e4m3 prefill GEMMs, Llama-3-8B QKV/O/gate_up/down at "
                          "M=512,2048,8192: static per-tensor activation quant + scaled_mm, "
                          "per-channel weights, bf16 out",
                     layers=workloads.LLAMA3_8B_LAYERS, Ms=workloads.FP8_PREFILL_M, qtype="fp8",
-                    act="per_tensor_static", dominant="gemm", bound="mfma"),
+                    act="per_tensor_static", cpu_n_frac=2),
     "int8": dict(desc="int8 w8a8 GEMMs, Llama-3-70B unsharded QKV/O/gate_up/down at "
                       "M=1,64,4096: per-token int8 activations + scaled_mm, per-channel int8 "
                       "weights, int32 accumulate, bf16 out",
                  layers=workloads.LLAMA3_70B_LAYERS, Ms=workloads.INT8_70B_M, qtype="int8",
-                 act="per_token", dominant="gemm", bound="mfma"),
+                 act="per_token", cpu_n_frac=1),
     "kv": dict(desc="scaled fp8 KV cache: per-tensor dynamic quant + dequant of 32 layers of "
                     "K and V [32768,8,128] bf16, plus per-token fp8 quant of [8192,4096]",
-               dominant="kv_quant", bound="hbm"),
+               ),
 }
 
 
 # --------------------------------------------------------------------------
-def capture(launches, stream, timed_kind=None):
-    """Capture every launch into one graph. With timed_kind, each launch of
-    that kind is bracketed by a pair of externally recorded timing events."""
+def capture(launches, stream):
+    """Capture the launches, in order, into one graph on `stream`."""
     g = torch.cuda.CUDAGraph()
-    pairs = []
     with torch.cuda.stream(stream):
         with torch.cuda.graph(g, stream=stream):
             for L in launches:
-                if timed_kind is not None and L.kind == timed_kind:
-                    e0 = torch.cuda.Event(enable_timing=True, external=True)
-                    e1 = torch.cuda.Event(enable_timing=True, external=True)
-                    e0.record(stream)
-                    L.fn()
-                    e1.record(stream)
-                    pairs.append((L, e0, e1))
-                else:
-                    L.fn()
-    return g, pairs
+                L.fn()
+    return g
+
+
+def time_graph(g, stream, reps):
+    """Average milliseconds of one replay over `reps` back-to-back replays,
+    from HIP events recorded on `stream` (the caller makes it current), and
+    the wall time of the loop."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record(stream)
+    for _ in range(reps):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps, time.perf_counter() - t0
+
+
+def source_digest():
+    """sha256 over the library's kernel sources: a PMC traffic record taken
+    from other sources no longer describes the kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "int8_scaled_gemm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` in `workload` from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE record (calibrated on a plain copy),
+    or None when there is none for the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    digest = source_digest()
+    for e in rec.get("entries", []):
+        if e.get("kernel") == kernel and e.get("workload") == workload \
+                and e.get("source_sha256") == digest:
+            return e.get("hbm_bytes_per_launch")
+    return None
+
+
+def roofline(name, k, spec, workload):
+    """Roofline entry of one kernel: algorithmic bytes (or flops) per launch
+    over its average launch time."""
+    tile = name.startswith("gemm_tile_kernel")
+    if tile:
+        achieved = k["flops"] / k["avg_s"] / 1e12
+        peak = MFMA_PEAK_TFLOPS[spec["qtype"]]
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s"}
+    else:
+        achieved = k["nbytes"] / k["avg_s"] / 1e9
+        peak = HBM_PEAK_GBS
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s"}
+    traffic = recorded_traffic(name, workload)
+    roof.update(frac=round(achieved / peak, 4),
+                traffic=None if traffic is None else round(traffic),
+                kernel=name, launches_per_step=k["launches"],
+                avg_launch_us=round(k["avg_s"] * 1e6, 3),
+                algorithmic_bytes_per_launch=round(k["nbytes"]),
+                algorithmic_flops_per_launch=round(k["flops"]),
+                timing="the step's launches of this kernel captured alone, replayed, "
+                       "HIP events on the launch stream")
+    return roof
 
 
 def cpu_baseline(spec, launches_meta, budget_s: float):
@@ -180,47 +267,59 @@ def cpu_baseline(spec, launches_meta, budget_s: float):
 
     import oracle
     cores = oracle.num_threads()
-    if spec.get("layers") is None:   # kv: quant + dequant of a slice of one layer tensor
-        x = workloads.kv_tensor(0, "k")
-        xh = workloads.as_u16(x).reshape(-1)
-        n = xh.size // 8
-        t0 = time.perf_counter()
-        q, s = oracle.kv_quant(xh[:n], xtype="bf16")
-        oracle.kv_dequant(q, s, "bf16")
-        dt = time.perf_counter() - t0
-        return {"value": round(5 * n / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+    if spec.get("layers") is None:   # kv: quant + dequant of whole layer tensors
+        n = 1
+        for d in workloads.KV_SHAPE:
+            n *= d
+        dt, done = 0.0, 0
+        for layer in range(workloads.KV_LAYERS):
+            for which in ("k", "v"):
+                xh = workloads.as_u16(workloads.kv_tensor(layer, which)).reshape(-1)
+                t0 = time.perf_counter()
+                q, s = oracle.kv_quant(xh, xtype="bf16")
+                oracle.kv_dequant(q, s, "bf16")
+                dt += time.perf_counter() - t0
+                done += 1
+                if dt > budget_s:
+                    break
+            if dt > budget_s:
+                break
+        return {"value": round(5 * n * done / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
                 "kind": "oracle",
-                "sample": f"KV quant+dequant of the first {n} elements of layer 0 K (1/8 tensor)"}
-    frac = 8
-    flops = 0
-    t0 = time.perf_counter()
-    done = 0
+                "sample": f"KV quant+dequant of {done} of the step's 64 layer tensors "
+                          f"[32768, 8, 128] ({dt:.1f} s; the step's per-token quant not sampled)"}
+    frac = spec["cpu_n_frac"]
+    flops, dt, done = 0, 0.0, 0
     for M in spec["Ms"]:
         for name, N, K in spec["layers"]:
             Ms = min(M, 64)
             Ns = max(16, N // frac)
+            # inputs and the offline weight quantisation are not timed
             x = workloads.as_u16(workloads.activations(Ms, K, seed=7))
             w = workloads.as_u16(workloads.weights(Ns, K, seed=8))
+            b, sb = oracle.quant_per_token(w, spec["qtype"], xtype="bf16")
+            t0 = time.perf_counter()
             if spec["act"] == "per_token":
                 a, sa = oracle.quant_per_token(x, spec["qtype"], xtype="bf16")
             else:
                 a, sa = oracle.quant_per_tensor(x, spec["qtype"], scale=np.float32(0.05),
                                                 xtype="bf16")
                 sa = np.array([sa], np.float32)
-            b, sb = oracle.quant_per_token(w, spec["qtype"], xtype="bf16")
             oracle.scaled_mm(a, b, spec["qtype"], sa, sb, "bf16")
+            dt += time.perf_counter() - t0
             flops += 2 * Ms * Ns * K
             done += 1
-            if time.perf_counter() - t0 > budget_s:
+            if dt > budget_s:
                 break
-        if time.perf_counter() - t0 > budget_s:
+        if dt > budget_s:
             break
-    dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{done} of the step's (M, layer) GEMMs with their activation quant, "
-                      f"on the first N/{frac} weight rows and at most 64 rows of M "
-                      f"({flops / 1e9:.2f} GFLOP, {dt:.1f} s)"}
+            "sample": f"{done} of the step's {len(spec['Ms']) * len(spec['layers'])} (M, layer) "
+                      f"GEMMs with their activation quant, on "
+                      + ("all" if frac == 1 else f"the first N/{frac}")
+                      + f" weight rows and at most 64 rows of M ({flops / 1e9:.2f} GFLOP, "
+                      f"{dt:.1f} s)"}
 
 
 def main():
@@ -232,19 +331,31 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0: skip)")
     ap.add_argument("--detail", action="store_true", help="per-launch times on stderr")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 256 MiB on the device 4 times (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(collectives and sharding are out of scope); run with --gpus 1",
-              file=sys.stderr)
+        print("bench.py measures one GPU: multi-GPU runs (collectives, sharding) are "
+              "not implemented; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
-    spec = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
+        return
+
+    spec = WORKLOADS[args.workload]
     w8.load_library()
     log(f"[bench] workload {args.workload}: building inputs")
     if args.workload == "kv":
@@ -261,15 +372,7 @@ def main():
             L.fn()
     torch.cuda.synchronize()
 
-    dominant = spec["dominant"]
-    try:
-        graph, pairs = capture(launches, stream, timed_kind=dominant)
-        timed_in_graph = True
-    except Exception as e:  # event nodes unsupported: time the dominant launches separately
-        log(f"[bench] timing events inside the graph unavailable ({e}); falling back")
-        torch.cuda.synchronize()
-        graph, pairs = capture(launches, stream)
-        timed_in_graph = False
+    graph = capture(launches, stream)
 
     # Every replay and every timing event below goes to `stream` (a graph
     # replays on the current stream).
@@ -281,44 +384,10 @@ def main():
     torch.cuda.synchronize()
 
     log(f"[bench] timing {args.steps} steps")
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        graph.replay()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    step_ms = start.elapsed_time(end) / args.steps
-
-    if timed_in_graph:
-        # the event pairs hold the dominant launches of the last timed replay
-        dom_ms = sum(e0.elapsed_time(e1) for _, e0, e1 in pairs)
-        dom_n = len(pairs)
-    else:
-        dl = [L for L in launches if L.kind == dominant]
-        g2, _ = capture(dl, stream)
-        g2.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            g2.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        dom_ms = e0.elapsed_time(e1)
-        dom_n = args.steps * len(dl)
+    step_ms, wall = time_graph(graph, stream, args.steps)
 
     per_step_flops = sum(L.flops for L in launches)
     per_step_bytes = sum(L.nbytes for L in launches)
-    dl = [L for L in launches if L.kind == dominant]
-    dom_avg_s = dom_ms / 1e3 / dom_n
-    dom_bytes = sum(L.nbytes for L in dl) / len(dl)
-    dom_flops = sum(L.flops for L in dl) / len(dl)
-
     if args.workload == "kv":
         value = per_step_bytes / (step_ms / 1e3) / 1e9
         metric, unit = "scaled fp8 KV cache quant+dequant GB/s (algorithmic bytes)", "GB/s"
@@ -328,24 +397,26 @@ def main():
         metric, unit = METRIC, "TFLOP/s"
         dtype = "fp8e4m3" if spec["qtype"] == "fp8" else "int8"
 
-    if spec["bound"] == "hbm":
-        achieved = dom_bytes / dom_avg_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
-    else:
-        achieved = dom_flops / dom_avg_s / 1e12
-        peak = MFMA_PEAK_TFLOPS[spec["qtype"]]
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
-    roof["kernel"] = ("w8a8_scaled_mm" if dominant == "gemm" else "kv_fp8_scaled_quant")
-    roof["launches_per_step"] = len(dl)
-    roof["avg_launch_us"] = round(dom_avg_s * 1e6, 3)
-    roof["timing"] = "events in graph" if timed_in_graph else "graph of dominant launches"
+    # Per kernel: the step's launches of that kernel, captured alone and
+    # replayed `steps` times, timed with events on the launch stream.
+    log("[bench] timing each kernel's launches")
+    kernels = {}
+    for name in dict.fromkeys(L.kernel for L in launches):
+        group = [L for L in launches if L.kernel == name]
+        g = capture(group, stream)
+        g.replay()
+        ms, _ = time_graph(g, stream, args.steps)
+        avg_s = ms / 1e3 / len(group)
+        kernels[name] = dict(launches=len(group), avg_s=avg_s,
+                             nbytes=sum(L.nbytes for L in group) / len(group),
+                             flops=sum(L.flops for L in group) / len(group))
+    dom = max(kernels, key=lambda k: kernels[k]["avg_s"] * kernels[k]["launches"])
+    roof = roofline(dom, kernels[dom], spec, args.workload)
 
     if args.detail:
         # per-launch times: each launch alone, graph of 10 back-to-back copies
         for L in launches:
-            g3, _ = capture([L] * 10, stream)
+            g3 = capture([L] * 10, stream)
             g3.replay()
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -369,6 +440,12 @@ def main():
                    "step_bytes": per_step_bytes, "step_flops": per_step_flops,
                    "launches_per_step": len(launches), "parallelism": "single GPU"},
         "roofline": roof,
+        "kernels": {n: {"launches_per_step": k["launches"],
+                        "avg_launch_us": round(k["avg_s"] * 1e6, 3),
+                        "hbm_frac": round(k["nbytes"] / k["avg_s"] / 1e9 / HBM_PEAK_GBS, 4),
+                        "mfma_frac": round(k["flops"] / k["avg_s"] / 1e12
+                                           / MFMA_PEAK_TFLOPS.get(spec.get("qtype"), 5000.0), 4)}
+                    for n, k in kernels.items()},
     }
     if args.cpu_budget > 0:
         log("[bench] cpu baseline (oracle)")
