@@ -115,7 +115,7 @@ def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
             launches.append(Launch("quant", qf, 0, qbytes, f"quant M={M} {name}", qkern))
             launches.append(Launch("gemm", mf, 2 * M * N * K, _gemm_bytes(M, N, K, n_sa, N),
                                    f"gemm M={M} {name} {N}x{K}",
-                                   w8.w8a8_scaled_mm_kernel(M, N, K, with_workspace=True)))
+                                   w8.w8a8_scaled_mm_kernel(M, N, K)))
             keep += [wq, ws, x, q, s, out]
     return launches, keep
 

@@ -128,36 +128,6 @@ w8a8_status w8a8_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* a,
                            int64_t n_b, hipStream_t stream);
 
 /*
- * Bytes of workspace w8a8_scaled_mm_ws needs for an M x N x K problem of
- * code type qt (0 when the problem does not split K: M > 64, or a split
- * would not pay). Host-only, never fails for valid sizes.
- */
-w8a8_status w8a8_scaled_mm_workspace_size(w8a8_qtype qt, int64_t M, int64_t N, int64_t K,
-                                          int64_t* bytes);
-
-/*
- * w8a8_scaled_mm with a caller-provided device workspace, which lets the
- * decode path (M <= 64) split K across workgroups: every workgroup writes a
- * partial fp32 (int32 for int8) tile to the workspace and the last one to
- * finish a column tile adds the partials in a fixed order, so results are
- * deterministic and identical in value to w8a8_scaled_mm up to the fp8
- * accumulation order. Same operation and arguments as w8a8_scaled_mm, plus:
- * workspace: device memory of at least w8a8_scaled_mm_workspace_size()
- *   bytes, 256-byte aligned. Its first 64 KB hold per-tile arrival counters
- *   that must be zero before the first use; every call returns them to zero,
- *   so one workspace serves any sequence of calls. May be NULL when the size
- *   is 0.
- *   Calls that share a workspace must not run concurrently (use one
- *   workspace per stream).
- * A workspace smaller than required returns W8A8_ERR_INVALID_ARG.
- */
-w8a8_status w8a8_scaled_mm_ws(void* out, w8a8_dtype ot, int64_t ldo, const void* a, int64_t lda,
-                              const void* b, int64_t ldb, w8a8_qtype qt, int64_t M, int64_t N,
-                              int64_t K, const float* a_scales, int64_t n_a, const float* b_scales,
-                              int64_t n_b, void* workspace, int64_t workspace_bytes,
-                              hipStream_t stream);
-
-/*
  * Scaled fp8 KV-cache quantisation of one flat, contiguous tensor of n
  * elements (e.g. one layer's K or V cache) [P3 "Scaling semantics": per
  * tensor scale = absmax / 448, q = fp8(x / scale)].
@@ -178,12 +148,12 @@ w8a8_status kv_fp8_scaled_dequant(const uint8_t* q, int64_t n, const float* scal
                                   w8a8_dtype xt, hipStream_t stream);
 
 /*
- * Name of the kernel configuration that w8a8_scaled_mm (with_workspace = 0)
- * or w8a8_scaled_mm_ws (1) runs for an M x N x K problem, such as
- * "gemm_decode_kernel" or "gemm_tile_kernel<256x256>" (static string, ""
- * for negative sizes), so that profiles can be matched to calls.
+ * Name of the kernel configuration w8a8_scaled_mm runs for an M x N x K
+ * problem, such as "gemm_decode_kernel<16x16>" or
+ * "gemm_tile_kernel<256x256>" (a static string; "" for negative sizes), so
+ * that profiles can be matched to calls. Host-only.
  */
-const char* w8a8_scaled_mm_kernel(int64_t M, int64_t N, int64_t K, int with_workspace);
+const char* w8a8_scaled_mm_kernel(int64_t M, int64_t N, int64_t K);
 
 /* Name of a status code (static string). */
 const char* w8a8_status_string(w8a8_status s);

@@ -53,9 +53,6 @@ SIGNATURES = {
                        _I64, _P],
     "kv_fp8_scaled_quant": [_P, _I, _I64, _P, _P, _I, _P],
     "kv_fp8_scaled_dequant": [_P, _I64, _P, _P, _I, _P],
-    "w8a8_scaled_mm_ws": [_P, _I, _I64, _P, _I64, _P, _I64, _I, _I64, _I64, _I64, _P, _I64, _P,
-                          _I64, _P, _I64, _P],
-    "w8a8_scaled_mm_workspace_size": [_I, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_int64)],
 }
 
 
@@ -90,7 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.w8a8_last_error.restype = ctypes.c_char_p
     lib.w8a8_version.argtypes = []
     lib.w8a8_version.restype = ctypes.c_char_p
-    lib.w8a8_scaled_mm_kernel.argtypes = [_I64, _I64, _I64, _I]
+    lib.w8a8_scaled_mm_kernel.argtypes = [_I64, _I64, _I64]
     lib.w8a8_scaled_mm_kernel.restype = ctypes.c_char_p
     _lib = lib
     return lib
@@ -206,36 +203,9 @@ def kv_fp8_scaled_dequant(q: torch.Tensor, scale: torch.Tensor | None,
 
 
 # ---------------------------------------------------------------------- GEMM
-def w8a8_scaled_mm_workspace_size(qtype, M: int, N: int, K: int) -> int:
-    """Bytes of workspace w8a8_scaled_mm_ws needs (0: none)."""
-    n = ctypes.c_int64(0)
-    _call("w8a8_scaled_mm_workspace_size", _qtype(qtype), M, N, K, ctypes.byref(n))
-    return int(n.value)
-
-
-_workspaces: dict = {}
-
-
-def workspace_for(device, nbytes: int) -> torch.Tensor | None:
-    """The per-device workspace, grown to at least ``nbytes`` (zero-filled by a
-    fill kernel, never a memset). It cannot grow while a HIP graph is being
-    captured: run the call once before capturing."""
-    if nbytes <= 0:
-        return None
-    dev = torch.device(device)
-    ws = _workspaces.get(dev)
-    if ws is None or ws.numel() < nbytes:
-        if torch.cuda.is_current_stream_capturing():
-            raise RuntimeError("libw8a8 workspace must grow outside graph capture: "
-                               "run this call once before capturing")
-        ws = torch.zeros(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=dev)
-        _workspaces[dev] = ws
-    return ws
-
-
 def w8a8_scaled_mm(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | None,
                    b_scales: torch.Tensor | None, out_dtype=torch.bfloat16,
-                   out: torch.Tensor | None = None, workspace="auto") -> torch.Tensor:
+                   out: torch.Tensor | None = None) -> torch.Tensor:
     """D = a_scales (x) b_scales * (a @ b).
 
     a: codes [M, K] with unit column stride. b: codes K x N, COLUMN-major
@@ -243,10 +213,6 @@ def w8a8_scaled_mm(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | No
     a_scales: fp32 [1] or [M] (or [M, 1]); b_scales: fp32 [1] or [N] (or [1, N]).
     None means 1.0. out_dtype: bfloat16, float16, float32, or int32 (the raw
     int8 accumulator, scales must be None).
-    workspace: "auto" (a cached per-device buffer, letting small-M problems
-    split K across workgroups through w8a8_scaled_mm_ws), a zero-initialised
-    uint8 device tensor of at least w8a8_scaled_mm_workspace_size bytes, or
-    None (plain w8a8_scaled_mm, no split).
     """
     _check_cuda(a, b, a_scales, b_scales, out)
     qt = _qtype(a.dtype)
@@ -270,19 +236,7 @@ def w8a8_scaled_mm(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | No
     args = (_ptr(out), _dtype(out.dtype), ldo, _ptr(a), lda, _ptr(b), ldb, qt, M, N, K,
             _ptr(sa), 0 if sa is None else sa.numel(), _ptr(sb),
             0 if sb is None else sb.numel())
-    if workspace is None:
-        _call("w8a8_scaled_mm", *args, _stream(a))
-        return out
-    need = w8a8_scaled_mm_workspace_size(qt, M, N, K)
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError("workspace must be 'auto', None or a tensor")
-        ws = workspace_for(a.device, need)
-    else:
-        ws = workspace
-        _check_cuda(ws)
-    _call("w8a8_scaled_mm_ws", *args, _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-          _stream(a))
+    _call("w8a8_scaled_mm", *args, _stream(a))
     return out
 
 
@@ -293,9 +247,9 @@ def scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor | None,
     return w8a8_scaled_mm(a, b, scale_a, scale_b, out_dtype, out)
 
 
-def w8a8_scaled_mm_kernel(M: int, N: int, K: int, with_workspace: bool = True) -> str:
+def w8a8_scaled_mm_kernel(M: int, N: int, K: int) -> str:
     """Kernel configuration the library runs for an M x N x K problem."""
-    return load_library().w8a8_scaled_mm_kernel(M, N, K, 1 if with_workspace else 0).decode()
+    return load_library().w8a8_scaled_mm_kernel(M, N, K).decode()
 
 
 def version() -> str:
@@ -303,6 +257,6 @@ def version() -> str:
 
 
 __all__ = ["w8a8_quant_per_token", "w8a8_quant_per_tensor", "w8a8_scaled_mm",
-           "w8a8_scaled_mm_workspace_size", "w8a8_scaled_mm_kernel", "workspace_for",
+           "w8a8_scaled_mm_kernel",
            "kv_fp8_scaled_quant", "kv_fp8_scaled_dequant", "scaled_mm", "W8A8Error",
            "load_library", "version", "LIB_PATH", "SIGNATURES"]

@@ -69,8 +69,7 @@ w8a8_status check_quant_io(const char* fn, const void* x, w8a8_dtype xt, int64_t
 static w8a8_status scaled_mm_impl(const char* fn, void* out, w8a8_dtype ot, int64_t ldo, const void* a,
                                   int64_t lda, const void* b, int64_t ldb, w8a8_qtype qt, int64_t M,
                                   int64_t N, int64_t K, const float* a_scales, int64_t n_a,
-                                  const float* b_scales, int64_t n_b, void* workspace,
-                                  int64_t workspace_bytes, bool with_ws, hipStream_t stream) {
+                                  const float* b_scales, int64_t n_b, hipStream_t stream) {
     if (!valid_qtype(qt)) return fail(W8A8_ERR_DTYPE, "%s: code type %d is not INT8 or FP8_E4M3FN", fn, qt);
     if (ot != W8A8_BF16 && ot != W8A8_FP16 && ot != W8A8_F32 && ot != W8A8_I32)
         return fail(W8A8_ERR_DTYPE, "%s: output type %d unknown", fn, ot);
@@ -102,15 +101,6 @@ static w8a8_status scaled_mm_impl(const char* fn, void* out, w8a8_dtype ot, int6
     if (reinterpret_cast<uintptr_t>(out) % elem_size(ot)) return fail(W8A8_ERR_ALIGNMENT, "%s: out is not aligned to its element size", fn);
     if ((a_scales && (reinterpret_cast<uintptr_t>(a_scales) & 3u)) || (b_scales && (reinterpret_cast<uintptr_t>(b_scales) & 3u)))
         return fail(W8A8_ERR_ALIGNMENT, "%s: scale arrays must be 4-byte aligned", fn);
-    if (with_ws) {
-        const w8a8::DecodePlan d = w8a8::plan_decode(M, N, K);
-        if (d.workspace_bytes > 0) {
-            if (!workspace) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL workspace (%lld bytes needed)", fn, (long long)d.workspace_bytes);
-            if (workspace_bytes < d.workspace_bytes)
-                return fail(W8A8_ERR_INVALID_ARG, "%s: workspace of %lld bytes, %lld needed", fn, (long long)workspace_bytes, (long long)d.workspace_bytes);
-            if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(W8A8_ERR_ALIGNMENT, "%s: workspace must be 256-byte aligned", fn);
-        }
-    }
     w8a8::GemmProblem p;
     p.out = out;
     p.ot = ot;
@@ -127,8 +117,6 @@ static w8a8_status scaled_mm_impl(const char* fn, void* out, w8a8_dtype ot, int6
     p.sa_per_row = a_scales && n_a == M && M != 1;
     p.sb = b_scales;
     p.sb_per_col = b_scales && n_b == N && N != 1;
-    p.splitk = with_ws;
-    p.workspace = with_ws ? workspace : nullptr;
     return from_hip(w8a8::launch_scaled_mm(p, stream), fn);
 }
 
@@ -184,31 +172,12 @@ w8a8_status w8a8_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* a,
                            int64_t K, const float* a_scales, int64_t n_a, const float* b_scales,
                            int64_t n_b, hipStream_t stream) {
     return scaled_mm_impl("w8a8_scaled_mm", out, ot, ldo, a, lda, b, ldb, qt, M, N, K, a_scales, n_a,
-                          b_scales, n_b, nullptr, 0, false, stream);
+                          b_scales, n_b, stream);
 }
 
-const char* w8a8_scaled_mm_kernel(int64_t M, int64_t N, int64_t K, int with_workspace) {
+const char* w8a8_scaled_mm_kernel(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0) return "";
-    return w8a8::scaled_mm_kernel_name(M, N, K, with_workspace != 0);
-}
-
-w8a8_status w8a8_scaled_mm_workspace_size(w8a8_qtype qt, int64_t M, int64_t N, int64_t K,
-                                          int64_t* bytes) {
-    const char* fn = "w8a8_scaled_mm_workspace_size";
-    if (!valid_qtype(qt)) return fail(W8A8_ERR_DTYPE, "%s: code type %d is not INT8 or FP8_E4M3FN", fn, qt);
-    if (!bytes) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL bytes", fn);
-    if (M < 0 || N < 0 || K < 0) return fail(W8A8_ERR_SHAPE, "%s: negative size", fn);
-    *bytes = w8a8::plan_decode(M, N, K).workspace_bytes;
-    return ok();
-}
-
-w8a8_status w8a8_scaled_mm_ws(void* out, w8a8_dtype ot, int64_t ldo, const void* a, int64_t lda,
-                              const void* b, int64_t ldb, w8a8_qtype qt, int64_t M, int64_t N,
-                              int64_t K, const float* a_scales, int64_t n_a, const float* b_scales,
-                              int64_t n_b, void* workspace, int64_t workspace_bytes,
-                              hipStream_t stream) {
-    return scaled_mm_impl("w8a8_scaled_mm_ws", out, ot, ldo, a, lda, b, ldb, qt, M, N, K, a_scales,
-                          n_a, b_scales, n_b, workspace, workspace_bytes, true, stream);
+    return w8a8::scaled_mm_kernel_name(M, N);
 }
 
 w8a8_status kv_fp8_scaled_quant(const void* x, w8a8_dtype xt, int64_t n, uint8_t* q, float* scale,

@@ -6,33 +6,19 @@
 // fixes the operation and its scale granularities; the misaligned-address
 // report fixes B as K x N column-major, i.e. rows of an [N, K] weight.)
 //
-// The contraction runs on the CDNA4 matrix cores:
-//   fp8 e4m3:  v_mfma_f32_16x16x128_f8f6f4 (format 0 = e4m3), fp32 accumulate
-//   int8:      v_mfma_i32_16x16x64_i8, exact int32 accumulate
-// Both consume, per lane, 32 bytes of an A row and 32 bytes of a B row
-// (lane l: row l%16, bytes 32*(l/16) .. +32 of a 128-byte K slice), and
-// leave lane l holding D rows 4*(l/16)+i (i < 4) of column l%16. The int8
-// path issues two 64-deep MFMAs on the two 16-byte halves of the same
-// fragment: both operands see the same K permutation, so the integer sum is
-// unchanged.
-//
-// Two kernels:
-//  - gemm_tile_kernel: a BM x BN block tile per workgroup (4 waves, 2 x 2),
-//    K walked in 128-byte slices staged through LDS with double buffering
-//    (global -> registers for slice k+1 while MFMAs consume slice k), rows
-//    padded by 16 bytes so the 16-lane fragment reads spread over the banks.
-//    Tiles are numbered so that consecutive tiles land on one XCD (blocks
-//    are dealt round-robin over the 8 XCDs) and walk groups of 8 row-tiles,
-//    keeping shared A and B slices in that XCD's L2.
-//  - gemm_decode_kernel: M <= 64 rows. The weight stream dominates (HBM
-//    bound), so each workgroup owns 16 output columns and its waves split K,
-//    every lane keeping several 16-byte weight loads in flight; fragments go
-//    straight from global memory to the MFMA, and the waves' partial sums are
-//    added through LDS before the epilogue.
+// The contraction runs on the CDNA4 matrix cores, fp32 accumulation for fp8
+// e4m3 (format 0 of the f8f6f4 MFMAs) and exact int32 for int8:
+//  - gemm_tile_kernel (M > 64): block tiles of 256x256 down to 64x64 with
+//    32 x 32 MFMAs (v_mfma_f32_32x32x64_f8f6f4, v_mfma_i32_32x32x32_i8),
+//    operands staged in LDS by direct global -> LDS loads.
+//  - gemm_decode_kernel (M <= 64, bound by the weight stream): 16 x 16 MFMAs
+//    (v_mfma_f32_16x16x128_f8f6f4, v_mfma_i32_16x16x64_i8) on a block of
+//    16 or 64 output columns, weights streamed once through an LDS ring.
+// Each MFMA lane holds a run of contiguous K bytes of one row of each
+// operand; the order of K inside a fragment differs from memory order, but A
+// and B always share it, so the sum is the same.
 // The epilogue is fused: scales applied in fp32 and the result rounded to
 // nearest even into bf16/fp16 in registers, then stored once.
-#include <algorithm>
-#include <type_traits>
 
 #include "device.hpp"
 #include "launch.hpp"
@@ -55,11 +41,6 @@ struct GemmArgs {
     int sb_per_col;
     int tiles_m, tiles_n;
     int vec_out;  // out and ldo allow 4-element vector stores
-    // split-K decode: partial sums [splits][M][N] and one arrival counter per
-    // 64-column tile, both in the caller's workspace
-    void* ws_part;
-    uint32_t* ws_count;
-    int splits, slices_per_split;
 };
 
 template <int QT>
@@ -356,154 +337,108 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
     }
 }
 
-// M <= 64 rows in up to 4 row-tiles of 16 (p.tiles_m of them, a runtime
-// value so that one kernel serves every decode batch size); one workgroup
-// per 16 columns; WAVES waves split the 128-byte K slices round-robin
-// (neighbouring waves read neighbouring slices of the same weight rows);
-// U slices per wave per step in flight.
-template <int QT, int OT, int WAVES, int U>
-__global__ __launch_bounds__(WAVES * 64) void gemm_decode_kernel(GemmArgs p) {
-    typedef typename AccOf<QT>::type Acc;
-    constexpr int TM = 4;
-    const int mt = p.tiles_m;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n0 = blockIdx.x * 16;
-    const int nrow = n0 + (lane & 15);
-    const uint8_t* bp = p.b + static_cast<int64_t>(nrow < p.N ? nrow : p.N - 1) * p.ldb;
-    const int koff = (lane >> 4) * 32;
-    const int KS = (p.K + kBK - 1) / kBK;
-
-    Acc acc[TM];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) acc[i] = Acc{0, 0, 0, 0};
-
-    const u32x4 z = {0, 0, 0, 0};
-    for (int ks = wave; ks < KS; ks += WAVES * U) {
-        i32x8 bf[U];
-        i32x8 af[U][TM];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = (ks + u * WAVES) * kBK + koff;
-            const bool lo = k < p.K, hi = k + 16 < p.K;
-            bf[u] = join(lo ? load16(bp + k) : z, hi ? load16(bp + k + 16) : z);
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                if (i >= mt) break;
-                const int m = i * 16 + (lane & 15);
-                const uint8_t* ap = p.a + static_cast<int64_t>(m) * p.lda + k;
-                const bool mv = m < p.M;
-                af[u][i] = join((mv && lo) ? load16(ap) : z, (mv && hi) ? load16(ap + 16) : z);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                if (i >= mt) break;
-                mma<QT>(acc[i], af[u][i], bf[u]);
-            }
-    }
-
-    // Add the waves' partial sums (fixed order), then the fused epilogue.
-    __shared__ Acc red[WAVES][TM][64];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-        if (i < mt) red[wave][i][lane] = acc[i];
-    __syncthreads();
-    for (int i = wave; i < mt; i += WAVES) {
-        Acc s = red[0][i][lane];
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w) s += red[w][i][lane];
-        const int n = n0 + (lane & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = i * 16 + 4 * (lane >> 4) + r;
-            if (m < p.M && n < p.N) store_out<OT>(p, m, n, s[r]);
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Split-K decode kernel, M <= 16*MT rows. A block owns 64 output columns (one
-// 16-column tile per wave) and a range of K slices. The 4 waves share the
-// activation rows, staged through LDS one 1 KB K-chunk at a time with
-// row-contiguous direct loads (row stride padded by 16 bytes, so the 16-row
-// fragment reads spread over the banks); each wave streams its own weight
-// rows straight from HBM with non-temporal loads, the whole chunk (8 slices,
-// 16 loads per lane) in flight at once. With splits > 1 every block writes
-// its fp32 (int32 for int8) partial tile to the workspace; the last block to
-// arrive on a column tile adds the partials in split order (deterministic),
-// applies the fused epilogue and resets the tile's counter to zero.
+// Decode kernel, M <= 16*MT <= 64 rows: the weight stream from HBM bounds it.
+// A workgroup (4 waves) owns CB output columns (16 or 64) over all of K. K is
+// walked in stages of CH bytes through an ST-deep LDS ring; a stage holds the
+// CB weight rows and the 16*MT activation rows, filled by direct global -> LDS
+// loads in which each wave-wide load reads 1 KB of contiguous bytes (1024/CH
+// whole row segments). The 16-byte chunk c of row r is stored at slot
+// c ^ (r % 16), so the 16-row fragment reads of the MFMAs spread over all LDS
+// banks. Weight loads are non-temporal: they are read once.
+//  - CB = 64: wave w computes columns 16w .. 16w+15 over every K slice.
+//  - CB = 16: wave w computes the block's 16 columns over the stage's K slices
+//    w, w+4, ...; the four partial sums are added through LDS in a fixed order.
+// Activation rows past M read as zeros; their results are never stored.
 // ---------------------------------------------------------------------------
-constexpr int kDecChunk = 1024;
-constexpr int kDecRow = kDecChunk + 16;
+constexpr int kNonTemporal = 2;  // cache-policy operand of the buffer load: nt
 
-__device__ __forceinline__ u32x4 load16_nt(const uint8_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-
-template <int QT, int OT, int MT>
-__global__ __launch_bounds__(256) void gemm_decode_sk_kernel(GemmArgs p) {
+template <int QT, int OT, int CB, int MT, int CH, int ST>
+__global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
     typedef typename AccOf<QT>::type Acc;
-    __shared__ __attribute__((aligned(16))) uint8_t sa_lds[MT * 16 * kDecRow];
-    __shared__ int last_block;
+    constexpr int AROWS = 16 * MT;
+    constexpr int STAGE = (CB + AROWS) * CH;
+    constexpr int WL = CB * CH / 4096, AL = AROWS * CH / 4096;  // loads per wave per stage
+    constexpr int LPW = WL + AL;
+    constexpr int SL = CH / kBK;  // 128-byte K slices per stage
+    static_assert(CB == 16 || CB == 64, "columns per workgroup");
+    static_assert(CH % 256 == 0 && WL >= 1 && AL >= 1, "stage shape");
+    static_assert(CB == 64 || SL % 4 == 0, "slices per wave");
+    static_assert(ST >= 2 && LPW * (ST - 2) <= 63, "loads in flight");
+    static_assert(ST * STAGE >= 4 * MT * 64 * 16, "room for the wave reduction");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int S = p.splits;
-    const int ct = blockIdx.x / S, sp = blockIdx.x % S;
-    const int n0 = ct * 64 + wave * 16;
-    const int KS = (p.K + kBK - 1) / kBK;
-    const int s0 = sp * p.slices_per_split, s1 = min(KS, s0 + p.slices_per_split);
-    const int kbeg = s0 * kBK, kend = min(p.K, s1 * kBK);
-    const int mt = p.tiles_m;  // 16-row tiles of A, <= MT
-    const int g = lane >> 4;
+    const int n0 = blockIdx.x * CB;
+    const int nst = (p.K + CH - 1) / CH;
+    const int mt = (p.M + 15) / 16;
+    const int wrows = min(CB, p.N - n0);
+    const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
+    const i32x4 rb = buffer_rsrc(p.b + static_cast<int64_t>(n0) * p.ldb,
+                                 static_cast<uint32_t>((wrows - 1) * ldb + p.K));
+    const i32x4 ra = buffer_rsrc(p.a, static_cast<uint32_t>((p.M - 1) * lda + p.K));
 
-    const i32x4 ra = buffer_rsrc(p.a, static_cast<uint32_t>((p.M - 1) * p.lda + p.K));
-    const int nrow = n0 + (lane & 15);
-    const uint8_t* bp = p.b + static_cast<int64_t>(nrow < p.N ? nrow : p.N - 1) * p.ldb + 16 * g;
-    const bool nvalid = nrow < p.N;
+    auto issue = [&](int st, int buf) {
+        const int k0 = st * CH;
+        uint8_t* base = smem + buf * STAGE;
+#pragma unroll
+        for (int j = 0; j < WL + AL; ++j) {
+            const bool is_w = j < WL;
+            const int t = wave + 4 * (is_w ? j : j - WL);  // 1 KB piece of the operand's tile
+            const int o = t * 1024 + 16 * lane;
+            const int r = o / CH, c = ((o % CH) >> 4) ^ (r & 15);
+            const int k = k0 + 16 * c;
+            const bool ok = r < (is_w ? wrows : p.M) && k < p.K;
+            const int off = ok ? r * (is_w ? ldb : lda) + k : kOutOfRange;
+            raw_buffer_load_lds(is_w ? rb : ra, (lds_u32p)(base + (is_w ? 0 : CB * CH) + t * 1024),
+                                16, off, 0, 0, is_w ? kNonTemporal : 0);
+        }
+    };
 
     Acc acc[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[i] = Acc{0, 0, 0, 0};
 
-    const u32x4 z = {0, 0, 0, 0};
-    for (int kc = kbeg; kc < kend; kc += kDecChunk) {
-        // A chunk -> LDS: one wave-wide 1 KB load per row
-        for (int r = wave; r < 16 * mt; r += 4) {
-            const int k = kc + 16 * lane;
-            const int off = (r < p.M && k < kend) ? r * static_cast<int>(p.lda) + k : kOutOfRange;
-            raw_buffer_load_lds(ra, (lds_u32p)(sa_lds + r * kDecRow), 16, off, 0, 0, 0);
-        }
-        // this wave's weight fragments for the chunk: lane group g takes K
-        // bytes 16g..16g+15 and 64+16g..64+16g+15 of each 128-byte slice
-        constexpr int U = kDecChunk / kBK;
-        i32x8 wf[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = kc + u * kBK;
-            const bool lo = nvalid && k + 16 * g < kend, hi = nvalid && k + 64 + 16 * g < kend;
-            wf[u] = join(lo ? load16_nt(bp + k) : z, hi ? load16_nt(bp + k + 64) : z);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+    for (int st = 0; st < ST - 1; ++st)
+        if (st < nst) issue(st, st);
+    const int g = lane >> 4, r16 = lane & 15;
+    for (int st = 0; st < nst; ++st) {
+        // Wait for this stage's loads; later stages' loads stay in flight.
+        const int pending = min(nst - 1 - st, ST - 2);
+        if (ST >= 4 && pending >= 2)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW) : "memory");
+        else if (ST >= 3 && pending >= 1)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // every wave's loads of this stage have landed
+        if (st + ST - 1 < nst) issue(st + ST - 1, (st + ST - 1) % ST);  // slot freed last step
+        const uint8_t* wb = smem + (st % ST) * STAGE;
+        const uint8_t* ab = wb + CB * CH;
+        const uint8_t* wrow = wb + ((CB == 64 ? 16 * wave : 0) + r16) * CH;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int uu = 0; uu < (CB == 64 ? SL : SL / 4); ++uu) {
+            const int u = CB == 64 ? uu : 4 * uu + wave;
+            // lane's fragment: K bytes 32g .. 32g+31 of slice u (chunks 8u+2g, 8u+2g+1)
+            const int c0 = (8 * u + 2 * g) ^ r16, c1 = (8 * u + 2 * g + 1) ^ r16;
+            const i32x8 wf = join(*reinterpret_cast<const u32x4*>(wrow + 16 * c0),
+                                  *reinterpret_cast<const u32x4*>(wrow + 16 * c1));
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
                 if (i >= mt) break;
-                const uint8_t* ar = sa_lds + (16 * i + (lane & 15)) * kDecRow + u * kBK + 16 * g;
-                const i32x8 af = join(*reinterpret_cast<const u32x4*>(ar),
-                                      *reinterpret_cast<const u32x4*>(ar + 64));
-                mma<QT>(acc[i], af, wf[u]);
+                const uint8_t* arow = ab + (16 * i + r16) * CH;
+                const i32x8 af = join(*reinterpret_cast<const u32x4*>(arow + 16 * c0),
+                                      *reinterpret_cast<const u32x4*>(arow + 16 * c1));
+                mma<QT>(acc[i], af, wf);
             }
         }
-        __syncthreads();  // the next chunk overwrites the staged rows
     }
 
-    const int n = n0 + (lane & 15);
-    if (S == 1) {
+    // In a 16 x 16 tile lane l holds rows 4 (l / 16) + r, r < 4, of column l % 16.
+    if constexpr (CB == 64) {
+        const int n = n0 + 16 * wave + r16;
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             if (i >= mt) break;
@@ -513,54 +448,24 @@ __global__ __launch_bounds__(256) void gemm_decode_sk_kernel(GemmArgs p) {
                 if (m < p.M && n < p.N) store_out<OT>(p, m, n, acc[i][r]);
             }
         }
-        return;
-    }
-
-    // Partial tile -> workspace, then the last arriving block reduces. The
-    // partials travel with agent-coherent (L2 write-through / L2-bypassing)
-    // atomic stores and loads, and each block waits for its stores to be
-    // acknowledged before it counts itself in, so no cache-wide write-back or
-    // invalidate (an agent-scope fence) is needed.
-    typedef typename std::conditional<QT == Q_FP8, float, int32_t>::type Part;
-    Part* part = static_cast<Part*>(p.ws_part);
-    const int64_t plane = static_cast<int64_t>(p.M) * p.N;
+    } else {
+        __syncthreads();  // the ring is free: reuse it for the four waves' sums
+        Acc* red = reinterpret_cast<Acc*>(smem);
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        if (i >= mt) break;
+        for (int i = 0; i < MT; ++i) red[(wave * MT + i) * 64 + lane] = acc[i];
+        __syncthreads();
+        const int n = n0 + r16;
+        for (int i = wave; i < mt; i += 4) {
+            Acc s = red[i * 64 + lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 16 * i + 4 * g + r;
-            if (m < p.M && n < p.N)
-                __hip_atomic_store(part + sp * plane + static_cast<int64_t>(m) * p.N + n,
-                                   static_cast<Part>(acc[i][r]), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0)
-        last_block = __hip_atomic_fetch_add(p.ws_count + ct, 1u, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(S - 1);
-    __syncthreads();
-    if (!last_block) return;
+            for (int w = 1; w < 4; ++w) s += red[(w * MT + i) * 64 + lane];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        if (i >= mt) break;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 16 * i + 4 * g + r;
-            if (m < p.M && n < p.N) {
-                const int64_t o = static_cast<int64_t>(m) * p.N + n;
-                Part sum = __hip_atomic_load(part + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                for (int q = 1; q < S; ++q)
-                    sum += __hip_atomic_load(part + q * plane + o, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-                store_out<OT>(p, m, n, sum);
+            for (int r = 0; r < 4; ++r) {
+                const int m = 16 * i + 4 * g + r;
+                if (m < p.M && n < p.N) store_out<OT>(p, m, n, s[r]);
             }
         }
     }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(p.ws_count + ct, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int QT, int OT, int BM, int BN, int WGM, int WGN>
@@ -574,46 +479,33 @@ hipError_t run_tile(GemmArgs a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int QT, int OT>
-hipError_t run_decode(GemmArgs a, hipStream_t st) {
-    constexpr int kWaves = 4, kU = 4;
-    a.tiles_m = (a.M + 15) / 16;
-    const int grid = (a.N + 15) / 16;
-    hipLaunchKernelGGL((gemm_decode_kernel<QT, OT, kWaves, kU>), dim3(grid), dim3(kWaves * 64), 0, st, a);
-    return hipGetLastError();
-}
-
-template <int QT, int OT>
-hipError_t run_decode_sk(GemmArgs a, hipStream_t st) {
-    a.tiles_m = (a.M + 15) / 16;
-    const int grid = ((a.N + 63) / 64) * a.splits;
-    if (a.tiles_m <= 1)
-        hipLaunchKernelGGL((gemm_decode_sk_kernel<QT, OT, 1>), dim3(grid), dim3(256), 0, st, a);
-    else if (a.tiles_m <= 2)
-        hipLaunchKernelGGL((gemm_decode_sk_kernel<QT, OT, 2>), dim3(grid), dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL((gemm_decode_sk_kernel<QT, OT, 4>), dim3(grid), dim3(256), 0, st, a);
+template <int QT, int OT, int CB, int MT, int CH, int ST>
+hipError_t run_decode(const GemmArgs& a, hipStream_t st) {
+    const int grid = (a.N + CB - 1) / CB;
+    hipLaunchKernelGGL((gemm_decode_kernel<QT, OT, CB, MT, CH, ST>), dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 // The kernel configuration a problem runs with (shared by the launch and by
 // scaled_mm_kernel_name, so that profiles can be matched to launches).
 enum Config {
-    kDecode,         // gemm_decode_kernel: 16 columns per workgroup, K split over its waves
-    kDecodeSplit1,   // gemm_decode_sk_kernel<MT = 1>
-    kDecodeSplit2,   // gemm_decode_sk_kernel<MT = 2>
-    kDecodeSplit4,   // gemm_decode_sk_kernel<MT = 4>
+    kDecode64x16,    // gemm_decode_kernel, 64 columns, M <= 16 (stage 512 B, 2 stages)
+    kDecode64x64,    // gemm_decode_kernel, 64 columns, M <= 64 (stage 256 B, 2 stages)
+    kDecode16x16,    // gemm_decode_kernel, 16 columns, M <= 16 (stage 1 KB, 2 stages)
+    kDecode16x64,    // gemm_decode_kernel, 16 columns, M <= 64 (stage 512 B, 2 stages)
     kTile256x256,    // gemm_tile_kernel 256 x 256, 8 waves
     kTile256x128,    // gemm_tile_kernel 256 x 128, 8 waves
     kTile128x128,    // gemm_tile_kernel 128 x 128, 4 waves
     kTile64x64,      // gemm_tile_kernel 64 x 64, 4 waves
 };
 
-Config select_config(int64_t M, int64_t N, bool splitk_planned) {
+Config select_config(int64_t M, int64_t N) {
     if (M <= 64) {
-        if (!splitk_planned) return kDecode;
-        const int64_t mt = (M + 15) / 16;
-        return mt <= 1 ? kDecodeSplit1 : (mt <= 2 ? kDecodeSplit2 : kDecodeSplit4);
+        // Measured on MI355X at the Llama-3 decode shapes: 64-column blocks
+        // stream fastest once they still give every CU a block (N >= 16384);
+        // narrower weights need 16-column blocks to reach every CU.
+        if ((N + 63) / 64 >= 256) return M <= 16 ? kDecode64x16 : kDecode64x64;
+        return M <= 16 ? kDecode16x16 : kDecode16x64;
     }
     // The largest tile that still gives every CU a block, else the smallest.
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
@@ -625,11 +517,11 @@ Config select_config(int64_t M, int64_t N, bool splitk_planned) {
 
 template <int QT, int OT>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
-    switch (select_config(a.M, a.N, a.splits > 0)) {
-        case kDecode: return run_decode<QT, OT>(a, st);
-        case kDecodeSplit1:
-        case kDecodeSplit2:
-        case kDecodeSplit4: return run_decode_sk<QT, OT>(a, st);
+    switch (select_config(a.M, a.N)) {
+        case kDecode64x16: return run_decode<QT, OT, 64, 1, 512, 2>(a, st);
+        case kDecode64x64: return run_decode<QT, OT, 64, 4, 256, 2>(a, st);
+        case kDecode16x16: return run_decode<QT, OT, 16, 1, 1024, 2>(a, st);
+        case kDecode16x64: return run_decode<QT, OT, 16, 4, 512, 2>(a, st);
         case kTile256x256: return run_tile<QT, OT, 256, 256, 2, 4>(a, st);
         case kTile256x128: return run_tile<QT, OT, 256, 128, 4, 2>(a, st);
         case kTile128x128: return run_tile<QT, OT, 128, 128, 2, 2>(a, st);
@@ -651,30 +543,6 @@ hipError_t dispatch_ot(int ot, const GemmArgs& a, hipStream_t st) {
 
 }  // namespace
 
-// The workspace starts with a fixed region of tile counters, so that the
-// partial sums of one call never land where another call keeps its counters.
-constexpr int64_t kCounterBytes = 65536;
-
-DecodePlan plan_decode(int64_t M, int64_t N, int64_t K) {
-    DecodePlan d{0, 0, 0};
-    if (M < 1 || M > 64 || N < 1) return d;
-    const int64_t tiles = (N + 63) / 64;
-    const int64_t slices = (K + kBK - 1) / kBK;
-    // Measured on MI355X (Llama-3-8B decode shapes, M = 1..64): the 64-column
-    // split-K kernel wins once N gives at least 256 column tiles (gate_up,
-    // 28672 wide), where two splits keep ~900 workgroups in flight; on
-    // narrower N its partial-sum traffic (splits x M x N x 4 bytes each way)
-    // costs more than it saves, and the 16-column kernel without a workspace
-    // is faster. splits == 0 selects that kernel.
-    if (tiles < 256 || tiles * 4 > kCounterBytes) return d;
-    const int64_t splits = std::max<int64_t>(1, std::min<int64_t>(2, slices / 4));
-    d.splits = static_cast<int>(splits);
-    d.slices_per_split = static_cast<int>((slices + splits - 1) / splits);
-    if (d.slices_per_split == 0) d.slices_per_split = 1;
-    if (splits > 1) d.workspace_bytes = kCounterBytes + splits * M * N * 4;
-    return d;
-}
-
 hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     GemmArgs a;
@@ -694,28 +562,16 @@ hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st) {
     a.tiles_m = a.tiles_n = 0;
     const int esz = (p.ot == D_BF16 || p.ot == D_FP16) ? 2 : 4;
     a.vec_out = (reinterpret_cast<uintptr_t>(p.out) % (4 * esz) == 0) && (p.ldo % 4 == 0);
-    a.ws_part = nullptr;
-    a.ws_count = nullptr;
-    a.splits = 0;
-    a.slices_per_split = 0;
-    if (p.splitk && p.M <= 64) {
-        const DecodePlan d = plan_decode(p.M, p.N, p.K);  // splits == 0: plain decode kernel
-        a.splits = d.splits;
-        a.slices_per_split = d.slices_per_split;
-        a.ws_count = static_cast<uint32_t*>(p.workspace);
-        a.ws_part = static_cast<uint8_t*>(p.workspace) + kCounterBytes;
-    }
     if (p.qt == Q_FP8) return dispatch_ot<Q_FP8>(p.ot, a, st);
     return dispatch_ot<Q_INT8>(p.ot, a, st);
 }
 
-const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K, bool splitk) {
-    const bool planned = splitk && M <= 64 && plan_decode(M, N, K).splits > 0;
-    switch (select_config(M, N, planned)) {
-        case kDecode: return "gemm_decode_kernel";
-        case kDecodeSplit1: return "gemm_decode_sk_kernel<MT=1>";
-        case kDecodeSplit2: return "gemm_decode_sk_kernel<MT=2>";
-        case kDecodeSplit4: return "gemm_decode_sk_kernel<MT=4>";
+const char* scaled_mm_kernel_name(int64_t M, int64_t N) {
+    switch (select_config(M, N)) {
+        case kDecode64x16: return "gemm_decode_kernel<64x16>";
+        case kDecode64x64: return "gemm_decode_kernel<64x64>";
+        case kDecode16x16: return "gemm_decode_kernel<16x16>";
+        case kDecode16x64: return "gemm_decode_kernel<16x64>";
         case kTile256x256: return "gemm_tile_kernel<256x256>";
         case kTile256x128: return "gemm_tile_kernel<256x128>";
         case kTile128x128: return "gemm_tile_kernel<128x128>";

@@ -31,22 +31,11 @@ struct GemmProblem {
     bool sa_per_row;
     const float* sb;  // NULL: 1.0
     bool sb_per_col;
-    bool splitk;      // decode path may split K (needs plan_decode().workspace_bytes)
-    void* workspace;  // zero-initialised before first use; left zeroed
 };
-
-// How the decode path (M <= 64) splits K across workgroups when given a
-// workspace; workspace_bytes == 0 means no workspace is needed.
-struct DecodePlan {
-    int splits;
-    int slices_per_split;
-    int64_t workspace_bytes;
-};
-DecodePlan plan_decode(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st);
 
 // Name of the kernel configuration a problem runs with.
-const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K, bool splitk);
+const char* scaled_mm_kernel_name(int64_t M, int64_t N);
 
 }  // namespace w8a8

@@ -118,3 +118,16 @@ def test_binding_layout_errors_are_python_errors():
     a = torch.zeros(4, 128, dtype=torch.float8_e4m3fn)
     with pytest.raises(ValueError):
         w8.w8a8_scaled_mm(a, a.t(), None, None)
+
+
+def test_kernel_configuration_names(lib):
+    """Host-only query of the kernel configuration a GEMM problem runs with."""
+    name = lambda M, N, K: lib.w8a8_scaled_mm_kernel(M, N, K).decode()
+    assert name(1, 4096, 4096) == "gemm_decode_kernel<16x16>"
+    assert name(64, 6144, 4096) == "gemm_decode_kernel<16x64>"
+    assert name(1, 28672, 4096) == "gemm_decode_kernel<64x16>"
+    assert name(17, 28672, 4096) == "gemm_decode_kernel<64x64>"
+    assert name(8192, 28672, 4096) == "gemm_tile_kernel<256x256>"
+    assert name(2048, 4096, 4096) == "gemm_tile_kernel<256x128>"
+    assert name(512, 4096, 4096) == "gemm_tile_kernel<64x64>"
+    assert name(-1, 4, 4) == ""

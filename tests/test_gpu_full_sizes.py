@@ -1,5 +1,5 @@
 """Parity at the workloads' full sizes, in the launch configuration bench.py
-times (graph-free here, same library calls, workspace "auto"), on sampled
+times (graph-free here, same library calls), on sampled
 output rows the oracle computes one by one.
 
 Workloads: fp8 decode and prefill GEMMs at the Llama-3-8B layer shapes

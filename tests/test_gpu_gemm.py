@@ -237,51 +237,29 @@ def bits_t(t):
     return t.view(torch.int16)
 
 
-def _run_ws(a, b, qtype, sa, sb, otype, workspace):
-    ad = codes_to_dev(a, qtype)
-    bd = codes_to_dev(b, qtype)
-    sad = None if sa is None else torch.from_numpy(np.asarray(sa, np.float32)).to(DEV)
-    sbd = None if sb is None else torch.from_numpy(np.asarray(sb, np.float32)).to(DEV)
-    out = w8.w8a8_scaled_mm(ad, bd.t(), sad, sbd, TORCH_OF[otype], workspace=workspace)
-    torch.cuda.synchronize()
-    return out
+# Shapes that select each decode configuration: 64-column blocks (N with at
+# least 256 column tiles) and 16-column blocks, at M <= 16 and M <= 64, with
+# ragged M, N and K tails and K past several ring stages.
+DECODE_SHAPES = [(1, 4096, 4096), (5, 6144 + 16, 4096 + 16), (16, 4096, 14336), (17, 100, 272),
+                 (33, 1000, 1040), (64, 4096, 4096), (64, 48, 144), (1, 16384 + 16, 1024 + 16),
+                 (16, 16384, 2064), (17, 16384, 2048), (64, 16400, 272), (40, 20000, 512),
+                 (3, 16336, 16), (64, 28672, 4096)]
 
 
 @pytest.mark.parametrize("qtype", ["fp8", "int8"])
-@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (5, 6144 + 16, 4096 + 16), (16, 4096, 14336),
-                                   (17, 100, 272), (33, 1000, 1040), (64, 4096, 4096),
-                                   (64, 48, 144), (1, 16384 + 16, 1024 + 16), (17, 16384, 2048),
-                                   (64, 16400, 272), (40, 20000, 512)])
-@pytest.mark.parametrize("workspace", ["auto", None])
-def test_decode_paths_parity(qtype, M, N, K, workspace):
-    """Both decode paths (split-K through a workspace, and the workspace-free
-    kernel) against the oracle."""
+@pytest.mark.parametrize("M,N,K", DECODE_SHAPES)
+def test_decode_configs_parity(qtype, M, N, K):
     a, sa, b, sb = _quantized(M, N, K, qtype, seed=3 * M + N + K)
-    got = _run_ws(a, b, qtype, sa, sb, "bf16", workspace)
+    got = _run(a, b, qtype, sa, sb, "bf16")
     info = check_scaled_mm(got, a, b, qtype, sa, sb, "bf16")
     assert info["exact_frac"] > 0.9, info
     if qtype == "int8":
-        raw = _run_ws(a, b, qtype, None, None, "i32", workspace)
+        raw = _run(a, b, qtype, None, None, "i32")
         check_scaled_mm(raw, a, b, qtype, None, None, "i32")
 
 
-def test_splitk_workspace_is_reusable():
-    """Two calls in a row on one workspace (the second smaller): the tile
-    counters return to zero after each call, so both results are right."""
-    ws = torch.zeros(w8.w8a8_scaled_mm_workspace_size("fp8", 64, 16384, 1024), dtype=torch.uint8,
-                     device=DEV)
-    for M, N, K, seed in [(64, 16384, 1024, 1), (16, 16400, 512, 2), (64, 16384, 1024, 3)]:
-        a, sa, b, sb = _quantized(M, N, K, "fp8", seed=seed)
-        got = _run_ws(a, b, "fp8", sa, sb, "bf16", ws)
-        check_scaled_mm(got, a, b, "fp8", sa, sb, "bf16")
-    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0  # counters back to zero
-
-
-def test_splitk_workspace_too_small_is_an_error():
-    a = torch.zeros(4, 1024, dtype=torch.float8_e4m3fn, device=DEV)
-    b = torch.zeros(16384, 1024, dtype=torch.float8_e4m3fn, device=DEV).t()
-    need = w8.w8a8_scaled_mm_workspace_size("fp8", 4, 16384, 1024)
-    assert need > 0
-    small = torch.zeros(need - 256, dtype=torch.uint8, device=DEV)
-    with pytest.raises(w8.W8A8Error, match="workspace"):
-        w8.w8a8_scaled_mm(a, b, None, None, workspace=small)
+def test_decode_configs_are_the_ones_named():
+    """The shapes above cover every decode configuration."""
+    names = {w8.w8a8_scaled_mm_kernel(M, N, K) for M, N, K in DECODE_SHAPES}
+    assert names == {"gemm_decode_kernel<16x16>", "gemm_decode_kernel<16x64>",
+                     "gemm_decode_kernel<64x16>", "gemm_decode_kernel<64x64>"}, names
