@@ -134,19 +134,12 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t nbytes) 
     return r;
 }
 
-// LDS layout of one 32-row x 128-byte operand group (4 KB), in the order the
-// 32 x 32 MFMAs consume it: half h (2 KB, K bytes 64h .. 64h+63) holds two
-// 1 KB sub-blocks s; entry p (16 bytes) of sub-block s is row p % 32 at K
-// bytes 64h + 32s + 16 (p / 32). One wave-wide direct load fills one
-// sub-block from 32 rows x 32 contiguous bytes, and a lane's reads of
-// 16-byte words at 16 * lane are bank-conflict free.
-//  - fp8 (v_mfma_f32_32x32x64_f8f6f4, 64 K per op): lane l's fragment for
-//    half h is sub-block 0 word l followed by sub-block 1 word l;
-//  - int8 (v_mfma_i32_32x32x32_i8, 32 K per op): sub-block s alone is the
-//    fragment of one op.
-// The K order inside a fragment differs from memory order; A and B use the
-// same order, so the sum is the same, and every run of 8 consecutive k stays
-// one input group of the fp8 matrix core.
+// LDS layout of a tile stage: every operand row keeps its 128 K bytes in
+// one 128-byte LDS row, 32-row groups of 4 KB one after another. The 16-byte
+// chunk c of row r sits at slot c ^ ((r / 2) % 8), so that the 32 x 32
+// fragment reads below (lanes 0..31 on rows 0..31 at one chunk, lanes
+// 32..63 two chunks further) meet every LDS bank once per 16 lanes. One
+// wave-wide direct load fills 8 rows x 128 bytes: whole cache lines.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
@@ -161,32 +154,31 @@ struct Acc32Of<Q_INT8> {
     typedef i32x16 type;
 };
 
+// The 32-byte fragment of K half h (bytes 64h .. 64h+63) for one 32-row
+// group: lane l takes row l % 32, K bytes 64h + 32 (l / 32) .. +31 (the
+// operand layout of v_mfma_f32_32x32x64_f8f6f4).
+__device__ __forceinline__ i32x8 frag32(const uint8_t* group, int h, int lane) {
+    const int r = lane & 31, sw = (r >> 1) & 7;
+    const int c = 4 * h + 2 * (lane >> 5);
+    const uint8_t* row = group + r * 128;
+    return join(*reinterpret_cast<const u32x4*>(row + 16 * (c ^ sw)),
+                *reinterpret_cast<const u32x4*>(row + 16 * ((c + 1) ^ sw)));
+}
+
 // c += W_frag . X_frag over one 64-byte K half: the weight fragment is the
 // first operand, so the result's 32 x 32 tile has output columns (n) along
-// its rows and output rows (m) along lanes.
+// its rows and output rows (m) along lanes. int8 splits the half into two
+// 32-deep products over the fragment's two 16-byte words; both operands
+// take the same words, so the integer sum is unchanged.
 template <int QT>
-__device__ __forceinline__ void mma32_half(typename Acc32Of<QT>::type& c, const uint8_t* wb,
-                                           const uint8_t* xb, int lane) {
-    const u32x4 w0 = *reinterpret_cast<const u32x4*>(wb + 16 * lane);
-    const u32x4 w1 = *reinterpret_cast<const u32x4*>(wb + 1024 + 16 * lane);
-    const u32x4 x0 = *reinterpret_cast<const u32x4*>(xb + 16 * lane);
-    const u32x4 x1 = *reinterpret_cast<const u32x4*>(xb + 1024 + 16 * lane);
+__device__ __forceinline__ void mma32(typename Acc32Of<QT>::type& c, const i32x8& w, const i32x8& x) {
     if constexpr (QT == Q_FP8) {
-        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(join(w0, w1), join(x0, x1), c, 0, 0, 0,
-                                                            0, 0, 0);
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, c, 0, 0, 0, 0, 0, 0);
     } else {
-        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-            i32x4{static_cast<int>(w0[0]), static_cast<int>(w0[1]), static_cast<int>(w0[2]),
-                  static_cast<int>(w0[3])},
-            i32x4{static_cast<int>(x0[0]), static_cast<int>(x0[1]), static_cast<int>(x0[2]),
-                  static_cast<int>(x0[3])},
-            c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-            i32x4{static_cast<int>(w1[0]), static_cast<int>(w1[1]), static_cast<int>(w1[2]),
-                  static_cast<int>(w1[3])},
-            i32x4{static_cast<int>(x1[0]), static_cast<int>(x1[1]), static_cast<int>(x1[2]),
-                  static_cast<int>(x1[3])},
-            c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{w[0], w[1], w[2], w[3]},
+                                                  i32x4{x[0], x[1], x[2], x[3]}, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(i32x4{w[4], w[5], w[6], w[7]},
+                                                  i32x4{x[4], x[5], x[6], x[7]}, c, 0, 0, 0);
     }
 }
 
@@ -240,17 +232,24 @@ __device__ __forceinline__ void store4(const GemmArgs& p, int m, int n, const Ac
 }
 
 // BM x BN block tile; WGM x WGN waves, each owning a (BM/WGM) x (BN/WGN)
-// wave tile of 32 x 32 MFMA tiles. K is walked in 128-byte slices through two
-// LDS stages filled by direct loads: the loads of slice k+1 are in flight
-// while the MFMAs consume slice k, with one barrier per slice.
+// wave tile of 32 x 32 MFMA tiles. K is walked in 128-byte stages through a
+// 2-stage LDS ring filled by direct loads, the loads of stage k+1 in flight
+// while stage k is consumed, one barrier per stage. Inside a stage the
+// fragments of the next 64-byte half are read from LDS while the MFMAs of
+// the current half run (two register sets, interleaved by the scheduler
+// hints below).
 template <int QT, int OT, int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
     typedef typename Acc32Of<QT>::type Acc;
     constexpr int NW = WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int kGroup = 32 * kBK;          // one 32-row group of a stage
     constexpr int kStage = (BM + BN) * kBK;
-    constexpr int kLoads = (BM + BN) / 8;  // 1 KB wave-wide loads per stage
+    constexpr int kLoads = (BM + BN) / 8;     // 1 KB wave-wide loads per stage
+    constexpr int kLPW = kLoads / NW;
+    constexpr int kMfma = TM * TN * (QT == Q_FP8 ? 1 : 2), kReads = 2 * (TM + TN);
+    constexpr int kReadsPerMfma = (kReads + kMfma - 1) / kMfma;
     static_assert(TM >= 1 && TN >= 1 && kLoads % NW == 0, "tile shape");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
 
@@ -266,31 +265,32 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
                                  static_cast<uint32_t>((rows_a - 1) * p.lda + p.K));
     const i32x4 rb = buffer_rsrc(p.b + static_cast<int64_t>(n0) * p.ldb,
                                  static_cast<uint32_t>((rows_b - 1) * p.ldb + p.K));
-    const int q_row = lane & 31, q_k = 16 * (lane >> 5);
 
-    // Per load: this lane's byte offset within the slice (or out of range).
-    int base_off[kLoads / NW];
+    // Load j of this wave: 8 rows x 128 bytes; lane q reads row 8 (i % 4) + q / 8
+    // of 32-row group i / 4, the 16-byte chunk that lands at slot q % 8.
+    int base_off[kLPW], kin[kLPW];
 #pragma unroll
-    for (int j = 0; j < kLoads / NW; ++j) {
+    for (int j = 0; j < kLPW; ++j) {
         const int i = wave + NW * j;
         const bool is_a = i < BM / 8;
         const int ii = is_a ? i : i - BM / 8;
-        const int row = 32 * (ii >> 2) + q_row;
+        const int r = 8 * (ii & 3) + (lane >> 3);
+        const int row = 32 * (ii >> 2) + r;
+        kin[j] = 16 * ((lane & 7) ^ ((r >> 1) & 7));
         base_off[j] = (row < (is_a ? rows_a : rows_b))
-                          ? row * static_cast<int>(is_a ? p.lda : p.ldb) + 32 * (ii & 3) + q_k
+                          ? row * static_cast<int>(is_a ? p.lda : p.ldb) + kin[j]
                           : kOutOfRange;
     }
     auto issue = [&](int kt, int buf) {
         uint8_t* st = smem + buf * kStage;
 #pragma unroll
-        for (int j = 0; j < kLoads / NW; ++j) {
+        for (int j = 0; j < kLPW; ++j) {
             const int i = wave + NW * j;
             const bool is_a = i < BM / 8;
-            const int ii = is_a ? i : i - BM / 8;
-            const bool ok = base_off[j] != kOutOfRange && kt * kBK + 32 * (ii & 3) + q_k < p.K;
+            const bool ok = base_off[j] != kOutOfRange && kt * kBK + kin[j] < p.K;
             const int off = ok ? base_off[j] + kt * kBK : kOutOfRange;
-            uint8_t* dst = st + (is_a ? 0 : BM * kBK) + (ii >> 2) * 4096 + (ii & 3) * 1024;
-            raw_buffer_load_lds(is_a ? ra : rb, (lds_u32p)(dst), 16, off, 0, 0, 0);
+            raw_buffer_load_lds(is_a ? ra : rb, (lds_u32p)(st + (is_a ? 0 : BM * kBK) + (is_a ? i : i - BM / 8) * 1024),
+                                16, off, 0, 0, 0);
         }
     };
 
@@ -302,23 +302,53 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    const int KT = (p.K + kBK - 1) / kBK;
-    if (KT > 0) issue(0, 0);
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (kt + 1 < KT) issue(kt + 1, cur ^ 1);
-        const uint8_t* sa = smem + cur * kStage;
+    i32x8 xa[TM], wa[TN], xb[TM], wb[TN];  // two fragment sets
+    auto read = [&](i32x8* x, i32x8* w, int buf, int h) {
+        const uint8_t* sa = smem + buf * kStage;
         const uint8_t* sb = sa + BM * kBK;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int i = 0; i < TM; ++i) x[i] = frag32(sa + (wm * TM + i) * kGroup, h, lane);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+        for (int j = 0; j < TN; ++j) w[j] = frag32(sb + (wn * TN + j) * kGroup, h, lane);
+    };
+    auto mfmas = [&](const i32x8* x, const i32x8* w) {
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    mma32_half<QT>(acc[i][j], sb + (wn * TN + j) * 4096 + h * 2048,
-                                   sa + (wm * TM + i) * 4096 + h * 2048, lane);
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) mma32<QT>(acc[i][j], w[j], x[i]);
+    };
+    // Scheduler hint: alternate one MFMA with a few LDS reads.
+    auto interleave = [&]() {
+#pragma unroll
+        for (int t = 0; t < kMfma; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerMfma, 0);
+        }
+    };
+
+    const int KT = (p.K + kBK - 1) / kBK;
+    if (KT > 0) {
+        issue(0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (KT > 1) issue(1, 1);
+        read(xa, wa, 0, 0);
+        for (int kt = 0; kt + 1 < KT; ++kt) {
+            const int cur = kt & 1;
+            read(xb, wb, cur, 1);  // half 1 of stage kt, while half 0 runs
+            mfmas(xa, wa);
+            interleave();
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            __syncthreads();  // stage kt+1 has landed; every wave is done reading stage kt
+            if (kt + 2 < KT) issue(kt + 2, cur);
+            read(xa, wa, cur ^ 1, 0);  // half 0 of stage kt+1, while half 1 of kt runs
+            mfmas(xb, wb);
+            interleave();
+        }
+        read(xb, wb, (KT - 1) & 1, 1);
+        mfmas(xa, wa);
+        interleave();
+        mfmas(xb, wb);
     }
 
     // Fused epilogue. In a 32 x 32 tile lane l holds, for q = 0..3, output
