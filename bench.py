@@ -120,9 +120,10 @@ def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
     return launches, keep
 
 
-# A dynamic per-tensor quantisation is one library call of four kernels: zero
-# the max, the absmax reduction, the quantisation, and max -> scale.
-KV_QUANT_KERNELS = "fill_f32_kernel+absmax_kernel+quant_tensor_kernel+finalize_scale_kernel"
+# A dynamic per-tensor quantisation is one library call of three kernels: the
+# absmax pass (partial maxima), the quantisation, and the scale plus the last
+# few KB of codes.
+KV_QUANT_KERNELS = "absmax_kernel+quant_tensor_kernel+finish_tail_kernel"
 
 
 def build_kv_workload(dev, layers=workloads.KV_LAYERS):

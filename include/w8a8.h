@@ -95,8 +95,9 @@ w8a8_status w8a8_quant_per_token(const void* x, w8a8_dtype xt, int64_t M, int64_
  * dynamic == 0 (static, calibrated): s = *scale (scale == NULL means 1.0,
  *   the pages' default); *scale is not written.
  * dynamic == 1: s = absmax(x) / Qmax is computed and written to *scale
- *   (scale must not be NULL). This takes four short kernels on `stream`;
- *   *scale holds intermediate values until the last one ends.
+ *   (scale must not be NULL). This takes three kernels on `stream`; until the
+ *   last one ends, the last (at most 4 KB of) codes of q hold intermediate
+ *   values (partial maxima).
  * q[m, k] = enc(x[m, k] / s), row strides ldx (elements) and ldq (bytes).
  */
 w8a8_status w8a8_quant_per_tensor(const void* x, w8a8_dtype xt, int64_t M, int64_t K, int64_t ldx,
@@ -132,7 +133,9 @@ w8a8_status w8a8_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* a,
  * elements (e.g. one layer's K or V cache) [P3 "Scaling semantics": per
  * tensor scale = absmax / 448, q = fp8(x / scale)].
  * dynamic == 1: *scale = absmax / 448 is computed and written (as in
- * w8a8_quant_per_tensor). dynamic == 0: the given *scale is used (NULL: 1.0).
+ * w8a8_quant_per_tensor, three kernels, the tail of q holding intermediate
+ * values until the last ends). dynamic == 0: the given *scale is used
+ * (NULL: 1.0).
  * q: device, n bytes of e4m3fn codes. n must be a multiple of 16.
  */
 w8a8_status kv_fp8_scaled_quant(const void* x, w8a8_dtype xt, int64_t n, uint8_t* q, float* scale,

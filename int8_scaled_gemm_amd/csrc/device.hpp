@@ -127,6 +127,11 @@ __device__ __forceinline__ float scale_from_absmax(float amax) {
     return amax == 0.0f ? 1.0f : amax / QMax<QT>::value;
 }
 
+template <int QT>
+__host__ __device__ constexpr float scale_of_zero() {
+    return 1.0f;  // the scale of an all-zero group (scale_from_absmax(0))
+}
+
 // --------------------------------------------------------- output stores
 // The float argument is first pinned in a register: otherwise instruction
 // selection folds a preceding float multiply into the narrowing conversion

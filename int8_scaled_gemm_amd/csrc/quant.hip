@@ -12,6 +12,8 @@
 // (bf16 -> code), plus a 2-byte read pass for a dynamic per-tensor scale.
 // Loads and stores are 16-byte vectors per lane; a row's absmax is reduced
 // across the wavefront with lane shuffles, and across waves through LDS.
+#include <algorithm>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -126,28 +128,45 @@ __device__ __forceinline__ bool unit_coords(const Units& u, uint32_t id, int64_t
     return k < K;
 }
 
-// Writes v into *p (a float). Used to reset the absmax slot, as a kernel so
-// that a captured graph holds no memset node.
+// Writes v into *p (a float), as a kernel so that a captured graph holds no
+// memset node.
 __global__ void fill_f32_kernel(float* p, float v) { *p = v; }
 
-// absmax over the tensor, merged into *amax_slot (float bits; every value is
-// >= 0, so unsigned integer order is float order).
+// Dynamic per-tensor scale without atomics or a workspace: every absmax
+// workgroup stores its partial maximum (a float) in the tail of the code
+// buffer q, the last `tail` elements of the tensor in row order. The quantise
+// pass reduces the partials in every workgroup (a few KB, L2-resident) and
+// leaves the tail alone; a last one-workgroup kernel reduces them once more,
+// writes the scale and quantises the tail over them. The maximum does not
+// depend on the order of the partials, so the scale is deterministic.
+constexpr int kAbsUnroll = 8;  // loads in flight per lane in the read-only absmax pass
+
+struct Tail {
+    int64_t start;  // first tail element (row-major index over M x K)
+    int parts;      // partial maxima stored at the start of the tail, 4 bytes each
+};
+
+// Address of byte e of the row-major M x K code tensor with row stride ldq.
+__device__ __forceinline__ uint8_t* code_at(uint8_t* q, int64_t ldq, int64_t K, int64_t e) {
+    return q + (e / K) * ldq + (e % K);
+}
+
 template <int XT>
 __global__ __launch_bounds__(kBlock) void absmax_kernel(const void* __restrict__ x, int64_t ldx,
-                                                        Units u, int64_t K,
-                                                        float* __restrict__ amax_slot) {
+                                                        Units u, int64_t K, uint8_t* q,
+                                                        int64_t ldq, Tail tail) {
     float amax = 0.0f;
-    for (uint32_t base = blockIdx.x * kUnroll; base < u.total; base += gridDim.x * kUnroll) {
-        float v[kUnroll][8];
-        bool ok[kUnroll];
+    for (uint32_t base = blockIdx.x * kAbsUnroll; base < u.total; base += gridDim.x * kAbsUnroll) {
+        float v[kAbsUnroll][8];
+        bool ok[kAbsUnroll];
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
+        for (int j = 0; j < kAbsUnroll; ++j) {
             int64_t row, k;
             ok[j] = unit_coords(u, base + j, K, row, k);
             if (ok[j]) load8<XT>(x, row * ldx + k, v[j]);
         }
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j)
+        for (int j = 0; j < kAbsUnroll; ++j)
             if (ok[j])
 #pragma unroll
                 for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
@@ -159,21 +178,34 @@ __global__ __launch_bounds__(kBlock) void absmax_kernel(const void* __restrict__
     if (threadIdx.x == 0) {
 #pragma unroll
         for (int w = 0; w < kBlock / 64; ++w) amax = fmaxf(amax, part[w]);
-        atomicMax(reinterpret_cast<unsigned int*>(amax_slot), __float_as_uint(amax));
+        *reinterpret_cast<float*>(code_at(q, ldq, K, tail.start + 4 * blockIdx.x)) = amax;
     }
 }
 
-// Quantise with one scale for the whole tensor. FROM_AMAX: *scale holds the
-// tensor's absmax (bits) and the scale is derived here; otherwise *scale is
-// the scale itself, NULL meaning 1.0.
-template <int XT, int QT, bool FROM_AMAX>
+// Maximum of the stored partials, in every thread of the workgroup.
+__device__ float reduce_partials(uint8_t* q, int64_t ldq, int64_t K, const Tail& tail) {
+    float amax = 0.0f;
+    for (int i = threadIdx.x; i < tail.parts; i += kBlock)
+        amax = fmaxf(amax, *reinterpret_cast<const float*>(code_at(q, ldq, K, tail.start + 4 * i)));
+    amax = wave_max(amax);
+    __shared__ float part[kBlock / 64];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) amax = fmaxf(amax, part[w]);
+    return amax;
+}
+
+// Quantise with one scale for the whole tensor. DYNAMIC: the scale comes
+// from the partial maxima in the tail, and the tail is left to
+// finish_tail_kernel; otherwise *scale is the scale (NULL: 1.0).
+template <int XT, int QT, bool DYNAMIC>
 __global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const void* __restrict__ x,
-                                                              int64_t ldx,
-                                                              uint8_t* __restrict__ q, int64_t ldq,
+                                                              int64_t ldx, uint8_t* q, int64_t ldq,
                                                               const float* __restrict__ scale,
-                                                              Units u, int64_t K) {
+                                                              Units u, int64_t K, Tail tail) {
     float s;
-    if constexpr (FROM_AMAX) s = scale_from_absmax<QT>(*scale);
+    if constexpr (DYNAMIC) s = scale_from_absmax<QT>(reduce_partials(q, ldq, K, tail));
     else s = scale ? *scale : 1.0f;
     const double r = 1.0 / static_cast<double>(s);
     for (uint32_t base = blockIdx.x * kUnroll; base < u.total; base += gridDim.x * kUnroll) {
@@ -183,6 +215,7 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const void* __rest
 #pragma unroll
         for (int j = 0; j < kUnroll; ++j) {
             ok[j] = unit_coords(u, base + j, K, row[j], k[j]);
+            if (DYNAMIC && ok[j] && row[j] * K + k[j] >= tail.start) ok[j] = false;
             if (ok[j]) load8<XT>(x, row[j] * ldx + k[j], v[j]);
         }
 #pragma unroll
@@ -191,9 +224,24 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const void* __rest
     }
 }
 
-// absmax (bits, in *scale) -> scale, in place. Runs after the quantise pass.
-template <int QT>
-__global__ void finalize_scale_kernel(float* scale) { *scale = scale_from_absmax<QT>(*scale); }
+// One workgroup: the scale from the partials, written to *scale, then the
+// tail's codes, over the partials once every thread has read them.
+template <int XT, int QT>
+__global__ __launch_bounds__(kBlock) void finish_tail_kernel(const void* __restrict__ x,
+                                                             int64_t ldx, uint8_t* q, int64_t ldq,
+                                                             float* scale, int64_t M, int64_t K,
+                                                             Tail tail) {
+    const float s = scale_from_absmax<QT>(reduce_partials(q, ldq, K, tail));
+    __syncthreads();  // every partial has been read
+    if (threadIdx.x == 0) *scale = s;
+    const double r = 1.0 / static_cast<double>(s);
+    for (int64_t e = tail.start + 8 * static_cast<int64_t>(threadIdx.x); e < M * K; e += 8 * kBlock) {
+        const int64_t row = e / K, k = e % K;  // 8 elements, never across a row (K % 16 == 0)
+        float v[8];
+        load8<XT>(x, row * ldx + k, v);
+        *reinterpret_cast<u32x2*>(q + row * ldq + k) = quant8<QT>(v, r);
+    }
+}
 
 // ------------------------------------------------------------------------
 // KV dequant: 16 codes per lane (one 16-byte load), product in float32,
@@ -300,15 +348,22 @@ hipError_t per_tensor_typed(const void* x, int64_t M, int64_t K, int64_t ldx, ui
     const Units u = make_units(M, K);
     const int g = grid_for(u.total, kUnroll);
     if (dynamic) {
-        // Every absmax workgroup merges its result with one atomic on the
-        // same word: keep them few (two per CU), each striding over the data.
-        const int ga = g < 512 ? g : 512;
-        hipLaunchKernelGGL(fill_f32_kernel, dim3(1), dim3(1), 0, st, scale, 0.0f);
-        hipLaunchKernelGGL((absmax_kernel<XT>), dim3(ga), dim3(kBlock), 0, st, x, ldx, u, K, scale);
-        hipLaunchKernelGGL((quant_tensor_kernel<XT, QT, true>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, static_cast<const float*>(scale), u, K);
-        hipLaunchKernelGGL((finalize_scale_kernel<QT>), dim3(1), dim3(1), 0, st, scale);
+        const int64_t total = M * K;
+        if (total == 0) {  // an empty tensor has absmax 0: scale 1.0
+            hipLaunchKernelGGL(fill_f32_kernel, dim3(1), dim3(1), 0, st, scale, scale_of_zero<QT>());
+            return hipGetLastError();
+        }
+        Tail tail;
+        tail.parts = std::min(grid_for(u.total, kAbsUnroll), 1024);
+        // the tail holds the partials; small tensors are finished by the last kernel alone
+        const int64_t tail_len = (4 * static_cast<int64_t>(tail.parts) + 15) / 16 * 16;
+        tail.start = total <= 65536 ? 0 : total - tail_len;
+        hipLaunchKernelGGL((absmax_kernel<XT>), dim3(tail.parts), dim3(kBlock), 0, st, x, ldx, u, K, q, ldq, tail);
+        if (tail.start > 0)
+            hipLaunchKernelGGL((quant_tensor_kernel<XT, QT, true>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, static_cast<const float*>(scale), u, K, tail);
+        hipLaunchKernelGGL((finish_tail_kernel<XT, QT>), dim3(1), dim3(kBlock), 0, st, x, ldx, q, ldq, scale, M, K, tail);
     } else {
-        hipLaunchKernelGGL((quant_tensor_kernel<XT, QT, false>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, static_cast<const float*>(scale), u, K);
+        hipLaunchKernelGGL((quant_tensor_kernel<XT, QT, false>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, static_cast<const float*>(scale), u, K, Tail{0, 0});
     }
     return hipGetLastError();
 }
