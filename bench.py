@@ -10,7 +10,8 @@ nothing, so a whole step captures). Workloads:
           layers (QKV 6144x4096, O 4096x4096, gate_up 28672x4096, down
           4096x14336) at M = 1, 16, 64: for each, dynamic per-token fp8
           quantisation of the bf16 activations, then the scaled GEMM with
-          per-channel fp8 weights, bf16 out.
+          per-channel fp8 weights, bf16 out (at M = 1 both in one kernel,
+          w8a8_quant_scaled_mm).
   prefill the same layers at M = 512, 2048, 8192 with a static per-tensor
           activation scale (calibrated on a seeded [512, K] batch), bf16 out.
   int8    Llama-3-70B layers (QKV 10240x8192, O 8192x8192, gate_up
@@ -111,11 +112,21 @@ def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
                 qbytes = 3 * M * K + 4
             mf = (lambda q=q, wq=wq, s=s, ws=ws, out=out:
                   w8.w8a8_scaled_mm(q, wq.t(), s, ws, torch.bfloat16, out=out))
-            qkern = ("quant_rows_kernel" if act_scheme == "per_token" else "quant_tensor_kernel")
-            launches.append(Launch("quant", qf, 0, qbytes, f"quant M={M} {name}", qkern))
-            launches.append(Launch("gemm", mf, 2 * M * N * K, _gemm_bytes(M, N, K, n_sa, N),
-                                   f"gemm M={M} {name} {N}x{K}",
-                                   w8.w8a8_scaled_mm_kernel(M, N, K)))
+            fused = (act_scheme == "per_token"
+                     and w8.w8a8_quant_scaled_mm_kernel(M, N, K) == "gemm_dynq_kernel")
+            if fused:  # one kernel quantises the token and runs the product
+                ff = (lambda x=x, wq=wq, ws=ws, out=out, q=q, s=s:
+                      w8.w8a8_quant_scaled_mm(x, wq.t(), ws, qtype, torch.bfloat16, out=out,
+                                              q=q, a_scales=s))
+                launches.append(Launch("gemm", ff, 2 * M * N * K,
+                                       _gemm_bytes(M, N, K, n_sa, N) + qbytes - M * K,
+                                       f"quant+gemm M={M} {name} {N}x{K}", "gemm_dynq_kernel"))
+            else:
+                qkern = ("quant_rows_kernel" if act_scheme == "per_token" else "quant_tensor_kernel")
+                launches.append(Launch("quant", qf, 0, qbytes, f"quant M={M} {name}", qkern))
+                launches.append(Launch("gemm", mf, 2 * M * N * K, _gemm_bytes(M, N, K, n_sa, N),
+                                       f"gemm M={M} {name} {N}x{K}",
+                                       w8.w8a8_scaled_mm_kernel(M, N, K)))
             keep += [wq, ws, x, q, s, out]
     return launches, keep
 

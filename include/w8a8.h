@@ -129,6 +129,26 @@ w8a8_status w8a8_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* a,
                            int64_t n_b, hipStream_t stream);
 
 /*
+ * Dynamic per-token quantisation followed by the scaled matrix multiply, the
+ * decode step of a w8a8 linear layer [P1 bullet list: per-token activation
+ * scales with per-channel weight scales; P2: dynamic activation scales]:
+ *   w8a8_quant_per_token(x -> q, a_scales), then
+ *   w8a8_scaled_mm(out, q, B, a_scales (per token), b_scales).
+ * Same arguments and rules as those two calls: x [M, K] (row stride ldx
+ * elements, type xt in BF16/FP16/F32), q [M, ldq] codes and a_scales [M]
+ * (device, written: the caller can reuse them), B and b_scales as in
+ * w8a8_scaled_mm, out of type BF16/FP16/F32 (I32 is refused). Results are
+ * identical to the two calls (codes and scales bit for bit, out up to the
+ * fp8 accumulation order). M == 1 with K <= 15360 runs as one kernel that
+ * quantises the row in every workgroup; other sizes run the two kernels.
+ */
+w8a8_status w8a8_quant_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* x,
+                                 w8a8_dtype xt, int64_t ldx, const void* b, int64_t ldb,
+                                 w8a8_qtype qt, int64_t M, int64_t N, int64_t K,
+                                 const float* b_scales, int64_t n_b, void* q, int64_t ldq,
+                                 float* a_scales, hipStream_t stream);
+
+/*
  * Scaled fp8 KV-cache quantisation of one flat, contiguous tensor of n
  * elements (e.g. one layer's K or V cache) [P3 "Scaling semantics": per
  * tensor scale = absmax / 448, q = fp8(x / scale)].
@@ -157,6 +177,12 @@ w8a8_status kv_fp8_scaled_dequant(const uint8_t* q, int64_t n, const float* scal
  * that profiles can be matched to calls. Host-only.
  */
 const char* w8a8_scaled_mm_kernel(int64_t M, int64_t N, int64_t K);
+
+/*
+ * The same for w8a8_quant_scaled_mm: "gemm_dynq_kernel" for the fused
+ * one-token kernel, else "quant_rows_kernel+scaled_mm" (host-only).
+ */
+const char* w8a8_quant_scaled_mm_kernel(int64_t M, int64_t N, int64_t K);
 
 /* Name of a status code (static string). */
 const char* w8a8_status_string(w8a8_status s);

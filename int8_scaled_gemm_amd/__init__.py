@@ -51,6 +51,8 @@ SIGNATURES = {
     "w8a8_quant_per_tensor": [_P, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _I, _P],
     "w8a8_scaled_mm": [_P, _I, _I64, _P, _I64, _P, _I64, _I, _I64, _I64, _I64, _P, _I64, _P,
                        _I64, _P],
+    "w8a8_quant_scaled_mm": [_P, _I, _I64, _P, _I, _I64, _P, _I64, _I, _I64, _I64, _I64, _P, _I64,
+                             _P, _I64, _P, _P],
     "kv_fp8_scaled_quant": [_P, _I, _I64, _P, _P, _I, _P],
     "kv_fp8_scaled_dequant": [_P, _I64, _P, _P, _I, _P],
 }
@@ -89,6 +91,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.w8a8_version.restype = ctypes.c_char_p
     lib.w8a8_scaled_mm_kernel.argtypes = [_I64, _I64, _I64]
     lib.w8a8_scaled_mm_kernel.restype = ctypes.c_char_p
+    lib.w8a8_quant_scaled_mm_kernel.argtypes = [_I64, _I64, _I64]
+    lib.w8a8_quant_scaled_mm_kernel.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -240,6 +244,50 @@ def w8a8_scaled_mm(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | No
     return out
 
 
+def w8a8_quant_scaled_mm(x: torch.Tensor, b: torch.Tensor, b_scales: torch.Tensor | None,
+                         qtype="fp8", out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                         q: torch.Tensor | None = None,
+                         a_scales: torch.Tensor | None = None) -> torch.Tensor:
+    """Dynamic per-token quantisation of x, then D = a_scales (x) b_scales * (q @ b).
+
+    x: bf16/fp16/fp32 [M, K] with unit column stride; b: codes K x N,
+    column-major (e.g. weight.t()); b_scales: fp32 [1] or [N] or None.
+    q ([M, K] codes) and a_scales (fp32 [M]) receive the quantised
+    activations; they are allocated when not given. Returns out.
+    """
+    _check_cuda(x, b, b_scales, out, q, a_scales)
+    qt = _qtype(qtype)
+    if b.dtype != CODE_DTYPE[qt]:
+        raise ValueError(f"b must hold {CODE_DTYPE[qt]} codes, got {b.dtype}")
+    M, K, ldx = _rows(x, "x")
+    if b.dim() != 2 or b.size(0) != K:
+        raise ValueError(f"b must be K x N with K={K}, got shape {tuple(b.shape)}")
+    N = b.size(1)
+    if b.size(0) > 1 and b.stride(0) != 1:
+        raise ValueError("b must be column-major (K x N with stride(0) == 1), e.g. weight.t()")
+    ldb = b.stride(1) if N > 1 else max(K, b.stride(1))
+    if q is None:
+        q = torch.empty((M, K), dtype=CODE_DTYPE[qt], device=x.device)
+    if a_scales is None:
+        a_scales = torch.empty(M, dtype=torch.float32, device=x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _, _, ldq = _rows(q, "q")
+    _, _, ldo = _rows(out, "out")
+    sb = None if b_scales is None else b_scales.reshape(-1)
+    if sb is not None and (sb.dtype != torch.float32 or not sb.is_contiguous()):
+        raise ValueError("b_scales must be a contiguous float32 tensor")
+    _call("w8a8_quant_scaled_mm", _ptr(out), _dtype(out.dtype), ldo, _ptr(x), _dtype(x.dtype), ldx,
+          _ptr(b), ldb, qt, M, N, K, _ptr(sb), 0 if sb is None else sb.numel(), _ptr(q), ldq,
+          _ptr(a_scales), _stream(x))
+    return out
+
+
+def w8a8_quant_scaled_mm_kernel(M: int, N: int, K: int) -> str:
+    """Kernel(s) w8a8_quant_scaled_mm runs for an M x N x K problem."""
+    return load_library().w8a8_quant_scaled_mm_kernel(M, N, K).decode()
+
+
 def scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor | None,
               scale_b: torch.Tensor | None, out_dtype=torch.bfloat16,
               out: torch.Tensor | None = None) -> torch.Tensor:
@@ -257,6 +305,6 @@ def version() -> str:
 
 
 __all__ = ["w8a8_quant_per_token", "w8a8_quant_per_tensor", "w8a8_scaled_mm",
-           "w8a8_scaled_mm_kernel",
+           "w8a8_scaled_mm_kernel", "w8a8_quant_scaled_mm", "w8a8_quant_scaled_mm_kernel",
            "kv_fp8_scaled_quant", "kv_fp8_scaled_dequant", "scaled_mm", "W8A8Error",
            "load_library", "version", "LIB_PATH", "SIGNATURES"]

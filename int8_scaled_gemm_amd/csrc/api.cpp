@@ -66,10 +66,12 @@ w8a8_status check_quant_io(const char* fn, const void* x, w8a8_dtype xt, int64_t
     return W8A8_OK;
 }
 
-static w8a8_status scaled_mm_impl(const char* fn, void* out, w8a8_dtype ot, int64_t ldo, const void* a,
-                                  int64_t lda, const void* b, int64_t ldb, w8a8_qtype qt, int64_t M,
-                                  int64_t N, int64_t K, const float* a_scales, int64_t n_a,
-                                  const float* b_scales, int64_t n_b, hipStream_t stream) {
+// Checks of a scaled product's arguments (host only, from the arguments).
+static w8a8_status scaled_mm_check(const char* fn, void* out, w8a8_dtype ot, int64_t ldo,
+                                   const void* a, int64_t lda, const void* b, int64_t ldb,
+                                   w8a8_qtype qt, int64_t M, int64_t N, int64_t K,
+                                   const float* a_scales, int64_t n_a, const float* b_scales,
+                                   int64_t n_b) {
     if (!valid_qtype(qt)) return fail(W8A8_ERR_DTYPE, "%s: code type %d is not INT8 or FP8_E4M3FN", fn, qt);
     if (ot != W8A8_BF16 && ot != W8A8_FP16 && ot != W8A8_F32 && ot != W8A8_I32)
         return fail(W8A8_ERR_DTYPE, "%s: output type %d unknown", fn, ot);
@@ -101,6 +103,13 @@ static w8a8_status scaled_mm_impl(const char* fn, void* out, w8a8_dtype ot, int6
     if (reinterpret_cast<uintptr_t>(out) % elem_size(ot)) return fail(W8A8_ERR_ALIGNMENT, "%s: out is not aligned to its element size", fn);
     if ((a_scales && (reinterpret_cast<uintptr_t>(a_scales) & 3u)) || (b_scales && (reinterpret_cast<uintptr_t>(b_scales) & 3u)))
         return fail(W8A8_ERR_ALIGNMENT, "%s: scale arrays must be 4-byte aligned", fn);
+    return ok();
+}
+
+static w8a8::GemmProblem make_problem(void* out, w8a8_dtype ot, int64_t ldo, const void* a,
+                                      int64_t lda, const void* b, int64_t ldb, w8a8_qtype qt,
+                                      int64_t M, int64_t N, int64_t K, const float* a_scales,
+                                      int64_t n_a, const float* b_scales, int64_t n_b) {
     w8a8::GemmProblem p;
     p.out = out;
     p.ot = ot;
@@ -117,6 +126,18 @@ static w8a8_status scaled_mm_impl(const char* fn, void* out, w8a8_dtype ot, int6
     p.sa_per_row = a_scales && n_a == M && M != 1;
     p.sb = b_scales;
     p.sb_per_col = b_scales && n_b == N && N != 1;
+    return p;
+}
+
+static w8a8_status scaled_mm_impl(const char* fn, void* out, w8a8_dtype ot, int64_t ldo, const void* a,
+                                  int64_t lda, const void* b, int64_t ldb, w8a8_qtype qt, int64_t M,
+                                  int64_t N, int64_t K, const float* a_scales, int64_t n_a,
+                                  const float* b_scales, int64_t n_b, hipStream_t stream) {
+    w8a8_status s = scaled_mm_check(fn, out, ot, ldo, a, lda, b, ldb, qt, M, N, K, a_scales, n_a,
+                                    b_scales, n_b);
+    if (s != W8A8_OK || M == 0 || N == 0) return s;
+    w8a8::GemmProblem p = make_problem(out, ot, ldo, a, lda, b, ldb, qt, M, N, K, a_scales, n_a,
+                                       b_scales, n_b);
     return from_hip(w8a8::launch_scaled_mm(p, stream), fn);
 }
 
@@ -173,6 +194,30 @@ w8a8_status w8a8_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* a,
                            int64_t n_b, hipStream_t stream) {
     return scaled_mm_impl("w8a8_scaled_mm", out, ot, ldo, a, lda, b, ldb, qt, M, N, K, a_scales, n_a,
                           b_scales, n_b, stream);
+}
+
+w8a8_status w8a8_quant_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* x,
+                                 w8a8_dtype xt, int64_t ldx, const void* b, int64_t ldb,
+                                 w8a8_qtype qt, int64_t M, int64_t N, int64_t K,
+                                 const float* b_scales, int64_t n_b, void* q, int64_t ldq,
+                                 float* a_scales, hipStream_t stream) {
+    const char* fn = "w8a8_quant_scaled_mm";
+    if (ot == W8A8_I32) return fail(W8A8_ERR_DTYPE, "%s: the output is scaled: BF16, FP16 or F32", fn);
+    w8a8_status s = check_quant_io(fn, x, xt, M, K, ldx, q, qt, ldq);
+    if (s != W8A8_OK) return s;
+    if (M > 0 && !a_scales) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL a_scales", fn);
+    if (a_scales && (reinterpret_cast<uintptr_t>(a_scales) & 3u)) return fail(W8A8_ERR_ALIGNMENT, "%s: a_scales must be 4-byte aligned", fn);
+    // The product's own checks, with the codes as A (a_scales per token).
+    s = scaled_mm_check(fn, out, ot, ldo, q, ldq, b, ldb, qt, M, N, K, a_scales, M, b_scales, n_b);
+    if (s != W8A8_OK) return s;
+    if (M == 0) return ok();
+    w8a8::GemmProblem p = make_problem(out, ot, ldo, q, ldq, b, ldb, qt, M, N, K, a_scales, M, b_scales, n_b);
+    return from_hip(w8a8::launch_quant_scaled_mm(p, xt, x, ldx, static_cast<uint8_t*>(q), ldq, a_scales, stream), fn);
+}
+
+const char* w8a8_quant_scaled_mm_kernel(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return "";
+    return w8a8::quant_scaled_mm_fused(M, K) ? "gemm_dynq_kernel" : "quant_rows_kernel+scaled_mm";
 }
 
 const char* w8a8_scaled_mm_kernel(int64_t M, int64_t N, int64_t K) {

@@ -94,6 +94,17 @@ __device__ __forceinline__ void store_out(const GemmArgs& p, int m, int n, T acc
     }
 }
 
+// store_out with the row's scale given in a register.
+template <int OT, typename T>
+__device__ __forceinline__ void store_scaled(const GemmArgs& p, int m, int n, T acc, float sa) {
+    const float sb = p.sb ? p.sb[p.sb_per_col ? n : 0] : 1.0f;
+    const float d = static_cast<float>(acc) * sa * sb;
+    const int64_t o = static_cast<int64_t>(m) * p.ldo + n;
+    if constexpr (OT == D_BF16) static_cast<uint16_t*>(p.out)[o] = to_bf16_bits(d);
+    else if constexpr (OT == D_FP16) static_cast<uint16_t*>(p.out)[o] = to_fp16_bits(d);
+    else static_cast<float*>(p.out)[o] = d;
+}
+
 // Block id -> (tile_m, tile_n). Consecutive logical tiles share an XCD, and
 // the walk goes down groups of 8 row-tiles before moving to the next column.
 __device__ __forceinline__ bool tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -498,6 +509,119 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// One-token decode with the activation quantised in place (M == 1): dynamic
+// per-token quantisation of x followed by the scaled product, in one kernel.
+// Every workgroup (4 waves, 16 output columns) quantises the whole row x
+// itself (a few KB, L2-resident once the first workgroups have read it) with
+// the per-token quantizer's arithmetic: the same maximum, scale and
+// correctly rounded division, so codes and scale are bit-identical to
+// w8a8_quant_per_token. The codes stay in LDS; workgroup 0 also writes them
+// and the scale to memory. Meanwhile the weight rows stream through LDS in
+// bursts of 16 rows x 4 KB (64 KB in flight per workgroup), requested before
+// the row is quantised; weight chunk c of row r sits at slot c ^ (r % 16).
+// ---------------------------------------------------------------------------
+constexpr int kDynqChunk = 4096;       // K bytes of weight per burst
+constexpr int kDynqMaxK = 15360;       // longest row quantised in LDS (two workgroups per CU)
+
+template <int XT, int QT, int OT>
+__global__ __launch_bounds__(256) void gemm_dynq_kernel(GemmArgs p, const void* __restrict__ x,
+                                                        uint8_t* __restrict__ q,
+                                                        float* __restrict__ x_scale) {
+    typedef typename AccOf<QT>::type Acc;
+    constexpr int CH = kDynqChunk;
+    constexpr int WL = 16 * CH / 4096;  // weight loads per wave per burst
+    constexpr int SW = CH / kBK / 4;    // slices per wave per burst
+    __shared__ __attribute__((aligned(1024))) uint8_t wbuf[16 * CH];
+    __shared__ __attribute__((aligned(16))) uint8_t arow[kDynqMaxK];
+    __shared__ float part[4];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n0 = blockIdx.x * 16;
+    const int K = p.K;
+    const int wrows = min(16, p.N - n0);
+    const int ldb = static_cast<int>(p.ldb);
+    const i32x4 rb = buffer_rsrc(p.b + static_cast<int64_t>(n0) * p.ldb,
+                                 static_cast<uint32_t>((wrows - 1) * ldb + K));
+    auto burst = [&](int kc) {
+#pragma unroll
+        for (int j = 0; j < WL; ++j) {
+            const int t = wave + 4 * j;
+            const int o = t * 1024 + 16 * lane;
+            const int r = o / CH, c = ((o % CH) >> 4) ^ (r & 15);
+            const int k = kc + 16 * c;
+            const int off = (r < wrows && k < K) ? r * ldb + k : kOutOfRange;
+            raw_buffer_load_lds(rb, (lds_u32p)(wbuf + t * 1024), 16, off, 0, 0, kNonTemporal);
+        }
+    };
+    if (K > 0) burst(0);
+
+    // The row's maximum |x|, then its codes (8 elements per thread and step).
+    float amax = 0.0f;
+    for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) {
+        float v[8];
+        load8<XT>(x, k, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
+    amax = wave_max(amax);
+    if (lane == 0) part[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    const float s = scale_from_absmax<QT>(amax);
+    const double rcp = 1.0 / static_cast<double>(s);
+    for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) {
+        float v[8];
+        load8<XT>(x, k, v);
+        const u32x2 c = quant8<QT>(v, rcp);
+        *reinterpret_cast<u32x2*>(arow + k) = c;
+        if (blockIdx.x == 0) *reinterpret_cast<u32x2*>(q + k) = c;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) *x_scale = s;
+
+    const int g = lane >> 4, r16 = lane & 15;
+    const u32x4 z = {0, 0, 0, 0};
+    Acc acc = Acc{0, 0, 0, 0};
+    for (int kc = 0; kc < K; kc += CH) {
+        if (kc > 0) {
+            __syncthreads();  // every wave is done with the previous burst
+            burst(kc);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // the burst (and, the first time, the codes) have landed
+        const uint8_t* wrow = wbuf + r16 * CH;
+#pragma unroll
+        for (int v = 0; v < SW; ++v) {
+            const int u = 4 * v + wave;
+            const int k = kc + u * kBK + 32 * g;  // this lane's 32 K bytes of the slice
+            if (kc + u * kBK >= K) break;
+            const int c0 = (8 * u + 2 * g) ^ r16, c1 = (8 * u + 2 * g + 1) ^ r16;
+            const i32x8 wf = join(*reinterpret_cast<const u32x4*>(wrow + 16 * c0),
+                                  *reinterpret_cast<const u32x4*>(wrow + 16 * c1));
+            // only MFMA row 0 carries the token; the other rows multiply zeros
+            const bool lo = r16 == 0 && k < K, hi = lo && k + 16 < K;
+            const i32x8 af = join(lo ? *reinterpret_cast<const u32x4*>(arow + k) : z,
+                                  hi ? *reinterpret_cast<const u32x4*>(arow + k + 16) : z);
+            mma<QT>(acc, af, wf);
+        }
+    }
+
+    // Add the four waves' sums in a fixed order; row 0 of column l % 16 is
+    // element 0 of lanes 0..15.
+    __syncthreads();
+    Acc* red = reinterpret_cast<Acc*>(wbuf);
+    red[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (wave == 0 && lane < 16) {
+        Acc t = red[lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) t += red[w * 64 + lane];
+        const int n = n0 + lane;
+        if (n < p.N) store_scaled<OT>(p, 0, n, t[0], s);
+    }
+}
+
 template <int QT, int OT, int BM, int BN, int WGM, int WGN>
 hipError_t run_tile(GemmArgs a, hipStream_t st) {
     a.tiles_m = (a.M + BM - 1) / BM;
@@ -594,6 +718,59 @@ hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st) {
     a.vec_out = (reinterpret_cast<uintptr_t>(p.out) % (4 * esz) == 0) && (p.ldo % 4 == 0);
     if (p.qt == Q_FP8) return dispatch_ot<Q_FP8>(p.ot, a, st);
     return dispatch_ot<Q_INT8>(p.ot, a, st);
+}
+
+bool quant_scaled_mm_fused(int64_t M, int64_t K) { return M == 1 && K <= kDynqMaxK; }
+
+hipError_t launch_quant_scaled_mm(const GemmProblem& p, int xt, const void* x, int64_t ldx,
+                                  uint8_t* q, int64_t ldq, float* a_scales, hipStream_t st) {
+    if (p.M == 0) return hipSuccess;
+    if (!quant_scaled_mm_fused(p.M, p.K) || p.N == 0) {
+        hipError_t e = launch_quant_per_token(xt, x, p.M, p.K, ldx, q, p.qt, ldq, a_scales, st);
+        if (e != hipSuccess) return e;
+        GemmProblem g = p;
+        g.a = q;
+        g.lda = ldq;
+        g.sa = a_scales;
+        g.sa_per_row = p.M != 1;
+        return launch_scaled_mm(g, st);
+    }
+    GemmArgs a;
+    a.out = p.out;
+    a.ldo = p.ldo;
+    a.a = q;
+    a.lda = ldq;
+    a.b = p.b;
+    a.ldb = p.ldb;
+    a.M = 1;
+    a.N = static_cast<int>(p.N);
+    a.K = static_cast<int>(p.K);
+    a.sa = a_scales;
+    a.sa_per_row = 0;
+    a.sb = p.sb;
+    a.sb_per_col = p.sb_per_col ? 1 : 0;
+    a.tiles_m = a.tiles_n = 0;
+    a.vec_out = 0;
+    const dim3 grid((p.N + 15) / 16), block(256);
+#define W8A8_DYNQ(XT_, QT_, OT_) \
+    hipLaunchKernelGGL((gemm_dynq_kernel<XT_, QT_, OT_>), grid, block, 0, st, a, x, q, a_scales)
+#define W8A8_DYNQ_OT(XT_, QT_)                             \
+    switch (p.ot) {                                         \
+        case D_BF16: W8A8_DYNQ(XT_, QT_, D_BF16); break;    \
+        case D_FP16: W8A8_DYNQ(XT_, QT_, D_FP16); break;    \
+        default: W8A8_DYNQ(XT_, QT_, D_F32); break;         \
+    }
+#define W8A8_DYNQ_QT(XT_)                                                    \
+    if (p.qt == Q_FP8) { W8A8_DYNQ_OT(XT_, Q_FP8) } else { W8A8_DYNQ_OT(XT_, Q_INT8) }
+    switch (xt) {
+        case D_BF16: W8A8_DYNQ_QT(D_BF16) break;
+        case D_FP16: W8A8_DYNQ_QT(D_FP16) break;
+        default: W8A8_DYNQ_QT(D_F32) break;
+    }
+#undef W8A8_DYNQ_QT
+#undef W8A8_DYNQ_OT
+#undef W8A8_DYNQ
+    return hipGetLastError();
 }
 
 const char* scaled_mm_kernel_name(int64_t M, int64_t N) {

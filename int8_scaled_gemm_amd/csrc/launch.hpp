@@ -35,6 +35,13 @@ struct GemmProblem {
 
 hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st);
 
+// Dynamic per-token quantisation of x [M, K] into q / a_scales, then the
+// scaled product with p's B and b scales (p.a, p.lda, p.sa are ignored).
+// M == 1 with K <= 16384 runs as one fused kernel.
+hipError_t launch_quant_scaled_mm(const GemmProblem& p, int xt, const void* x, int64_t ldx,
+                                  uint8_t* q, int64_t ldq, float* a_scales, hipStream_t st);
+bool quant_scaled_mm_fused(int64_t M, int64_t K);
+
 // Name of the kernel configuration a problem runs with.
 const char* scaled_mm_kernel_name(int64_t M, int64_t N);
 

@@ -131,3 +131,22 @@ def test_kernel_configuration_names(lib):
     assert name(2048, 4096, 4096) == "gemm_tile_kernel<256x128>"
     assert name(512, 4096, 4096) == "gemm_tile_kernel<64x64>"
     assert name(-1, 4, 4) == ""
+
+
+def test_quant_scaled_mm_validation(lib):
+    def f(out=FAKE, ot=0, ldo=64, x=FAKE, xt=0, ldx=128, b=FAKE, ldb=128, qt=1, M=1, N=64, K=128,
+          sb=None, n_b=1, q=FAKE, ldq=128, sa=FAKE):
+        return lib.w8a8_quant_scaled_mm(out, ot, ldo, x, xt, ldx, b, ldb, qt, M, N, K, sb, n_b, q,
+                                        ldq, sa, None)
+    assert f(ot=3, qt=0) == DTYPE          # the output is scaled: no raw accumulator
+    assert f(sa=None) == INVALID           # the per-token scales are an output
+    assert f(ldb=64) == LAYOUT             # B not column-major
+    assert f(xt=9) == DTYPE
+    assert f(ldx=100) == LAYOUT
+    assert f(sb=FAKE, n_b=7) == SHAPE
+    assert f(x=None) == INVALID
+    assert f(M=0, out=None, x=None, b=None, q=None, sa=None) == OK
+    name = lambda M, N, K: lib.w8a8_quant_scaled_mm_kernel(M, N, K).decode()
+    assert name(1, 4096, 14336) == "gemm_dynq_kernel"
+    assert name(1, 4096, 15376) == "quant_rows_kernel+scaled_mm"
+    assert name(2, 4096, 4096) == "quant_rows_kernel+scaled_mm"
