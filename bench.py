@@ -87,12 +87,16 @@ def _gemm_bytes(M, N, K, n_sa, n_sb, out_bytes=2):
 def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
     launches, keep = [], []
     code_dtype = torch.float8_e4m3fn if qtype == "fp8" else torch.int8
+    # one workspace for the step's split-K problems (they run one after another)
+    ws_bytes = max(w8.w8a8_scaled_mm_workspace_size(M, N, K) for M in Ms for _, N, K in layers)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    keep.append(ws)
     seed = 1000
     for M in Ms:
         for name, N, K in layers:
             seed += 1
             w = workloads.weights(N, K, seed=seed, device=dev)
-            wq, ws = w8.w8a8_quant_per_token(w, qtype)   # offline: per-channel weights
+            wq, wsc = w8.w8a8_quant_per_token(w, qtype)   # offline: per-channel weights
             del w
             x = workloads.activations(M, K, seed=seed + 500, device=dev)
             q = torch.empty((M, K), dtype=code_dtype, device=dev)
@@ -110,13 +114,13 @@ def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
                 qf = (lambda x=x, q=q, s=s: w8.w8a8_quant_per_tensor(x, qtype, scale=s, q=q))
                 n_sa = 1
                 qbytes = 3 * M * K + 4
-            mf = (lambda q=q, wq=wq, s=s, ws=ws, out=out:
-                  w8.w8a8_scaled_mm(q, wq.t(), s, ws, torch.bfloat16, out=out))
+            mf = (lambda q=q, wq=wq, s=s, wsc=wsc, out=out:
+                  w8.w8a8_scaled_mm(q, wq.t(), s, wsc, torch.bfloat16, out=out, workspace=ws))
             fused = (act_scheme == "per_token"
                      and w8.w8a8_quant_scaled_mm_kernel(M, N, K) == "gemm_dynq_kernel")
             if fused:  # one kernel quantises the token and runs the product
-                ff = (lambda x=x, wq=wq, ws=ws, out=out, q=q, s=s:
-                      w8.w8a8_quant_scaled_mm(x, wq.t(), ws, qtype, torch.bfloat16, out=out,
+                ff = (lambda x=x, wq=wq, wsc=wsc, out=out, q=q, s=s:
+                      w8.w8a8_quant_scaled_mm(x, wq.t(), wsc, qtype, torch.bfloat16, out=out,
                                               q=q, a_scales=s))
                 launches.append(Launch("gemm", ff, 2 * M * N * K,
                                        _gemm_bytes(M, N, K, n_sa, N) + qbytes - M * K,
@@ -126,8 +130,8 @@ def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
                 launches.append(Launch("quant", qf, 0, qbytes, f"quant M={M} {name}", qkern))
                 launches.append(Launch("gemm", mf, 2 * M * N * K, _gemm_bytes(M, N, K, n_sa, N),
                                        f"gemm M={M} {name} {N}x{K}",
-                                       w8.w8a8_scaled_mm_kernel(M, N, K)))
-            keep += [wq, ws, x, q, s, out]
+                                       w8.w8a8_scaled_mm_kernel(M, N, K, workspace=True)))
+            keep += [wq, wsc, x, q, s, out]
     return launches, keep
 
 

@@ -129,6 +129,31 @@ w8a8_status w8a8_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* a,
                            int64_t n_b, hipStream_t stream);
 
 /*
+ * Bytes of device workspace with which w8a8_scaled_mm_ws splits K for an
+ * M x N x K problem (0: it would not split, and needs none). Host-only.
+ * Splitting pays for decode problems with 16 < M <= 64, K >= 8192 and
+ * N < 16321: 4 splits of fp32 (int32 for int8) partial sums, 16*M*N bytes.
+ */
+int64_t w8a8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/*
+ * w8a8_scaled_mm with an optional caller workspace [P1: the same operation].
+ * When workspace_bytes >= w8a8_scaled_mm_workspace_size(M, N, K) > 0, four
+ * workgroups share each 64-column tile along K, write their partial sums to
+ * the workspace, and a second kernel adds them in a fixed split order and
+ * applies the scales: results are deterministic, and equal to
+ * w8a8_scaled_mm's up to the fp8 summation order (bit-identical for int8).
+ * Otherwise this is w8a8_scaled_mm. The workspace needs no initialisation
+ * and holds nothing between calls; calls that share one must not overlap.
+ * workspace: device memory, 256-byte aligned (may be NULL with 0 bytes).
+ */
+w8a8_status w8a8_scaled_mm_ws(void* out, w8a8_dtype ot, int64_t ldo, const void* a, int64_t lda,
+                              const void* b, int64_t ldb, w8a8_qtype qt, int64_t M, int64_t N,
+                              int64_t K, const float* a_scales, int64_t n_a, const float* b_scales,
+                              int64_t n_b, void* workspace, int64_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
  * Dynamic per-token quantisation followed by the scaled matrix multiply, the
  * decode step of a w8a8 linear layer [P1 bullet list: per-token activation
  * scales with per-channel weight scales; P2: dynamic activation scales]:
@@ -139,8 +164,9 @@ w8a8_status w8a8_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* a,
  * (device, written: the caller can reuse them), B and b_scales as in
  * w8a8_scaled_mm, out of type BF16/FP16/F32 (I32 is refused). Results are
  * identical to the two calls (codes and scales bit for bit, out up to the
- * fp8 accumulation order). M == 1 with K <= 15360 runs as one kernel that
- * quantises the row in every workgroup; other sizes run the two kernels.
+ * fp8 accumulation order). M == 1 with K <= 15360 and N < 16321 runs as one
+ * kernel that quantises the row in every workgroup; other sizes run the two
+ * kernels (w8a8_quant_scaled_mm_kernel names which).
  */
 w8a8_status w8a8_quant_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* x,
                                  w8a8_dtype xt, int64_t ldx, const void* b, int64_t ldb,
@@ -177,6 +203,9 @@ w8a8_status kv_fp8_scaled_dequant(const uint8_t* q, int64_t n, const float* scal
  * that profiles can be matched to calls. Host-only.
  */
 const char* w8a8_scaled_mm_kernel(int64_t M, int64_t N, int64_t K);
+
+/* The same for w8a8_scaled_mm_ws given enough workspace. */
+const char* w8a8_scaled_mm_ws_kernel(int64_t M, int64_t N, int64_t K);
 
 /*
  * The same for w8a8_quant_scaled_mm: "gemm_dynq_kernel" for the fused

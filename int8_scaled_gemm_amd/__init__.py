@@ -51,6 +51,8 @@ SIGNATURES = {
     "w8a8_quant_per_tensor": [_P, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _I, _P],
     "w8a8_scaled_mm": [_P, _I, _I64, _P, _I64, _P, _I64, _I, _I64, _I64, _I64, _P, _I64, _P,
                        _I64, _P],
+    "w8a8_scaled_mm_ws": [_P, _I, _I64, _P, _I64, _P, _I64, _I, _I64, _I64, _I64, _P, _I64, _P,
+                          _I64, _P, _I64, _P],
     "w8a8_quant_scaled_mm": [_P, _I, _I64, _P, _I, _I64, _P, _I64, _I, _I64, _I64, _I64, _P, _I64,
                              _P, _I64, _P, _P],
     "kv_fp8_scaled_quant": [_P, _I, _I64, _P, _P, _I, _P],
@@ -93,6 +95,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.w8a8_scaled_mm_kernel.restype = ctypes.c_char_p
     lib.w8a8_quant_scaled_mm_kernel.argtypes = [_I64, _I64, _I64]
     lib.w8a8_quant_scaled_mm_kernel.restype = ctypes.c_char_p
+    lib.w8a8_scaled_mm_ws_kernel.argtypes = [_I64, _I64, _I64]
+    lib.w8a8_scaled_mm_ws_kernel.restype = ctypes.c_char_p
+    lib.w8a8_scaled_mm_workspace_size.argtypes = [_I64, _I64, _I64]
+    lib.w8a8_scaled_mm_workspace_size.restype = ctypes.c_int64
     _lib = lib
     return lib
 
@@ -207,9 +213,15 @@ def kv_fp8_scaled_dequant(q: torch.Tensor, scale: torch.Tensor | None,
 
 
 # ---------------------------------------------------------------------- GEMM
+def w8a8_scaled_mm_workspace_size(M: int, N: int, K: int) -> int:
+    """Bytes of workspace with which w8a8_scaled_mm_ws splits K (0: none)."""
+    return int(load_library().w8a8_scaled_mm_workspace_size(M, N, K))
+
+
 def w8a8_scaled_mm(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | None,
                    b_scales: torch.Tensor | None, out_dtype=torch.bfloat16,
-                   out: torch.Tensor | None = None) -> torch.Tensor:
+                   out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
     """D = a_scales (x) b_scales * (a @ b).
 
     a: codes [M, K] with unit column stride. b: codes K x N, COLUMN-major
@@ -217,6 +229,9 @@ def w8a8_scaled_mm(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | No
     a_scales: fp32 [1] or [M] (or [M, 1]); b_scales: fp32 [1] or [N] (or [1, N]).
     None means 1.0. out_dtype: bfloat16, float16, float32, or int32 (the raw
     int8 accumulator, scales must be None).
+    workspace: optional uint8 device tensor; with at least
+    w8a8_scaled_mm_workspace_size(M, N, K) bytes the call goes through
+    w8a8_scaled_mm_ws and may split K.
     """
     _check_cuda(a, b, a_scales, b_scales, out)
     qt = _qtype(a.dtype)
@@ -240,7 +255,12 @@ def w8a8_scaled_mm(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | No
     args = (_ptr(out), _dtype(out.dtype), ldo, _ptr(a), lda, _ptr(b), ldb, qt, M, N, K,
             _ptr(sa), 0 if sa is None else sa.numel(), _ptr(sb),
             0 if sb is None else sb.numel())
-    _call("w8a8_scaled_mm", *args, _stream(a))
+    if workspace is None:
+        _call("w8a8_scaled_mm", *args, _stream(a))
+    else:
+        _check_cuda(workspace)
+        _call("w8a8_scaled_mm_ws", *args, _ptr(workspace),
+              workspace.numel() * workspace.element_size(), _stream(a))
     return out
 
 
@@ -295,9 +315,12 @@ def scaled_mm(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor | None,
     return w8a8_scaled_mm(a, b, scale_a, scale_b, out_dtype, out)
 
 
-def w8a8_scaled_mm_kernel(M: int, N: int, K: int) -> str:
-    """Kernel configuration the library runs for an M x N x K problem."""
-    return load_library().w8a8_scaled_mm_kernel(M, N, K).decode()
+def w8a8_scaled_mm_kernel(M: int, N: int, K: int, workspace: bool = False) -> str:
+    """Kernel configuration the library runs for an M x N x K problem
+    (w8a8_scaled_mm, or w8a8_scaled_mm_ws with enough workspace)."""
+    lib = load_library()
+    f = lib.w8a8_scaled_mm_ws_kernel if workspace else lib.w8a8_scaled_mm_kernel
+    return f(M, N, K).decode()
 
 
 def version() -> str:
@@ -305,6 +328,6 @@ def version() -> str:
 
 
 __all__ = ["w8a8_quant_per_token", "w8a8_quant_per_tensor", "w8a8_scaled_mm",
-           "w8a8_scaled_mm_kernel", "w8a8_quant_scaled_mm", "w8a8_quant_scaled_mm_kernel",
+           "w8a8_scaled_mm_kernel", "w8a8_scaled_mm_workspace_size", "w8a8_quant_scaled_mm", "w8a8_quant_scaled_mm_kernel",
            "kv_fp8_scaled_quant", "kv_fp8_scaled_dequant", "scaled_mm", "W8A8Error",
            "load_library", "version", "LIB_PATH", "SIGNATURES"]

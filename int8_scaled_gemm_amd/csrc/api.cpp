@@ -217,12 +217,41 @@ w8a8_status w8a8_quant_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const vo
 
 const char* w8a8_quant_scaled_mm_kernel(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0) return "";
-    return w8a8::quant_scaled_mm_fused(M, K) ? "gemm_dynq_kernel" : "quant_rows_kernel+scaled_mm";
+    return w8a8::quant_scaled_mm_fused(M, N, K) ? "gemm_dynq_kernel" : "quant_rows_kernel+scaled_mm";
 }
 
 const char* w8a8_scaled_mm_kernel(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0) return "";
-    return w8a8::scaled_mm_kernel_name(M, N);
+    return w8a8::scaled_mm_kernel_name(M, N, K, false);
+}
+
+const char* w8a8_scaled_mm_ws_kernel(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return "";
+    return w8a8::scaled_mm_kernel_name(M, N, K, true);
+}
+
+int64_t w8a8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return 0;
+    return w8a8::plan_splitk(M, N, K).workspace_bytes;
+}
+
+w8a8_status w8a8_scaled_mm_ws(void* out, w8a8_dtype ot, int64_t ldo, const void* a, int64_t lda,
+                              const void* b, int64_t ldb, w8a8_qtype qt, int64_t M, int64_t N,
+                              int64_t K, const float* a_scales, int64_t n_a, const float* b_scales,
+                              int64_t n_b, void* workspace, int64_t workspace_bytes,
+                              hipStream_t stream) {
+    const char* fn = "w8a8_scaled_mm_ws";
+    if (workspace_bytes < 0) return fail(W8A8_ERR_INVALID_ARG, "%s: negative workspace_bytes", fn);
+    if (workspace_bytes > 0 && !workspace) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL workspace of %lld bytes", fn, (long long)workspace_bytes);
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return fail(W8A8_ERR_ALIGNMENT, "%s: workspace must be 256-byte aligned", fn);
+    w8a8_status s = scaled_mm_check(fn, out, ot, ldo, a, lda, b, ldb, qt, M, N, K, a_scales, n_a,
+                                    b_scales, n_b);
+    if (s != W8A8_OK || M == 0 || N == 0) return s;
+    w8a8::GemmProblem p = make_problem(out, ot, ldo, a, lda, b, ldb, qt, M, N, K, a_scales, n_a,
+                                       b_scales, n_b);
+    p.workspace = workspace;
+    p.workspace_bytes = workspace_bytes;
+    return from_hip(w8a8::launch_scaled_mm(p, stream), fn);
 }
 
 w8a8_status kv_fp8_scaled_quant(const void* x, w8a8_dtype xt, int64_t n, uint8_t* q, float* scale,

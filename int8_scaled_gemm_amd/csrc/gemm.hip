@@ -41,6 +41,11 @@ struct GemmArgs {
     int sb_per_col;
     int tiles_m, tiles_n;
     int vec_out;  // out and ldo allow 4-element vector stores
+    // split-K decode: splits > 1 workgroups per 64-column tile, each over
+    // stages_per_split K stages, writing fp32 (int32 for int8) partial sums
+    // [splits][M][N] to part; a second kernel adds them
+    void* part;
+    int splits, stages_per_split;
 };
 
 template <int QT>
@@ -411,8 +416,14 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n0 = blockIdx.x * CB;
-    const int nst = (p.K + CH - 1) / CH;
+    const int S = (CB == 64 && p.splits > 1) ? p.splits : 1;
+    const int sp = blockIdx.x % S;
+    const int n0 = (blockIdx.x / S) * CB;
+    const int nst_all = (p.K + CH - 1) / CH;
+    const int s0 = S > 1 ? sp * p.stages_per_split : 0;  // this workgroup's K stages
+    const int s1 = S > 1 ? min(nst_all, s0 + p.stages_per_split) : nst_all;
+    const int nst = max(s1 - s0, 0);
+    const int kend = min(p.K, s1 * CH);
     const int mt = (p.M + 15) / 16;
     const int wrows = min(CB, p.N - n0);
     const int lda = static_cast<int>(p.lda), ldb = static_cast<int>(p.ldb);
@@ -421,7 +432,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
     const i32x4 ra = buffer_rsrc(p.a, static_cast<uint32_t>((p.M - 1) * lda + p.K));
 
     auto issue = [&](int st, int buf) {
-        const int k0 = st * CH;
+        const int k0 = (s0 + st) * CH;
         uint8_t* base = smem + buf * STAGE;
 #pragma unroll
         for (int j = 0; j < WL + AL; ++j) {
@@ -430,7 +441,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
             const int o = t * 1024 + 16 * lane;
             const int r = o / CH, c = ((o % CH) >> 4) ^ (r & 15);
             const int k = k0 + 16 * c;
-            const bool ok = r < (is_w ? wrows : p.M) && k < p.K;
+            const bool ok = r < (is_w ? wrows : p.M) && k < kend;
             const int off = ok ? r * (is_w ? ldb : lda) + k : kOutOfRange;
             raw_buffer_load_lds(is_w ? rb : ra, (lds_u32p)(base + (is_w ? 0 : CB * CH) + t * 1024),
                                 16, off, 0, 0, is_w ? kNonTemporal : 0);
@@ -479,6 +490,8 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
 
     // In a 16 x 16 tile lane l holds rows 4 (l / 16) + r, r < 4, of column l % 16.
     if constexpr (CB == 64) {
+        typedef typename std::conditional<QT == Q_FP8, float, int32_t>::type Part;
+        Part* part = static_cast<Part*>(p.part) + static_cast<int64_t>(sp) * p.M * p.N;
         const int n = n0 + 16 * wave + r16;
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
@@ -486,7 +499,10 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = 16 * i + 4 * g + r;
-                if (m < p.M && n < p.N) store_out<OT>(p, m, n, acc[i][r]);
+                if (m < p.M && n < p.N) {
+                    if (S > 1) part[static_cast<int64_t>(m) * p.N + n] = static_cast<Part>(acc[i][r]);
+                    else store_out<OT>(p, m, n, acc[i][r]);
+                }
             }
         }
     } else {
@@ -517,11 +533,13 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
 // the per-token quantizer's arithmetic: the same maximum, scale and
 // correctly rounded division, so codes and scale are bit-identical to
 // w8a8_quant_per_token. The codes stay in LDS; workgroup 0 also writes them
-// and the scale to memory. Meanwhile the weight rows stream through LDS in
-// bursts of 16 rows x 4 KB (64 KB in flight per workgroup), requested before
-// the row is quantised; weight chunk c of row r sits at slot c ^ (r % 16).
+// and the scale to memory at the end. The weight rows stream through a
+// 2-slot LDS ring in chunks of 16 rows x 2 KB, two chunks in flight. The row
+// x is requested before the weights: loads retire in issue order, so the
+// quantisation then waits only for x. Weight chunk c of row r sits at slot
+// c ^ (r % 16).
 // ---------------------------------------------------------------------------
-constexpr int kDynqChunk = 4096;       // K bytes of weight per burst
+constexpr int kDynqChunk = 2048;       // K bytes of weight per chunk
 constexpr int kDynqMaxK = 15360;       // longest row quantised in LDS (two workgroups per CU)
 
 template <int XT, int QT, int OT>
@@ -530,9 +548,10 @@ __global__ __launch_bounds__(256) void gemm_dynq_kernel(GemmArgs p, const void* 
                                                         float* __restrict__ x_scale) {
     typedef typename AccOf<QT>::type Acc;
     constexpr int CH = kDynqChunk;
-    constexpr int WL = 16 * CH / 4096;  // weight loads per wave per burst
-    constexpr int SW = CH / kBK / 4;    // slices per wave per burst
-    __shared__ __attribute__((aligned(1024))) uint8_t wbuf[16 * CH];
+    constexpr int WL = 16 * CH / 4096;  // weight loads per wave per chunk
+    constexpr int SW = CH / kBK / 4;    // slices per wave per chunk
+    constexpr int kGroups = (kDynqMaxK + 2047) / 2048;  // 8-element groups of x per thread
+    __shared__ __attribute__((aligned(1024))) uint8_t wbuf[2][16 * CH];
     __shared__ __attribute__((aligned(16))) uint8_t arow[kDynqMaxK];
     __shared__ float part[4];
 
@@ -540,11 +559,13 @@ __global__ __launch_bounds__(256) void gemm_dynq_kernel(GemmArgs p, const void* 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n0 = blockIdx.x * 16;
     const int K = p.K;
+    const int nch = (K + CH - 1) / CH;
     const int wrows = min(16, p.N - n0);
     const int ldb = static_cast<int>(p.ldb);
     const i32x4 rb = buffer_rsrc(p.b + static_cast<int64_t>(n0) * p.ldb,
                                  static_cast<uint32_t>((wrows - 1) * ldb + K));
-    auto burst = [&](int kc) {
+    auto chunk = [&](int ci, int buf) {
+        const int kc = ci * CH;
 #pragma unroll
         for (int j = 0; j < WL; ++j) {
             const int t = wave + 4 * j;
@@ -552,48 +573,53 @@ __global__ __launch_bounds__(256) void gemm_dynq_kernel(GemmArgs p, const void* 
             const int r = o / CH, c = ((o % CH) >> 4) ^ (r & 15);
             const int k = kc + 16 * c;
             const int off = (r < wrows && k < K) ? r * ldb + k : kOutOfRange;
-            raw_buffer_load_lds(rb, (lds_u32p)(wbuf + t * 1024), 16, off, 0, 0, kNonTemporal);
+            raw_buffer_load_lds(rb, (lds_u32p)(wbuf[buf] + t * 1024), 16, off, 0, 0, kNonTemporal);
         }
     };
-    if (K > 0) burst(0);
 
-    // The row's maximum |x|, then its codes (8 elements per thread and step).
-    float amax = 0.0f;
-    for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) {
-        float v[8];
-        load8<XT>(x, k, v);
+    // x first, then the first two weight chunks.
+    float v[kGroups][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    for (int j = 0; j < kGroups; ++j) {
+        const int k = 8 * threadIdx.x + 2048 * j;
+        if (k < K) load8<XT>(x, k, v[j]);
     }
+    asm volatile("" ::: "memory");
+    if (nch > 0) chunk(0, 0);
+    if (nch > 1) chunk(1, 1);
+
+    // The row's maximum |x|, its scale and its codes (into LDS).
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j)
+        if (8 * static_cast<int>(threadIdx.x) + 2048 * j < K)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
     amax = wave_max(amax);
     if (lane == 0) part[wave] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
     const float s = scale_from_absmax<QT>(amax);
     const double rcp = 1.0 / static_cast<double>(s);
-    for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) {
-        float v[8];
-        load8<XT>(x, k, v);
-        const u32x2 c = quant8<QT>(v, rcp);
-        *reinterpret_cast<u32x2*>(arow + k) = c;
-        if (blockIdx.x == 0) *reinterpret_cast<u32x2*>(q + k) = c;
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j) {
+        const int k = 8 * threadIdx.x + 2048 * j;
+        if (k < K) *reinterpret_cast<u32x2*>(arow + k) = quant8<QT>(v[j], rcp);
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) *x_scale = s;
 
     const int g = lane >> 4, r16 = lane & 15;
     const u32x4 z = {0, 0, 0, 0};
     Acc acc = Acc{0, 0, 0, 0};
-    for (int kc = 0; kc < K; kc += CH) {
-        if (kc > 0) {
-            __syncthreads();  // every wave is done with the previous burst
-            burst(kc);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();  // the burst (and, the first time, the codes) have landed
-        const uint8_t* wrow = wbuf + r16 * CH;
+    for (int ci = 0; ci < nch; ++ci) {
+        // chunk ci has landed once at most the next chunk's loads are pending
+        if (ci + 1 < nch) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WL) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // every wave's share of chunk ci (and the codes) is in LDS
+        const int kc = ci * CH;
+        const uint8_t* wrow = wbuf[ci & 1] + r16 * CH;
 #pragma unroll
-        for (int v = 0; v < SW; ++v) {
-            const int u = 4 * v + wave;
+        for (int sv = 0; sv < SW; ++sv) {
+            const int u = 4 * sv + wave;
             const int k = kc + u * kBK + 32 * g;  // this lane's 32 K bytes of the slice
             if (kc + u * kBK >= K) break;
             const int c0 = (8 * u + 2 * g) ^ r16, c1 = (8 * u + 2 * g + 1) ^ r16;
@@ -605,12 +631,13 @@ __global__ __launch_bounds__(256) void gemm_dynq_kernel(GemmArgs p, const void* 
                                   hi ? *reinterpret_cast<const u32x4*>(arow + k + 16) : z);
             mma<QT>(acc, af, wf);
         }
+        __syncthreads();  // every wave is done with slot ci & 1
+        if (ci + 2 < nch) chunk(ci + 2, ci & 1);
     }
 
     // Add the four waves' sums in a fixed order; row 0 of column l % 16 is
     // element 0 of lanes 0..15.
-    __syncthreads();
-    Acc* red = reinterpret_cast<Acc*>(wbuf);
+    Acc* red = reinterpret_cast<Acc*>(wbuf[0]);
     red[wave * 64 + lane] = acc;
     __syncthreads();
     if (wave == 0 && lane < 16) {
@@ -619,6 +646,29 @@ __global__ __launch_bounds__(256) void gemm_dynq_kernel(GemmArgs p, const void* 
         for (int w = 1; w < 4; ++w) t += red[w * 64 + lane];
         const int n = n0 + lane;
         if (n < p.N) store_scaled<OT>(p, 0, n, t[0], s);
+    }
+    if (blockIdx.x == 0) {  // the codes and the scale, for the caller
+        for (int k = 16 * threadIdx.x; k < K; k += 16 * 256)
+            *reinterpret_cast<u32x4*>(q + k) = *reinterpret_cast<const u32x4*>(arow + k);
+        if (threadIdx.x == 0) *x_scale = s;
+    }
+}
+
+// Split-K epilogue: D = scales * (sum of the splits' partial sums, added in
+// split order), 4 elements per thread.
+template <int QT, int OT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
+    typedef typename std::conditional<QT == Q_FP8, float, int32_t>::type Part;
+    const Part* part = static_cast<const Part*>(p.part);
+    const int64_t plane = static_cast<int64_t>(p.M) * p.N;
+    const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int64_t e = e0 + r;
+        if (e >= plane) break;
+        Part sum = part[e];
+        for (int q = 1; q < p.splits; ++q) sum += part[q * plane + e];
+        store_out<OT>(p, static_cast<int>(e / p.N), static_cast<int>(e % p.N), sum);
     }
 }
 
@@ -635,8 +685,14 @@ hipError_t run_tile(GemmArgs a, hipStream_t st) {
 
 template <int QT, int OT, int CB, int MT, int CH, int ST>
 hipError_t run_decode(const GemmArgs& a, hipStream_t st) {
-    const int grid = (a.N + CB - 1) / CB;
+    const int S = (CB == 64 && a.splits > 1) ? a.splits : 1;
+    const int grid = (a.N + CB - 1) / CB * S;
     hipLaunchKernelGGL((gemm_decode_kernel<QT, OT, CB, MT, CH, ST>), dim3(grid), dim3(256), 0, st, a);
+    if (S > 1) {
+        const int64_t elems = static_cast<int64_t>(a.M) * a.N;
+        hipLaunchKernelGGL((splitk_reduce_kernel<QT, OT>), dim3(static_cast<int>((elems + 1023) / 1024)),
+                           dim3(256), 0, st, a);
+    }
     return hipGetLastError();
 }
 
@@ -671,6 +727,7 @@ Config select_config(int64_t M, int64_t N) {
 
 template <int QT, int OT>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
+    if (a.splits > 1) return run_decode<QT, OT, 64, 4, 256, 2>(a, st);
     switch (select_config(a.M, a.N)) {
         case kDecode64x16: return run_decode<QT, OT, 64, 1, 512, 2>(a, st);
         case kDecode64x64: return run_decode<QT, OT, 64, 4, 256, 2>(a, st);
@@ -697,6 +754,22 @@ hipError_t dispatch_ot(int ot, const GemmArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// Split-K for decode problems above 16 rows with a long K on weights too
+// narrow for 64-column blocks to occupy the GPU: 4 splits of the 64-column
+// kernel, so that each activation tile is read once per 64 columns instead
+// of once per 16 (measured on MI355X: Llama-3-8B down, 64 x 4096 x 14336,
+// from 29 to 20 us). Shorter K does not repay the extra pass.
+SplitPlan plan_splitk(int64_t M, int64_t N, int64_t K) {
+    SplitPlan d{1, 0, 0};
+    if (M <= 16 || M > 64 || K < 8192 || (N + 63) / 64 >= 256) return d;
+    constexpr int kStageBytes = 256;  // the 64-column kernel's K stage
+    const int64_t stages = (K + kStageBytes - 1) / kStageBytes;
+    d.splits = 4;
+    d.stages_per_split = static_cast<int>((stages + d.splits - 1) / d.splits);
+    d.workspace_bytes = static_cast<int64_t>(d.splits) * M * N * 4;
+    return d;
+}
+
 hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     GemmArgs a;
@@ -716,16 +789,33 @@ hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st) {
     a.tiles_m = a.tiles_n = 0;
     const int esz = (p.ot == D_BF16 || p.ot == D_FP16) ? 2 : 4;
     a.vec_out = (reinterpret_cast<uintptr_t>(p.out) % (4 * esz) == 0) && (p.ldo % 4 == 0);
+    a.part = nullptr;
+    a.splits = 1;
+    a.stages_per_split = 0;
+    if (p.workspace) {
+        const SplitPlan d = plan_splitk(p.M, p.N, p.K);
+        if (d.splits > 1 && p.workspace_bytes >= d.workspace_bytes) {
+            a.part = p.workspace;
+            a.splits = d.splits;
+            a.stages_per_split = d.stages_per_split;
+        }
+    }
     if (p.qt == Q_FP8) return dispatch_ot<Q_FP8>(p.ot, a, st);
     return dispatch_ot<Q_INT8>(p.ot, a, st);
 }
 
-bool quant_scaled_mm_fused(int64_t M, int64_t K) { return M == 1 && K <= kDynqMaxK; }
+// Measured on MI355X (Llama-3-8B decode shapes): the fused kernel saves the
+// quantizer launch on weights up to 16384 rows; on wider ones (gate_up,
+// 28672) the per-workgroup quantisation over N / 16 workgroups costs more
+// than the launch, and the 64-column decode kernel is faster.
+bool quant_scaled_mm_fused(int64_t M, int64_t N, int64_t K) {
+    return M == 1 && K <= kDynqMaxK && (N + 63) / 64 < 256;
+}
 
 hipError_t launch_quant_scaled_mm(const GemmProblem& p, int xt, const void* x, int64_t ldx,
                                   uint8_t* q, int64_t ldq, float* a_scales, hipStream_t st) {
     if (p.M == 0) return hipSuccess;
-    if (!quant_scaled_mm_fused(p.M, p.K) || p.N == 0) {
+    if (!quant_scaled_mm_fused(p.M, p.N, p.K) || p.N == 0) {
         hipError_t e = launch_quant_per_token(xt, x, p.M, p.K, ldx, q, p.qt, ldq, a_scales, st);
         if (e != hipSuccess) return e;
         GemmProblem g = p;
@@ -751,6 +841,9 @@ hipError_t launch_quant_scaled_mm(const GemmProblem& p, int xt, const void* x, i
     a.sb_per_col = p.sb_per_col ? 1 : 0;
     a.tiles_m = a.tiles_n = 0;
     a.vec_out = 0;
+    a.part = nullptr;
+    a.splits = 1;
+    a.stages_per_split = 0;
     const dim3 grid((p.N + 15) / 16), block(256);
 #define W8A8_DYNQ(XT_, QT_, OT_) \
     hipLaunchKernelGGL((gemm_dynq_kernel<XT_, QT_, OT_>), grid, block, 0, st, a, x, q, a_scales)
@@ -773,7 +866,8 @@ hipError_t launch_quant_scaled_mm(const GemmProblem& p, int xt, const void* x, i
     return hipGetLastError();
 }
 
-const char* scaled_mm_kernel_name(int64_t M, int64_t N) {
+const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K, bool workspace) {
+    if (workspace && plan_splitk(M, N, K).splits > 1) return "gemm_decode_kernel<64x64>+splitk_reduce_kernel";
     switch (select_config(M, N)) {
         case kDecode64x16: return "gemm_decode_kernel<64x16>";
         case kDecode64x64: return "gemm_decode_kernel<64x64>";

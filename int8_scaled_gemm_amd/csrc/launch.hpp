@@ -31,18 +31,28 @@ struct GemmProblem {
     bool sa_per_row;
     const float* sb;  // NULL: 1.0
     bool sb_per_col;
+    void* workspace = nullptr;    // optional: room for split-K partial sums
+    int64_t workspace_bytes = 0;
 };
+
+// How a decode problem splits K when given a workspace (splits == 1: no split).
+struct SplitPlan {
+    int splits;
+    int stages_per_split;
+    int64_t workspace_bytes;
+};
+SplitPlan plan_splitk(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st);
 
 // Dynamic per-token quantisation of x [M, K] into q / a_scales, then the
 // scaled product with p's B and b scales (p.a, p.lda, p.sa are ignored).
-// M == 1 with K <= 16384 runs as one fused kernel.
+// Problems with quant_scaled_mm_fused() run as one fused kernel.
 hipError_t launch_quant_scaled_mm(const GemmProblem& p, int xt, const void* x, int64_t ldx,
                                   uint8_t* q, int64_t ldq, float* a_scales, hipStream_t st);
-bool quant_scaled_mm_fused(int64_t M, int64_t K);
+bool quant_scaled_mm_fused(int64_t M, int64_t N, int64_t K);
 
 // Name of the kernel configuration a problem runs with.
-const char* scaled_mm_kernel_name(int64_t M, int64_t N);
+const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K, bool workspace);
 
 }  // namespace w8a8

@@ -263,3 +263,72 @@ def test_decode_configs_are_the_ones_named():
     names = {w8.w8a8_scaled_mm_kernel(M, N, K) for M, N, K in DECODE_SHAPES}
     assert names == {"gemm_decode_kernel<16x16>", "gemm_decode_kernel<16x64>",
                      "gemm_decode_kernel<64x16>", "gemm_decode_kernel<64x64>"}, names
+
+
+# Split-K through a caller workspace: decode problems above 16 rows with a
+# long K on narrow weights (the Llama-3-8B down projection at 64 tokens,
+# ragged N and K, the widest N that still splits).
+SPLITK_SHAPES = [(64, 4096, 14336), (40, 1000, 8192 + 16), (17, 300, 16384), (64, 16320, 8192),
+                 (33, 48, 9000 - 9000 % 16)]
+
+
+@pytest.mark.parametrize("qtype", ["fp8", "int8"])
+@pytest.mark.parametrize("M,N,K", SPLITK_SHAPES)
+def test_split_k_workspace_parity(qtype, M, N, K):
+    need = w8.w8a8_scaled_mm_workspace_size(M, N, K)
+    assert need > 0
+    assert w8.w8a8_scaled_mm_kernel(M, N, K, workspace=True).endswith("splitk_reduce_kernel")
+    a, sa, b, sb = _quantized(M, N, K, qtype, seed=5 * M + N + K)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    ad, bd = codes_to_dev(a, qtype), codes_to_dev(b, qtype)
+    sad = torch.from_numpy(np.asarray(sa, np.float32)).to(DEV)
+    sbd = torch.from_numpy(np.asarray(sb, np.float32)).to(DEV)
+    got = w8.w8a8_scaled_mm(ad, bd.t(), sad, sbd, torch.bfloat16, workspace=ws)
+    torch.cuda.synchronize()
+    info = check_scaled_mm(got, a, b, qtype, sa, sb, "bf16")
+    assert info["exact_frac"] > 0.9, info
+    if qtype == "int8":  # the split sums are exact: raw accumulators bit for bit
+        raw = w8.w8a8_scaled_mm(ad, bd.t(), None, None, torch.int32, workspace=ws)
+        torch.cuda.synchronize()
+        check_scaled_mm(raw, a, b, qtype, None, None, "i32")
+        plain = w8.w8a8_scaled_mm(ad, bd.t(), sad, sbd, torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(plain.view(torch.int16), got.view(torch.int16))
+
+
+def test_split_k_workspace_too_small_falls_back():
+    """A workspace below the size needed is not used: the plain kernel runs."""
+    M, N, K = 64, 4096, 14336
+    a, sa, b, sb = _quantized(M, N, K, "int8", seed=9)
+    need = w8.w8a8_scaled_mm_workspace_size(M, N, K)
+    ad, bd = codes_to_dev(a, "int8"), codes_to_dev(b, "int8")
+    small = torch.empty(need - 256, dtype=torch.uint8, device=DEV)
+    raw = w8.w8a8_scaled_mm(ad, bd.t(), None, None, torch.int32, workspace=small)
+    torch.cuda.synchronize()
+    check_scaled_mm(raw, a, b, "int8", None, None, "i32")
+
+
+def test_split_k_graph_replay():
+    """The two split-K kernels capture into a HIP graph; replays match eager."""
+    M, N, K = 64, 1024, 8192
+    a, sa, b, sb = _quantized(M, N, K, "fp8", seed=21)
+    ws = torch.empty(w8.w8a8_scaled_mm_workspace_size(M, N, K), dtype=torch.uint8, device=DEV)
+    ad, bd = codes_to_dev(a, "fp8"), codes_to_dev(b, "fp8")
+    sad = torch.from_numpy(sa).to(DEV)
+    sbd = torch.from_numpy(sb).to(DEV)
+    ref = w8.w8a8_scaled_mm(ad, bd.t(), sad, sbd, torch.bfloat16, workspace=ws)
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref)
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            w8.w8a8_scaled_mm(ad, bd.t(), sad, sbd, torch.bfloat16, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
