@@ -26,10 +26,10 @@ Weights are quantised once before timing (offline preparation). Every
 and the 256 MB last-level cache holds no weight from one use to the next.
 
 Prints one JSON line: the workload's throughput, a roofline entry for the
-kernel that takes the most time per step (the step's launches of that kernel
-captured alone and replayed, timed with HIP events on the launch stream), the
-same figures for every kernel, and the CPU oracle timed on a bounded sample of
-the same workload. The roofline's `traffic` is the HBM traffic per launch from
+scaled-product kernel (KV: the quant call) that takes the most time per step
+(the step's launches of that kernel captured alone and replayed, timed with HIP
+events on the launch stream), the same figures for every kernel, and the CPU
+oracle timed on a bounded sample of the same workload. The roofline's `traffic` is the HBM traffic per launch from
 the rocprofv3 FETCH_SIZE / WRITE_SIZE record under profiles/, when that record
 was taken from the current kernel sources (else null).
 
@@ -426,7 +426,13 @@ def main():
         kernels[name] = dict(launches=len(group), avg_s=avg_s,
                              nbytes=sum(L.nbytes for L in group) / len(group),
                              flops=sum(L.flops for L in group) / len(group))
-    dom = max(kernels, key=lambda k: kernels[k]["avg_s"] * kernels[k]["launches"])
+    # The roofline entry is for the scaled-product (or KV) kernel that takes the
+    # most time per step; the small per-token quantizations of decode batches
+    # are latency-bound (a few KB each) and are listed with their latency only.
+    kinds = {L.kernel: L.kind for L in launches}
+    main_kind = "kv_quant" if args.workload == "kv" else "gemm"
+    dom = max((k for k in kernels if kinds[k] == main_kind),
+              key=lambda k: kernels[k]["avg_s"] * kernels[k]["launches"])
     roof = roofline(dom, kernels[dom], spec, args.workload)
 
     if args.detail:

@@ -1,6 +1,7 @@
 """Parity at the workloads' full sizes, in the launch configuration bench.py
-times (graph-free here, same library calls), on sampled
-output rows the oracle computes one by one.
+times (graph-free here, same library calls: the fused one-token kernel and the
+split-K workspace where bench.py uses them), on sampled output rows the oracle
+computes one by one.
 
 Workloads: fp8 decode and prefill GEMMs at the Llama-3-8B layer shapes
 (QKV 6144x4096, O 4096x4096, gate_up 28672x4096, down 4096x14336), the
@@ -52,14 +53,23 @@ def _check_layer(M, N, K, qtype, act, seed):
     w, wq, ws, wq_h, ws_h = _weights_checked(N, K, qtype, seed)
     del w
     x = workloads.activations(M, K, seed=seed + 500, device=DEV)
-    if act == "per_token":
-        xq, xs = w8.w8a8_quant_per_token(x, qtype)
+    # the route bench.py times: the fused one-token kernel where the library
+    # fuses, else the quantizer and the product with a split-K workspace
+    ws_bytes = w8.w8a8_scaled_mm_workspace_size(M, N, K)
+    workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
+    if act == "per_token" and w8.w8a8_quant_scaled_mm_kernel(M, N, K) == "gemm_dynq_kernel":
+        xq = torch.empty((M, K), dtype=wq.dtype, device=DEV)
+        xs = torch.empty(M, dtype=torch.float32, device=DEV)
+        out = w8.w8a8_quant_scaled_mm(x, wq.t(), ws, qtype, torch.bfloat16, q=xq, a_scales=xs)
     else:
-        calib = workloads.activations(workloads.CALIBRATION_ROWS, K,
-                                      seed=workloads.CALIBRATION_SEED, device=DEV)
-        _, xs = w8.w8a8_quant_per_tensor(calib, qtype, dynamic=True)
-        xq, _ = w8.w8a8_quant_per_tensor(x, qtype, scale=xs)
-    out = w8.w8a8_scaled_mm(xq, wq.t(), xs, ws, torch.bfloat16)
+        if act == "per_token":
+            xq, xs = w8.w8a8_quant_per_token(x, qtype)
+        else:
+            calib = workloads.activations(workloads.CALIBRATION_ROWS, K,
+                                          seed=workloads.CALIBRATION_SEED, device=DEV)
+            _, xs = w8.w8a8_quant_per_tensor(calib, qtype, dynamic=True)
+            xq, _ = w8.w8a8_quant_per_tensor(x, qtype, scale=xs)
+        out = w8.w8a8_scaled_mm(xq, wq.t(), xs, ws, torch.bfloat16, workspace=workspace)
     torch.cuda.synchronize()
     rows = _sample_rows(M, seed + 1, 16 if M > 64 else M)
     # activation codes on the sampled rows against the oracle
