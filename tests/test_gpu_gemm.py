@@ -143,10 +143,12 @@ def test_tiny_int8_case_end_to_end():
     assert np.mean(bits(d) == d_ref) > 0.99
 
 
+@pytest.mark.parametrize("col0", [24, 23])
 @pytest.mark.parametrize("M", [7, 150])
-def test_submatrices_and_output_padding(M):
+def test_submatrices_and_output_padding(M, col0):
     """A and B as column windows of wider matrices (leading dimensions larger
-    than K), output into a window of a wider buffer: padding untouched."""
+    than K), output into a window of a wider buffer: padding untouched. An
+    odd first column leaves the output only 2-byte aligned (element stores)."""
     N, K = 96, 256
     qtype = "fp8"
     abig = workloads.random_codes((M, K + 64), qtype, seed=5).numpy()
@@ -158,13 +160,13 @@ def test_submatrices_and_output_padding(M):
     ad = codes_to_dev(abig, qtype)[:, 32:32 + K]
     bd = codes_to_dev(bbig, qtype)[4:4 + N, 16:16 + K]
     obig = torch.full((M, N + 40), 7.0, dtype=torch.bfloat16, device=DEV)
-    out = obig[:, 24:24 + N]
+    out = obig[:, col0:col0 + N]
     w8.w8a8_scaled_mm(ad, bd.t(), torch.from_numpy(sa).to(DEV), torch.from_numpy(sb).to(DEV),
                       torch.bfloat16, out=out)
     torch.cuda.synchronize()
     check_scaled_mm(out, a, b, qtype, sa, sb, "bf16")
     ob = obig.float().cpu().numpy()
-    assert (ob[:, :24] == 7.0).all() and (ob[:, 24 + N:] == 7.0).all()
+    assert (ob[:, :col0] == 7.0).all() and (ob[:, col0 + N:] == 7.0).all()
 
 
 def test_k_zero_writes_zeros_and_empty_is_noop():
