@@ -771,18 +771,31 @@ enum Config {
     kDecode64x64,    // gemm_decode_kernel, 64 columns, M <= 64 (stage 256 B, 2 stages)
     kDecode16x16,    // gemm_decode_kernel, 16 columns, M <= 16 (stage 1 KB, 2 stages)
     kDecode16x64,    // gemm_decode_kernel, 16 columns, M <= 64 (stage 512 B, 2 stages)
+    kDecode16x16L,   // gemm_decode_kernel, 16 columns, M <= 16, long K (stage 2 KB, 2 stages)
+    kDecode16x64L,   // gemm_decode_kernel, 16 columns, M <= 64, long K (stage 1 KB, 2 stages)
     kTile256x256,    // gemm_tile_kernel 256 x 256, 8 waves
     kTile256x128,    // gemm_tile_kernel 256 x 128, 8 waves
     kTile128x128,    // gemm_tile_kernel 128 x 128, 4 waves
     kTile64x64,      // gemm_tile_kernel 64 x 64, 4 waves
 };
 
-Config select_config(int64_t M, int64_t N) {
+// 16-column workgroups on a long K that fill at most one per CU: a stage
+// twice as long (the ring then fills a CU's LDS) keeps twice the bytes in
+// flight. Measured on MI355X at 4096 x 14336: 16 -> 14.8 us (16 rows) and
+// 28.8 -> 23.6 us (64 rows); with more workgroups than CUs the lost second
+// workgroup per CU costs more than it gains.
+bool long_k_16(int64_t N, int64_t K) {
+    const int64_t groups = (N + 15) / 16;
+    return K >= 8192 && groups > 128 && groups <= 256;
+}
+
+Config select_config(int64_t M, int64_t N, int64_t K) {
     if (M <= 64) {
         // Measured on MI355X at the Llama-3 decode shapes: 64-column blocks
         // stream fastest once they still give every CU a block (N >= 16384);
         // narrower weights need 16-column blocks to reach every CU.
         if ((N + 63) / 64 >= 256) return M <= 16 ? kDecode64x16 : kDecode64x64;
+        if (long_k_16(N, K)) return M <= 16 ? kDecode16x16L : kDecode16x64L;
         return M <= 16 ? kDecode16x16 : kDecode16x64;
     }
     // The largest tile that still gives every CU a block, else the smallest.
@@ -796,11 +809,13 @@ Config select_config(int64_t M, int64_t N) {
 template <int QT, int OT>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
     if (a.splits > 1) return run_decode<QT, OT, 64, 4, 256, 2>(a, st);
-    switch (select_config(a.M, a.N)) {
+    switch (select_config(a.M, a.N, a.K)) {
         case kDecode64x16: return run_decode<QT, OT, 64, 1, 512, 2>(a, st);
         case kDecode64x64: return run_decode<QT, OT, 64, 4, 256, 2>(a, st);
         case kDecode16x16: return run_decode<QT, OT, 16, 1, 1024, 2>(a, st);
         case kDecode16x64: return run_decode<QT, OT, 16, 4, 512, 2>(a, st);
+        case kDecode16x16L: return run_decode<QT, OT, 16, 1, 2048, 2>(a, st);
+        case kDecode16x64L: return run_decode<QT, OT, 16, 4, 1024, 2>(a, st);
         case kTile256x256: return run_tile<QT, OT, 256, 256, 2, 4>(a, st);
         case kTile256x128: return run_tile<QT, OT, 256, 128, 4, 2>(a, st);
         case kTile128x128: return run_tile<QT, OT, 128, 128, 2, 2>(a, st);
@@ -825,11 +840,13 @@ hipError_t dispatch_ot(int ot, const GemmArgs& a, hipStream_t st) {
 // Split-K for decode problems above 16 rows with a long K on weights too
 // narrow for 64-column blocks to occupy the GPU: 4 splits of the 64-column
 // kernel, so that each activation tile is read once per 64 columns instead
-// of once per 16 (measured on MI355X: Llama-3-8B down, 64 x 4096 x 14336,
-// from 29 to 20 us). Shorter K does not repay the extra pass.
+// of once per 16. Shorter K does not repay the extra pass. Where 16-column
+// workgroups fill 129..256 CUs the long-stage 16-column kernel is as fast
+// without the extra pass (Llama-3-8B down, 64 x 4096 x 14336: 23.6 us
+// against 24.0 us split) and takes those problems.
 SplitPlan plan_splitk(int64_t M, int64_t N, int64_t K) {
     SplitPlan d{1, 0, 0};
-    if (M <= 16 || M > 64 || K < 8192 || (N + 63) / 64 >= 256) return d;
+    if (M <= 16 || M > 64 || K < 8192 || (N + 63) / 64 >= 256 || long_k_16(N, K)) return d;
     constexpr int kStageBytes = 256;  // the 64-column kernel's K stage
     const int64_t stages = (K + kStageBytes - 1) / kStageBytes;
     d.splits = 4;
@@ -938,11 +955,13 @@ hipError_t launch_quant_scaled_mm(const GemmProblem& p, int xt, const void* x, i
 
 const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K, bool workspace) {
     if (workspace && plan_splitk(M, N, K).splits > 1) return "gemm_decode_kernel<64x64>+splitk_reduce_kernel";
-    switch (select_config(M, N)) {
+    switch (select_config(M, N, K)) {
         case kDecode64x16: return "gemm_decode_kernel<64x16>";
         case kDecode64x64: return "gemm_decode_kernel<64x64>";
         case kDecode16x16: return "gemm_decode_kernel<16x16>";
         case kDecode16x64: return "gemm_decode_kernel<16x64>";
+        case kDecode16x16L: return "gemm_decode_kernel<16x16,2K>";
+        case kDecode16x64L: return "gemm_decode_kernel<16x64,1K>";
         case kTile256x256: return "gemm_tile_kernel<256x256>";
         case kTile256x128: return "gemm_tile_kernel<256x128>";
         case kTile128x128: return "gemm_tile_kernel<128x128>";

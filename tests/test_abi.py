@@ -127,6 +127,8 @@ def test_kernel_configuration_names(lib):
     assert name(64, 6144, 4096) == "gemm_decode_kernel<16x64>"
     assert name(1, 28672, 4096) == "gemm_decode_kernel<64x16>"
     assert name(17, 28672, 4096) == "gemm_decode_kernel<64x64>"
+    assert name(16, 4096, 14336) == "gemm_decode_kernel<16x16,2K>"
+    assert name(16, 6144, 14336) == "gemm_decode_kernel<16x16>"  # more workgroups than CUs
     assert name(8192, 28672, 4096) == "gemm_tile_kernel<256x256>"
     assert name(2048, 4096, 4096) == "gemm_tile_kernel<256x128>"
     assert name(512, 4096, 4096) == "gemm_tile_kernel<64x64>"
@@ -156,16 +158,19 @@ def test_quant_scaled_mm_validation(lib):
 def test_split_k_workspace_plan(lib):
     """Which problems split K with a workspace, and how much they need."""
     size = lib.w8a8_scaled_mm_workspace_size
-    assert size(64, 4096, 14336) == 4 * 64 * 4096 * 4      # Llama-3-8B down, 64 tokens
+    assert size(64, 8192, 14336) == 4 * 64 * 8192 * 4
     assert size(17, 8192, 8192) == 4 * 17 * 8192 * 4
+    assert size(40, 1000, 8192) == 4 * 40 * 1000 * 4      # few 16-column workgroups
+    assert size(64, 4096, 14336) == 0                      # Llama-3-8B down: the long-stage kernel
     assert size(16, 4096, 14336) == 0                      # M <= 16: no split
     assert size(64, 4096, 4096) == 0                       # short K
     assert size(64, 28672, 8192) == 0                      # wide N
     assert size(65, 4096, 14336) == 0                      # the tiled path
     assert size(-1, 4096, 14336) == 0
     name = lambda M, N, K: lib.w8a8_scaled_mm_ws_kernel(M, N, K).decode()
-    assert name(64, 4096, 14336) == "gemm_decode_kernel<64x64>+splitk_reduce_kernel"
+    assert name(64, 8192, 14336) == "gemm_decode_kernel<64x64>+splitk_reduce_kernel"
     assert name(64, 4096, 4096) == lib.w8a8_scaled_mm_kernel(64, 4096, 4096).decode()
+    assert name(64, 4096, 14336) == "gemm_decode_kernel<16x64,1K>"
     ws = lib.w8a8_scaled_mm_ws
     args = (FAKE, 0, 64, FAKE, 128, FAKE, 128, 1, 16, 64, 128, None, 1, None, 1)
     assert ws(*args, FAKE + 16, 1024, None) == ALIGN       # 256-byte aligned workspace

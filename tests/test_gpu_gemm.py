@@ -245,7 +245,9 @@ def bits_t(t):
 DECODE_SHAPES = [(1, 4096, 4096), (5, 6144 + 16, 4096 + 16), (16, 4096, 14336), (17, 100, 272),
                  (33, 1000, 1040), (64, 4096, 4096), (64, 48, 144), (1, 16384 + 16, 1024 + 16),
                  (16, 16384, 2064), (17, 16384, 2048), (64, 16400, 272), (40, 20000, 512),
-                 (3, 16336, 16), (64, 28672, 4096)]
+                 (3, 16336, 16), (64, 28672, 4096),
+                 # long K on 129..256 sixteen-column workgroups: the long-stage variants
+                 (64, 4096, 14336), (40, 3000 + 8, 8192 + 16)]
 
 
 @pytest.mark.parametrize("qtype", ["fp8", "int8"])
@@ -264,13 +266,14 @@ def test_decode_configs_are_the_ones_named():
     """The shapes above cover every decode configuration."""
     names = {w8.w8a8_scaled_mm_kernel(M, N, K) for M, N, K in DECODE_SHAPES}
     assert names == {"gemm_decode_kernel<16x16>", "gemm_decode_kernel<16x64>",
-                     "gemm_decode_kernel<64x16>", "gemm_decode_kernel<64x64>"}, names
+                     "gemm_decode_kernel<64x16>", "gemm_decode_kernel<64x64>",
+                     "gemm_decode_kernel<16x16,2K>", "gemm_decode_kernel<16x64,1K>"}, names
 
 
 # Split-K through a caller workspace: decode problems above 16 rows with a
 # long K on narrow weights (the Llama-3-8B down projection at 64 tokens,
 # ragged N and K, the widest N that still splits).
-SPLITK_SHAPES = [(64, 4096, 14336), (40, 1000, 8192 + 16), (17, 300, 16384), (64, 16320, 8192),
+SPLITK_SHAPES = [(64, 4608, 14336), (40, 1000, 8192 + 16), (17, 300, 16384), (64, 16320, 8192),
                  (33, 48, 9000 - 9000 % 16)]
 
 
@@ -300,7 +303,7 @@ def test_split_k_workspace_parity(qtype, M, N, K):
 
 def test_split_k_workspace_too_small_falls_back():
     """A workspace below the size needed is not used: the plain kernel runs."""
-    M, N, K = 64, 4096, 14336
+    M, N, K = 64, 4608, 14336
     a, sa, b, sb = _quantized(M, N, K, "int8", seed=9)
     need = w8.w8a8_scaled_mm_workspace_size(M, N, K)
     ad, bd = codes_to_dev(a, "int8"), codes_to_dev(b, "int8")
