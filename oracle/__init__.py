@@ -14,6 +14,9 @@ their sources on the reference pages are in the C file's header:
   divide, clamp to the e4m3 range, cast.
 * "Enable scaled FP8 (e4m3fn) KV cache on ROCm" ("Scaling semantics"):
   scale = absmax/448, q = fp8(x/scale), x' = dequant(q)*scale.
+* "[Kernel] Support Fp8 Checkpoints (Dynamic + Static)": merged layers with
+  per-shard weight scales, either expanded to per-channel scales or rescaled
+  to one shared scale max(s_i) by the ratio s_i / max(s_i).
 
 Parity pins: every function here is pinned in ``tests/test_oracle_*.py``
 against something other than itself (torch's CPU float8 cast, numpy's
@@ -82,6 +85,10 @@ def lib():
         L.oracle_kv_quant.argtypes = [P, I, I64, P, P, I]
         L.oracle_kv_dequant.restype = None
         L.oracle_kv_dequant.argtypes = [P, I64, P, P, I]
+        L.oracle_expand_shard_scales.restype = None
+        L.oracle_expand_shard_scales.argtypes = [P, P, I64, P]
+        L.oracle_requant_shared_scale.restype = None
+        L.oracle_requant_shared_scale.argtypes = [P, I64, I, I64, P, I64, P, P, I64, P]
         L.oracle_scaled_mm.restype = None
         L.oracle_scaled_mm.argtypes = [P, I, I64, P, I64, P, I64, I, I64, I64, I64, P, I64, P, I64]
         L.oracle_num_threads.restype = ctypes.c_int
@@ -193,6 +200,37 @@ def kv_dequant(q: np.ndarray, scale, xtype: str = "bf16") -> np.ndarray:
     out = np.empty(q.size, np.float32 if xtype == "f32" else np.uint16)
     lib().oracle_kv_dequant(_ptr(q), q.size, _ptr(s), _ptr(out), DTYPES[xtype])
     return out
+
+
+# -------------------------------------------------------------- merged layers
+def expand_shard_scales(shard_scales, rows) -> np.ndarray:
+    """Per-channel weight scales of a merged layer: shard i's scale on each of
+    its rows ("[Kernel] Support Fp8 Checkpoints (Dynamic + Static)")."""
+    s = np.ascontiguousarray(np.asarray(shard_scales, dtype=np.float32).reshape(-1))
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+    if s.size != r.size or (r < 0).any():
+        raise ValueError("one non-negative row count per shard scale")
+    out = np.empty(int(r.sum()), np.float32)
+    lib().oracle_expand_shard_scales(_ptr(s), _ptr(r), s.size, _ptr(out))
+    return out
+
+
+def requant_shared_scale(w: np.ndarray, qtype: str, rows, shard_scales):
+    """Codes of a merged weight [N, K] rescaled to one shared scale
+    s = max(s_i): code c of shard i becomes enc(fl32(dec(c) * fl32(s_i / s)))
+    (review comment on "[Kernel] Support Fp8 Checkpoints"). Returns
+    (codes [N, K] uint8, s as float32)."""
+    w = np.ascontiguousarray(w).view(np.uint8)
+    s = np.ascontiguousarray(np.asarray(shard_scales, dtype=np.float32).reshape(-1))
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+    if s.size != r.size or s.size == 0 or (r < 0).any() or int(r.sum()) != w.shape[0]:
+        raise ValueError("one non-negative row count per shard scale, summing to N")
+    N, K = w.shape
+    out = np.empty((N, K), np.uint8)
+    shared = np.zeros(1, np.float32)
+    lib().oracle_requant_shared_scale(_ptr(w), K, QTYPES[qtype], K, _ptr(r), s.size, _ptr(s),
+                                      _ptr(out), K, _ptr(shared))
+    return out, np.float32(shared[0])
 
 
 # -------------------------------------------------------------------- the GEMM

@@ -19,6 +19,10 @@
  *    "Scaling semantics": scale = absmax / 448 (the e4m3 max-norm),
  *    q = fp8_quant(x / scale), x' = fp8_dequant(q) * scale, per tensor; and
  *    the review answers on the same page: no scale given means scale 1.0.
+ *  - "[Kernel] Support Fp8 Checkpoints (Dynamic + Static)" (vLLM PR 4332):
+ *    merged layers (QKV, gate_up) whose shards carry their own weight
+ *    scales; a review comment there proposes one shared scale max(s_i) with
+ *    every shard rescaled by s_i / max(s_i).
  *
  * Readings taken where the pages are silent (listed with the reasons in the
  * design notes of the repository):
@@ -262,6 +266,53 @@ void oracle_kv_dequant(const uint8_t* q, int64_t n, const float* scale, void* x,
     for (int64_t i = 0; i < n; ++i) {
         float d = (float)oracle_e4m3_decode(q[i]);   /* exact */
         store_x(x, xtype, i, d * s);
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Merged layers: a weight made of S shards stacked along N (QKV, gate_up), */
+/* shard i holding n_i consecutive rows and its own per-tensor scale s_i    */
+/* ("[Kernel] Support Fp8 Checkpoints (Dynamic + Static)": the loader must  */
+/* handle merged layers whose shards do not share one weight scale).        */
+/* ---------------------------------------------------------------------- */
+
+/* Per-output-channel form of the shard scales: b_scales[n] = s_i for every
+ * row n of shard i, so that one scaled product with per-channel weight
+ * scales covers the whole merged layer. */
+void oracle_expand_shard_scales(const float* shard_scales, const int64_t* rows, int64_t S,
+                                float* out) {
+    int64_t n = 0;
+    for (int64_t i = 0; i < S; ++i)
+        for (int64_t r = 0; r < rows[i]; ++r) out[n++] = shard_scales[i];
+}
+
+/* One shared scale (the review comment on the same page): s = max_i s_i,
+ * and every code c of shard i is rescaled by the shard's ratio to it,
+ * w' = (s_i / s) * w. Read literally, in binary32 with round-to-nearest-
+ * even at each step: the ratio t_i = fl32(s_i / s) first, then the value
+ * v = fl32(dec(c) * t_i), then the usual encode of v (saturating RNE for
+ * e4m3, round-half-even and clamp to +-127 for int8). w is [N, K] with row
+ * stride ldw (N = sum of rows), out likewise with stride ldo; *shared = s. */
+void oracle_requant_shared_scale(const uint8_t* w, int64_t ldw, int qtype, int64_t K,
+                                 const int64_t* rows, int64_t S, const float* shard_scales,
+                                 uint8_t* out, int64_t ldo, float* shared) {
+    float smax = shard_scales[0];
+    for (int64_t i = 1; i < S; ++i)
+        if (shard_scales[i] > smax) smax = shard_scales[i];
+    *shared = smax;
+    int64_t n0 = 0;
+    for (int64_t i = 0; i < S; ++i) {
+        const float t = shard_scales[i] / smax;
+#pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < rows[i]; ++r)
+            for (int64_t k = 0; k < K; ++k) {
+                const uint8_t c = w[(n0 + r) * ldw + k];
+                const float d = qtype == QT_FP8 ? (float)oracle_e4m3_decode(c) : (float)(int8_t)c;
+                const float v = d * t;
+                out[(n0 + r) * ldo + k] =
+                    qtype == QT_FP8 ? oracle_e4m3_encode(v) : (uint8_t)oracle_int8_encode(v);
+            }
+        n0 += rows[i];
     }
 }
 
