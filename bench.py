@@ -172,6 +172,34 @@ def build_kv_workload(dev, layers=workloads.KV_LAYERS):
     return launches, keep
 
 
+def shard_scales(S: int, seed: int) -> torch.Tensor:
+    g = torch.Generator().manual_seed(seed)
+    return torch.rand(S, generator=g) * 3.8e-3 + 2e-4
+
+
+def build_merge_workload(dev):
+    """Merged QKV / gate_up weights: the per-shard scales expanded to
+    per-channel scales, and the codes rescaled to one shared scale."""
+    launches, keep = [], []
+    for i, (name, rows, K, qtype) in enumerate(workloads.MERGED_LAYERS):
+        N, S = sum(rows), len(rows)
+        w = workloads.random_codes((N, K), qtype, seed=40 + i, device=dev).view(
+            torch.float8_e4m3fn if qtype == "fp8" else torch.int8)
+        s = shard_scales(S, 50 + i).to(dev)
+        sb = torch.empty(N, dtype=torch.float32, device=dev)
+        out = torch.empty_like(w)
+        sh = torch.empty(1, dtype=torch.float32, device=dev)
+        launches.append(Launch("merge_expand",
+                               lambda s=s, rows=rows, sb=sb: w8.w8a8_expand_shard_scales(s, rows, out=sb),
+                               0, 4 * S + 4 * N, f"expand {name}", "expand_shard_scales_kernel"))
+        launches.append(Launch("merge_requant",
+                               lambda w=w, rows=rows, s=s, out=out, sh=sh:
+                               w8.w8a8_requant_shared_scale(w, rows, s, out=out, shared_scale=sh),
+                               0, 2 * N * K + 4 * S + 4, f"requant {name}", "requant_shared_kernel"))
+        keep += [w, s, sb, out, sh]
+    return launches, keep
+
+
 WORKLOADS = {
     "decode": dict(desc="fp8 e4m3 decode GEMMs, Llama-3-8B QKV/O/gate_up/down at M=1,16,64: "
                         "dynamic per-token activation quant + scaled_mm, per-channel weights, "
@@ -191,6 +219,9 @@ WORKLOADS = {
     "kv": dict(desc="scaled fp8 KV cache: per-tensor dynamic quant + dequant of 32 layers of "
                     "K and V [32768,8,128] bf16, plus per-token fp8 quant of [8192,4096]",
                ),
+    "merge": dict(desc="merged-layer weight scales: per-shard scales of the merged QKV and "
+                       "gate_up weights (Llama-3-8B fp8, Llama-3-70B int8) expanded to "
+                       "per-channel scales, and the codes rescaled to one shared scale"),
 }
 
 
@@ -283,6 +314,23 @@ def cpu_baseline(spec, launches_meta, budget_s: float):
 
     import oracle
     cores = oracle.num_threads()
+    if spec is WORKLOADS["merge"]:   # the oracle's requantisation of the 8B merged weights
+        dt, nbytes, done = 0.0, 0, 0
+        for i, (name, rows, K, qtype) in enumerate(workloads.MERGED_LAYERS):
+            w = workloads.random_codes((sum(rows), K), qtype, seed=40 + i).numpy()
+            s = shard_scales(len(rows), 50 + i).numpy()
+            t0 = time.perf_counter()
+            oracle.expand_shard_scales(s, rows)
+            oracle.requant_shared_scale(w, qtype, rows, s)
+            dt += time.perf_counter() - t0
+            nbytes += 2 * w.size + 4 * sum(rows)
+            done += 1
+            if dt > budget_s:
+                break
+        return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+                "kind": "oracle",
+                "sample": f"expansion + requantisation of {done} of the step's "
+                          f"{len(workloads.MERGED_LAYERS)} merged weights ({dt:.1f} s)"}
     if spec.get("layers") is None:   # kv: quant + dequant of whole layer tensors
         n = 1
         for d in workloads.KV_SHAPE:
@@ -376,6 +424,8 @@ def main():
     log(f"[bench] workload {args.workload}: building inputs")
     if args.workload == "kv":
         launches, keep = build_kv_workload(dev)
+    elif args.workload == "merge":
+        launches, keep = build_merge_workload(dev)
     else:
         launches, keep = build_gemm_workload(spec["layers"], spec["Ms"], spec["qtype"],
                                              spec["act"], dev)
@@ -408,6 +458,10 @@ def main():
         value = per_step_bytes / (step_ms / 1e3) / 1e9
         metric, unit = "scaled fp8 KV cache quant+dequant GB/s (algorithmic bytes)", "GB/s"
         dtype = "fp8e4m3"
+    elif args.workload == "merge":
+        value = per_step_bytes / (step_ms / 1e3) / 1e9
+        metric, unit = "merged-layer scale expansion + shared-scale requant GB/s (algorithmic bytes)", "GB/s"
+        dtype = "u8 codes (fp8e4m3, int8), f32 arithmetic"
     else:
         value = per_step_flops / (step_ms / 1e3) / 1e12
         metric, unit = METRIC, "TFLOP/s"
@@ -430,7 +484,7 @@ def main():
     # most time per step; the small per-token quantizations of decode batches
     # are latency-bound (a few KB each) and are listed with their latency only.
     kinds = {L.kernel: L.kind for L in launches}
-    main_kind = "kv_quant" if args.workload == "kv" else "gemm"
+    main_kind = {"kv": "kv_quant", "merge": "merge_requant"}.get(args.workload, "gemm")
     dom = max((k for k in kernels if kinds[k] == main_kind),
               key=lambda k: kernels[k]["avg_s"] * kernels[k]["launches"])
     roof = roofline(dom, kernels[dom], spec, args.workload)
@@ -456,8 +510,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic (seeded; Llama-3 layer shapes, bf16 N(0,1) activations with 1% "
-                "outlier channels x20, N(0,0.02) weights)" if args.workload != "kv" else
-                "synthetic (seeded; N(0,1) K/V with 0.1% outliers x10)",
+                "outlier channels x20, N(0,0.02) weights)" if args.workload not in ("kv", "merge") else
+                "synthetic (seeded; N(0,1) K/V with 0.1% outliers x10)" if args.workload == "kv" else
+                "synthetic (seeded; uniformly random valid codes, shard scales U(2e-4, 4e-3))",
         "config": {"workload": spec["desc"], "mode": "hip-graph replay, inputs resident in HBM",
                    "step_bytes": per_step_bytes, "step_flops": per_step_flops,
                    "launches_per_step": len(launches), "parallelism": "single GPU"},

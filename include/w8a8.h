@@ -197,6 +197,41 @@ w8a8_status kv_fp8_scaled_dequant(const uint8_t* q, int64_t n, const float* scal
                                   w8a8_dtype xt, hipStream_t stream);
 
 /*
+ * Merged layers [P2: the loader must handle merged QKV / gate_up layers
+ * whose shards carry their own weight scales; a review comment on the same
+ * page proposes one shared scale]. A merged weight stacks S shards along N:
+ * shard i holds shard_rows[i] consecutive rows (host array, >= 0 each, at
+ * most W8A8_MAX_SHARDS shards) and has the per-tensor weight scale
+ * shard_scales[i] (device, positive).
+ */
+#define W8A8_MAX_SHARDS 64
+
+/*
+ * Per-channel form: b_scales[n] = shard_scales[i] for every row n of shard
+ * i (device output, N = sum of shard_rows entries). Exact: one
+ * w8a8_scaled_mm with per-channel b_scales then computes every shard as its
+ * own per-tensor product would. N == 0 is a no-op.
+ */
+w8a8_status w8a8_expand_shard_scales(const float* shard_scales, const int64_t* shard_rows,
+                                     int64_t num_shards, float* b_scales, hipStream_t stream);
+
+/*
+ * Shared-scale form: *shared_scale = s = max_i shard_scales[i], and every
+ * code c of shard i is rescaled by the shard's ratio to it, in binary32
+ * with round-to-nearest-even at each step: t_i = s_i / s, v = dec(c) * t_i,
+ * code = enc(v) (e4m3: saturating RNE, NaN codes stay NaN 0x7F; int8: round
+ * half to even, clamp to +-127). Lossy by one rounding per code; the shard
+ * holding the maximum keeps its codes. w and out: [N, K] codes with row
+ * strides ldw and ldo bytes (device; out may be w itself with ldo == ldw,
+ * other overlaps are undefined). K, ldw, ldo multiples of 16; w and out
+ * 16-byte aligned. The scale is written even when N or K is 0.
+ */
+w8a8_status w8a8_requant_shared_scale(const void* w, int64_t ldw, w8a8_qtype qt, int64_t K,
+                                      const int64_t* shard_rows, int64_t num_shards,
+                                      const float* shard_scales, void* out, int64_t ldo,
+                                      float* shared_scale, hipStream_t stream);
+
+/*
  * Name of the kernel configuration w8a8_scaled_mm runs for an M x N x K
  * problem, such as "gemm_decode_kernel<16x16>" or
  * "gemm_tile_kernel<256x256>" (a static string; "" for negative sizes), so

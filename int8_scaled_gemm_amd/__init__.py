@@ -57,6 +57,8 @@ SIGNATURES = {
                              _P, _I64, _P, _P],
     "kv_fp8_scaled_quant": [_P, _I, _I64, _P, _P, _I, _P],
     "kv_fp8_scaled_dequant": [_P, _I64, _P, _P, _I, _P],
+    "w8a8_expand_shard_scales": [_P, _P, _I64, _P, _P],
+    "w8a8_requant_shared_scale": [_P, _I64, _I, _I64, _P, _I64, _P, _P, _I64, _P, _P],
 }
 
 
@@ -212,6 +214,54 @@ def kv_fp8_scaled_dequant(q: torch.Tensor, scale: torch.Tensor | None,
     return out
 
 
+# -------------------------------------------------------------- merged layers
+def _shard_rows(shard_rows):
+    rows = (ctypes.c_int64 * max(len(shard_rows), 1))(*[int(r) for r in shard_rows])
+    return rows, len(shard_rows), sum(int(r) for r in shard_rows)
+
+
+def w8a8_expand_shard_scales(shard_scales: torch.Tensor, shard_rows,
+                             out: torch.Tensor | None = None) -> torch.Tensor:
+    """Per-channel weight scales of a merged layer: shard i's scale on each of
+    its shard_rows[i] rows (float32 [N] on the device)."""
+    _check_cuda(shard_scales, out)
+    rows, S, N = _shard_rows(shard_rows)
+    if shard_scales.dtype != torch.float32 or not shard_scales.is_contiguous() or shard_scales.numel() != S:
+        raise ValueError("shard_scales must be a contiguous float32 tensor with one entry per shard")
+    if out is None:
+        out = torch.empty(N, dtype=torch.float32, device=shard_scales.device)
+    _call("w8a8_expand_shard_scales", _ptr(shard_scales), rows, S, _ptr(out), _stream(shard_scales))
+    return out
+
+
+def w8a8_requant_shared_scale(w: torch.Tensor, shard_rows, shard_scales: torch.Tensor,
+                              out: torch.Tensor | None = None,
+                              shared_scale: torch.Tensor | None = None):
+    """Codes of a merged weight [N, K] (float8_e4m3fn or int8) rescaled to one
+    shared scale max(shard_scales). out may be w (in place). Returns
+    (out, shared_scale) with shared_scale a float32 [1] device tensor."""
+    _check_cuda(w, shard_scales, out, shared_scale)
+    qt = _qtype(w.dtype)
+    N, K, ldw = _rows(w, "w")
+    rows, S, n = _shard_rows(shard_rows)
+    if n != N:
+        raise ValueError(f"shard_rows add up to {n}, w has {N} rows")
+    if shard_scales.dtype != torch.float32 or not shard_scales.is_contiguous() or shard_scales.numel() != S:
+        raise ValueError("shard_scales must be a contiguous float32 tensor with one entry per shard")
+    if out is None:
+        out = torch.empty((N, K), dtype=w.dtype, device=w.device)
+    if out.dtype != w.dtype or tuple(out.shape) != (N, K):
+        raise ValueError("out must match w in dtype and shape")
+    _, _, ldo = _rows(out, "out")
+    if K == 0:
+        ldw = ldo = 0  # no columns: the strides are never used
+    if shared_scale is None:
+        shared_scale = torch.empty(1, dtype=torch.float32, device=w.device)
+    _call("w8a8_requant_shared_scale", _ptr(w), ldw, qt, K, rows, S, _ptr(shard_scales), _ptr(out),
+          ldo, _ptr(shared_scale), _stream(w))
+    return out, shared_scale
+
+
 # ---------------------------------------------------------------------- GEMM
 def w8a8_scaled_mm_workspace_size(M: int, N: int, K: int) -> int:
     """Bytes of workspace with which w8a8_scaled_mm_ws splits K (0: none)."""
@@ -330,4 +380,5 @@ def version() -> str:
 __all__ = ["w8a8_quant_per_token", "w8a8_quant_per_tensor", "w8a8_scaled_mm",
            "w8a8_scaled_mm_kernel", "w8a8_scaled_mm_workspace_size", "w8a8_quant_scaled_mm", "w8a8_quant_scaled_mm_kernel",
            "kv_fp8_scaled_quant", "kv_fp8_scaled_dequant", "scaled_mm", "W8A8Error",
+           "w8a8_expand_shard_scales", "w8a8_requant_shared_scale",
            "load_library", "version", "LIB_PATH", "SIGNATURES"]

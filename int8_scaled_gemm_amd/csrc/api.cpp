@@ -14,6 +14,8 @@
 #include "../../include/w8a8.h"
 #include "launch.hpp"
 
+static_assert(W8A8_MAX_SHARDS == w8a8::kMaxShards, "shard limit of the C ABI and the kernels");
+
 namespace {
 
 thread_local char g_msg[512] = "";
@@ -280,6 +282,62 @@ w8a8_status kv_fp8_scaled_dequant(const uint8_t* q, int64_t n, const float* scal
     if (!aligned16(q) || !aligned16(x)) return fail(W8A8_ERR_ALIGNMENT, "%s: q and x must be 16-byte aligned", fn);
     if (scale && (reinterpret_cast<uintptr_t>(scale) & 3u)) return fail(W8A8_ERR_ALIGNMENT, "%s: scale must be 4-byte aligned", fn);
     return from_hip(w8a8::launch_kv_dequant(q, n, scale, x, xt, stream), fn);
+}
+
+static w8a8_status check_shards(const char* fn, const int64_t* rows, int64_t S, int64_t* N) {
+    if (S < 1) return fail(W8A8_ERR_SHAPE, "%s: num_shards=%lld must be >= 1", fn, (long long)S);
+    if (S > W8A8_MAX_SHARDS)
+        return fail(W8A8_ERR_UNSUPPORTED, "%s: num_shards=%lld above %d", fn, (long long)S, W8A8_MAX_SHARDS);
+    if (!rows) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL shard_rows", fn);
+    int64_t n = 0;
+    for (int64_t i = 0; i < S; ++i) {
+        if (rows[i] < 0) return fail(W8A8_ERR_SHAPE, "%s: shard %lld has %lld rows", fn, (long long)i, (long long)rows[i]);
+        n += rows[i];
+        if (n > kMaxDim) return fail(W8A8_ERR_UNSUPPORTED, "%s: more than 2^31-1 rows", fn);
+    }
+    *N = n;
+    return W8A8_OK;
+}
+
+w8a8_status w8a8_expand_shard_scales(const float* shard_scales, const int64_t* shard_rows,
+                                     int64_t num_shards, float* b_scales, hipStream_t stream) {
+    const char* fn = "w8a8_expand_shard_scales";
+    int64_t N = 0;
+    const w8a8_status e = check_shards(fn, shard_rows, num_shards, &N);
+    if (e != W8A8_OK) return e;
+    if (N == 0) return ok();
+    if (!shard_scales || !b_scales) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL shard_scales or b_scales", fn);
+    if ((reinterpret_cast<uintptr_t>(shard_scales) | reinterpret_cast<uintptr_t>(b_scales)) & 3u)
+        return fail(W8A8_ERR_ALIGNMENT, "%s: scale arrays must be 4-byte aligned", fn);
+    return from_hip(w8a8::launch_expand_shard_scales(shard_scales, shard_rows, num_shards, b_scales, stream), fn);
+}
+
+w8a8_status w8a8_requant_shared_scale(const void* w, int64_t ldw, w8a8_qtype qt, int64_t K,
+                                      const int64_t* shard_rows, int64_t num_shards,
+                                      const float* shard_scales, void* out, int64_t ldo,
+                                      float* shared_scale, hipStream_t stream) {
+    const char* fn = "w8a8_requant_shared_scale";
+    if (!valid_qtype(qt)) return fail(W8A8_ERR_DTYPE, "%s: code type %d is not INT8 or FP8_E4M3FN", fn, qt);
+    int64_t N = 0;
+    const w8a8_status e = check_shards(fn, shard_rows, num_shards, &N);
+    if (e != W8A8_OK) return e;
+    if (K < 0) return fail(W8A8_ERR_SHAPE, "%s: negative K", fn);
+    if (K > kMaxDim) return fail(W8A8_ERR_UNSUPPORTED, "%s: K above 2^31-1", fn);
+    if (ldw < K || ldo < K)
+        return fail(W8A8_ERR_LAYOUT, "%s: leading dimensions ldw=%lld ldo=%lld must be >= K=%lld", fn, (long long)ldw, (long long)ldo, (long long)K);
+    if (K % 16 || ldw % 16 || ldo % 16)
+        return fail(W8A8_ERR_ALIGNMENT, "%s: K, ldw and ldo must be multiples of 16", fn);
+    if (!shard_scales || !shared_scale) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL shard_scales or shared_scale", fn);
+    if ((reinterpret_cast<uintptr_t>(shard_scales) | reinterpret_cast<uintptr_t>(shared_scale)) & 3u)
+        return fail(W8A8_ERR_ALIGNMENT, "%s: scale pointers must be 4-byte aligned", fn);
+    if (N > 0 && K > 0) {
+        if (!w || !out) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL w or out", fn);
+        if (!aligned16(w) || !aligned16(out)) return fail(W8A8_ERR_ALIGNMENT, "%s: w and out must be 16-byte aligned", fn);
+    }
+    return from_hip(w8a8::launch_requant_shared_scale(static_cast<const uint8_t*>(w), ldw, qt, K, shard_rows,
+                                                      num_shards, shard_scales, static_cast<uint8_t*>(out), ldo,
+                                                      shared_scale, stream),
+                    fn);
 }
 
 }  // extern "C"

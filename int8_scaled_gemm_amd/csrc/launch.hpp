@@ -17,6 +17,20 @@ hipError_t launch_quant_per_tensor(int xt, const void* x, int64_t M, int64_t K, 
 hipError_t launch_kv_dequant(const uint8_t* q, int64_t n, const float* scale, void* x, int xt,
                              hipStream_t st);
 
+// Merged layers: the most shards one call takes (their row ends travel as
+// kernel arguments).
+constexpr int kMaxShards = 64;
+
+// b_scales[n] = s[i] for every row n of shard i (rows[i] rows each).
+hipError_t launch_expand_shard_scales(const float* s, const int64_t* rows, int64_t S, float* out,
+                                      hipStream_t st);
+
+// Codes of a merged [N, K] weight rescaled to the shared scale max(s):
+// out may be w itself (ldo == ldw); *shared receives max(s).
+hipError_t launch_requant_shared_scale(const uint8_t* w, int64_t ldw, int qt, int64_t K,
+                                       const int64_t* rows, int64_t S, const float* s, uint8_t* out,
+                                       int64_t ldo, float* shared, hipStream_t st);
+
 struct GemmProblem {
     void* out;
     int ot;

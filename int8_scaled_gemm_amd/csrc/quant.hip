@@ -404,6 +404,133 @@ hipError_t launch_quant_per_tensor(int xt, const void* x, int64_t M, int64_t K, 
     return per_tensor_q<Q_INT8>(xt, x, M, K, ldx, q, ldq, scale, dynamic, st);
 }
 
+// ------------------------------------------------------------------------
+// Merged layers [P2]: S shards stacked along N (QKV, gate_up), shard i on
+// rows [end[i-1], end[i]) with its own per-tensor weight scale s_i.
+// ------------------------------------------------------------------------
+struct ShardTable {
+    int S;
+    int64_t end[kMaxShards];  // running row counts; end[S-1] = N
+};
+
+// The shard of row n: the number of shard ends at or below n (unrolled over
+// the table so that it is indexed statically, from the kernel arguments).
+__device__ __forceinline__ int shard_of(const ShardTable& t, int64_t n) {
+    int i = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxShards - 1; ++j)
+        if (j < t.S - 1) i += n >= t.end[j] ? 1 : 0;
+    return i;
+}
+
+__global__ __launch_bounds__(kBlock) void expand_shard_scales_kernel(const float* __restrict__ s,
+                                                                    ShardTable t,
+                                                                    float* __restrict__ out) {
+    const int64_t n = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (n < t.end[t.S - 1]) out[n] = s[shard_of(t, n)];
+}
+
+// One wave per row at a time (the row's shard, and so its ratio, is uniform
+// across the wave), 8 KB of the row in flight per wave. The shared scale is
+// the largest shard scale; the row's ratio t = s_i / s is rounded once to
+// binary32 (the double quotient of two binary32 values rounds to the same
+// binary32 value as the exact one: 53 >= 2 * 24 + 2 bits), and every code
+// becomes enc(fl32(dec(c) * t)).
+constexpr int kRequantUnroll = 8;  // 16-byte chunks per lane in flight
+
+template <int QT>
+__device__ __forceinline__ uint32_t requant4(uint32_t c, float ratio) {
+    float d0, d1, d2, d3;
+    if constexpr (QT == Q_FP8) {
+        d0 = __builtin_amdgcn_cvt_f32_fp8(c, 0);
+        d1 = __builtin_amdgcn_cvt_f32_fp8(c, 1);
+        d2 = __builtin_amdgcn_cvt_f32_fp8(c, 2);
+        d3 = __builtin_amdgcn_cvt_f32_fp8(c, 3);
+    } else {
+        d0 = static_cast<float>(static_cast<int8_t>(c));
+        d1 = static_cast<float>(static_cast<int8_t>(c >> 8));
+        d2 = static_cast<float>(static_cast<int8_t>(c >> 16));
+        d3 = static_cast<float>(static_cast<int8_t>(c >> 24));
+    }
+    const float v0 = d0 * ratio, v1 = d1 * ratio, v2 = d2 * ratio, v3 = d3 * ratio;
+    return QT == Q_FP8 ? enc4_fp8(v0, v1, v2, v3) : enc4_i8(v0, v1, v2, v3);
+}
+
+template <int QT>
+__global__ __launch_bounds__(kBlock) void requant_shared_kernel(const uint8_t* __restrict__ w, int64_t ldw,
+                                                               int64_t K, const float* __restrict__ s,
+                                                               ShardTable t, uint8_t* out, int64_t ldo,
+                                                               float* __restrict__ shared) {
+    __shared__ float smax_lds;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    if (wave == 0) {
+        // scales are positive: 0 is neutral for the lanes past S
+        float v = lane < t.S ? s[lane] : 0.0f;
+        v = wave_max(v);
+        if (lane == 0) smax_lds = v;
+    }
+    __syncthreads();
+    const float smax = smax_lds;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *shared = smax;
+    const int64_t N = t.end[t.S - 1];
+    constexpr int kWaves = kBlock / 64;
+    for (int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + wave; row < N;
+         row += static_cast<int64_t>(gridDim.x) * kWaves) {
+        const int64_t r = __builtin_amdgcn_readfirstlane(static_cast<int>(row));
+        const float ratio =
+            static_cast<float>(static_cast<double>(s[shard_of(t, r)]) / static_cast<double>(smax));
+        const uint8_t* src = w + r * ldw;
+        uint8_t* dst = out + r * ldo;
+        for (int64_t k0 = 16 * lane; k0 < K; k0 += 1024 * kRequantUnroll) {
+            u32x4 c[kRequantUnroll];
+#pragma unroll
+            for (int u = 0; u < kRequantUnroll; ++u)
+                if (k0 + 1024 * u < K) c[u] = *reinterpret_cast<const u32x4*>(src + k0 + 1024 * u);
+#pragma unroll
+            for (int u = 0; u < kRequantUnroll; ++u) {
+                if (k0 + 1024 * u >= K) continue;
+                u32x4 q;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) q[j] = requant4<QT>(c[u][j], ratio);
+                *reinterpret_cast<u32x4*>(dst + k0 + 1024 * u) = q;
+            }
+        }
+    }
+}
+
+static ShardTable shard_table(const int64_t* rows, int64_t S) {
+    ShardTable t{};
+    t.S = static_cast<int>(S);
+    int64_t n = 0;
+    for (int64_t i = 0; i < S; ++i) t.end[i] = (n += rows[i]);
+    return t;
+}
+
+hipError_t launch_expand_shard_scales(const float* s, const int64_t* rows, int64_t S, float* out,
+                                      hipStream_t st) {
+    const ShardTable t = shard_table(rows, S);
+    const int64_t N = t.end[S - 1];
+    if (N == 0) return hipSuccess;
+    hipLaunchKernelGGL(expand_shard_scales_kernel, dim3(static_cast<unsigned>((N + kBlock - 1) / kBlock)),
+                       dim3(kBlock), 0, st, s, t, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_requant_shared_scale(const uint8_t* w, int64_t ldw, int qt, int64_t K,
+                                       const int64_t* rows, int64_t S, const float* s, uint8_t* out,
+                                       int64_t ldo, float* shared, hipStream_t st) {
+    const ShardTable t = shard_table(rows, S);
+    // a wave per row, at most 8 workgroups per CU's worth of grid (a grid-stride over rows)
+    const int64_t wg = (t.end[S - 1] + kBlock / 64 - 1) / (kBlock / 64);
+    const unsigned g = static_cast<unsigned>(std::min<int64_t>(std::max<int64_t>(wg, 1), 2048));
+    if (qt == Q_FP8)
+        hipLaunchKernelGGL((requant_shared_kernel<Q_FP8>), dim3(g), dim3(kBlock), 0, st, w, ldw, K, s, t, out, ldo, shared);
+    else
+        hipLaunchKernelGGL((requant_shared_kernel<Q_INT8>), dim3(g), dim3(kBlock), 0, st, w, ldw, K, s, t, out, ldo, shared);
+    return hipGetLastError();
+}
+
 hipError_t launch_kv_dequant(const uint8_t* q, int64_t n, const float* scale, void* x, int xt,
                              hipStream_t st) {
     if (n == 0) return hipSuccess;

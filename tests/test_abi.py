@@ -176,3 +176,31 @@ def test_split_k_workspace_plan(lib):
     assert ws(*args, FAKE + 16, 1024, None) == ALIGN       # 256-byte aligned workspace
     assert ws(*args, None, 1024, None) == INVALID
     assert ws(*args, FAKE, -1, None) == INVALID
+
+
+def test_merged_layer_validation(lib):
+    """Shard tables are checked on the host: counts, sizes, layout."""
+    I64 = ctypes.c_int64
+
+    def rows(*r):
+        return (I64 * len(r))(*r)
+
+    ex = lib.w8a8_expand_shard_scales
+    assert ex(FAKE, rows(4, -1), 2, FAKE, None) == SHAPE
+    assert "shard 1" in lib.w8a8_last_error().decode()
+    assert ex(FAKE, rows(4), 0, FAKE, None) == SHAPE
+    assert ex(FAKE, rows(*([1] * 65)), 65, FAKE, None) == UNSUP
+    assert ex(FAKE, None, 1, FAKE, None) == INVALID
+    assert ex(None, rows(3), 1, FAKE, None) == INVALID
+    assert ex(FAKE + 2, rows(3), 1, FAKE, None) == ALIGN
+    assert ex(None, rows(0, 0), 2, None, None) == OK           # no rows: nothing to write
+    rq = lib.w8a8_requant_shared_scale
+    r = rows(64, 64)
+    assert rq(FAKE, 128, 5, 128, r, 2, FAKE, FAKE, 128, FAKE, None) == DTYPE
+    assert rq(FAKE, 64, 1, 128, r, 2, FAKE, FAKE, 128, FAKE, None) == LAYOUT
+    assert rq(FAKE, 136, 1, 120, r, 2, FAKE, FAKE, 136, FAKE, None) == ALIGN
+    assert rq(FAKE + 16, 128, 1, 128, r, 2, FAKE, FAKE + 8, 128, FAKE, None) == ALIGN
+    assert rq(FAKE, 128, 1, 128, r, 2, FAKE, FAKE, 128, None, None) == INVALID  # the shared scale is an output
+    assert rq(None, 128, 1, 128, r, 2, FAKE, FAKE, 128, FAKE, None) == INVALID
+    assert rq(FAKE, 128, 1, -16, r, 2, FAKE, FAKE, 128, FAKE, None) == SHAPE
+    assert rq(FAKE, 128, 1, 128, rows(1, -2), 2, FAKE, FAKE, 128, FAKE, None) == SHAPE

@@ -43,6 +43,14 @@ INT8_70B_M = (1, 64, 4096)
 KV_SHAPE = (32768, 8, 128)
 KV_LAYERS = 32
 PER_TOKEN_STANDALONE = (8192, 4096)
+# Merged layers: the shards of the merged QKV and gate_up weights (rows per
+# shard, K, code type) whose per-shard scales are expanded or shared.
+MERGED_LAYERS = (
+    ("llama3-8b qkv", (4096, 1024, 1024), 4096, "fp8"),
+    ("llama3-8b gate_up", (14336, 14336), 4096, "fp8"),
+    ("llama3-70b qkv", (8192, 1024, 1024), 8192, "int8"),
+    ("llama3-70b gate_up", (28672, 28672), 8192, "int8"),
+)
 CALIBRATION_ROWS = 512
 CALIBRATION_SEED = 1
 OUTLIER_SEED = 2
