@@ -14,6 +14,9 @@ their sources on the reference pages are in the C file's header:
   divide, clamp to the e4m3 range, cast.
 * "Enable scaled FP8 (e4m3fn) KV cache on ROCm" ("Scaling semantics"):
   scale = absmax/448, q = fp8(x/scale), x' = dequant(q)*scale.
+* "[Kernel] Add w8a8 CUTLASS kernels" (the asymmetric int8 case): per-token
+  zero points, weight code sums, D = s_a s_b (acc - z colsum); the pages give
+  no formula, the textbook asymmetric scheme is taken (see oracle.c).
 * "[Kernel] Support Fp8 Checkpoints (Dynamic + Static)": merged layers with
   per-shard weight scales, either expanded to per-channel scales or rescaled
   to one shared scale max(s_i) by the ratio s_i / max(s_i).
@@ -85,6 +88,13 @@ def lib():
         L.oracle_kv_quant.argtypes = [P, I, I64, P, P, I]
         L.oracle_kv_dequant.restype = None
         L.oracle_kv_dequant.argtypes = [P, I64, P, P, I]
+        L.oracle_quant_per_token_azp.restype = None
+        L.oracle_quant_per_token_azp.argtypes = [P, I, I64, I64, I64, P, I64, P, P]
+        L.oracle_colsum.restype = None
+        L.oracle_colsum.argtypes = [P, I64, I64, I64, P]
+        L.oracle_scaled_mm_azp.restype = None
+        L.oracle_scaled_mm_azp.argtypes = [P, I, I64, P, I64, P, I64, I64, I64, I64, P, I64, P,
+                                           I64, P, I64]
         L.oracle_expand_shard_scales.restype = None
         L.oracle_expand_shard_scales.argtypes = [P, P, I64, P]
         L.oracle_requant_shared_scale.restype = None
@@ -199,6 +209,51 @@ def kv_dequant(q: np.ndarray, scale, xtype: str = "bf16") -> np.ndarray:
     s = None if scale is None else np.array([scale], np.float32)
     out = np.empty(q.size, np.float32 if xtype == "f32" else np.uint16)
     lib().oracle_kv_dequant(_ptr(q), q.size, _ptr(s), _ptr(out), DTYPES[xtype])
+    return out
+
+
+# ------------------------------------------------------- asymmetric int8 (azp)
+def quant_per_token_azp(x: np.ndarray, xtype: str | None = None):
+    """Asymmetric per-token int8: (codes [M, K] uint8, scales [M] f32, zero
+    points [M] int32), x ~ (q - z) * s over the row's range with 0 included."""
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    q = np.empty((M, K), np.uint8)
+    s = np.empty(M, np.float32)
+    z = np.empty(M, np.int32)
+    lib().oracle_quant_per_token_azp(_ptr(x), _xtype_of(x, xtype), M, K, K, _ptr(q), K, _ptr(s),
+                                     _ptr(z))
+    return q, s, z
+
+
+def colsum(b: np.ndarray) -> np.ndarray:
+    """Per-row sums of int8 weight codes b [N, K] (uint8 view), int32 [N]."""
+    b = np.ascontiguousarray(b).view(np.uint8)
+    N, K = b.shape
+    out = np.empty(N, np.int32)
+    lib().oracle_colsum(_ptr(b), K, N, K, _ptr(out))
+    return out
+
+
+def scaled_mm_azp(a: np.ndarray, b: np.ndarray, a_scales=None, azp=None, b_scales=None,
+                  otype: str = "bf16") -> np.ndarray:
+    """D = s_a (x) s_b * sum_k (a - z) b for int8 codes a [M, K], b [N, K]."""
+    a = np.ascontiguousarray(a).view(np.uint8)
+    b = np.ascontiguousarray(b).view(np.uint8)
+    M, K = a.shape
+    N = b.shape[0]
+    sa, n_a = _scales(a_scales, M)
+    sb, n_b = _scales(b_scales, N)
+    if azp is None:
+        z, n_z = None, 1
+    else:
+        z = np.ascontiguousarray(np.asarray(azp, dtype=np.int32).reshape(-1))
+        if z.size not in (1, M):
+            raise ValueError("azp length must be 1 or M")
+        n_z = z.size
+    out = np.empty((M, N), _OUT_NP[otype])
+    lib().oracle_scaled_mm_azp(_ptr(out), DTYPES[otype], N, _ptr(a), K, _ptr(b), K, M, N, K,
+                               _ptr(sa), n_a, _ptr(z), n_z, _ptr(sb), n_b)
     return out
 
 

@@ -19,6 +19,9 @@
  *    "Scaling semantics": scale = absmax / 448 (the e4m3 max-norm),
  *    q = fp8_quant(x / scale), x' = fp8_dequant(q) * scale, per tensor; and
  *    the review answers on the same page: no scale given means scale 1.0.
+ *  - the same page's note that the asymmetric int8 case needs small
+ *    operations fused onto the GEMM: zero points per token, the weights'
+ *    code sums, D = s_a s_b (acc - z colsum) (textbook asymmetric scheme).
  *  - "[Kernel] Support Fp8 Checkpoints (Dynamic + Static)" (vLLM PR 4332):
  *    merged layers (QKV, gate_up) whose shards carry their own weight
  *    scales; a review comment there proposes one shared scale max(s_i) with
@@ -267,6 +270,79 @@ void oracle_kv_dequant(const uint8_t* q, int64_t n, const float* scale, void* x,
         float d = (float)oracle_e4m3_decode(q[i]);   /* exact */
         store_x(x, xtype, i, d * s);
     }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Asymmetric int8 activations ("[Kernel] Add w8a8 CUTLASS kernels": the   */
+/* asymmetric int8 case brings small operations to fuse onto the GEMM; the */
+/* pages give no formula, so the textbook one is taken). Per row:          */
+/*   lo = min(0, min_k x), hi = max(0, max_k x) (0 stays representable),  */
+/*   s = fl32(hi - lo) / 255 in binary32 (1.0 when hi == lo, i.e. x == 0), */
+/*   z = clamp(rint(fl32(-128 - fl32(lo / s))), -128, 127) (int32),       */
+/*   q = clamp(rint(fl32(x / s)) + z, -128, 127),                          */
+/* so that x ~ (q - z) * s. Every rint rounds half to even.                */
+/* ---------------------------------------------------------------------- */
+void oracle_quant_per_token_azp(const void* x, int xtype, int64_t M, int64_t K, int64_t ldx,
+                                uint8_t* q, int64_t ldq, float* scales, int32_t* azp) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float lo = 0.0f, hi = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = load_x(x, xtype, m * ldx + k);
+            if (v > hi) hi = v;
+            if (v < lo) lo = v;
+        }
+        const float d = hi - lo;
+        const float s = d == 0.0f ? 1.0f : d / 255.0f;
+        float zf = rintf(-128.0f - lo / s);
+        if (zf < -128.0f) zf = -128.0f;
+        if (zf > 127.0f) zf = 127.0f;
+        scales[m] = s;
+        azp[m] = (int32_t)zf;
+        for (int64_t k = 0; k < K; ++k) {
+            float r = rintf(load_x(x, xtype, m * ldx + k) / s) + zf;
+            if (r < -128.0f) r = -128.0f;
+            if (r > 127.0f) r = 127.0f;
+            q[m * ldq + k] = (uint8_t)(int8_t)(int)r;
+        }
+    }
+}
+
+/* Sum of each int8 weight row's codes, colsum[n] = sum_k b[n, k]. */
+void oracle_colsum(const uint8_t* b, int64_t ldb, int64_t N, int64_t K, int32_t* out) {
+    for (int64_t n = 0; n < N; ++n) {
+        int64_t acc = 0;
+        for (int64_t k = 0; k < K; ++k) acc += (int8_t)b[n * ldb + k];
+        out[n] = (int32_t)acc;
+    }
+}
+
+/* The product with zero points: acc[m, n] = sum_k (a[m, k] - z[m or 0]) * b[n, k]
+ * (exact in int64), then D = acc * a_scale * b_scale in fp64, rounded once
+ * (DT_I32 stores acc itself). A NULL azp means zero points of 0. */
+void oracle_scaled_mm_azp(void* out, int otype, int64_t ldo, const uint8_t* a, int64_t lda,
+                          const uint8_t* b, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                          const float* sa, int64_t n_a, const int32_t* azp, int64_t n_azp,
+                          const float* sb, int64_t n_b) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            const int64_t z = azp ? azp[n_azp == 1 ? 0 : m] : 0;
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += ((int64_t)(int8_t)a[m * lda + k] - z) * (int64_t)(int8_t)b[n * ldb + k];
+            if (otype == DT_I32) {
+                ((int32_t*)out)[m * ldo + n] = (int32_t)acc;
+                continue;
+            }
+            const double s_a = sa ? (double)sa[n_a == 1 ? 0 : m] : 1.0;
+            const double s_b = sb ? (double)sb[n_b == 1 ? 0 : n] : 1.0;
+            const double d = (double)acc * s_a * s_b;
+            if (otype == DT_BF16) ((uint16_t*)out)[m * ldo + n] = oracle_bf16_from_double(d);
+            else if (otype == DT_FP16) ((uint16_t*)out)[m * ldo + n] = oracle_fp16_from_double(d);
+            else if (otype == DT_F64) ((double*)out)[m * ldo + n] = d;
+            else ((float*)out)[m * ldo + n] = (float)d;
+        }
 }
 
 /* ---------------------------------------------------------------------- */

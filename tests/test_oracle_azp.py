@@ -1,0 +1,110 @@
+"""Pins of the oracle's asymmetric int8 functions (the asymmetric int8 case
+of "[Kernel] Add w8a8 CUTLASS kernels": zero points per token and small
+operations fused onto the GEMM; the pages give no formula, the textbook
+scheme x ~ (q - z) * s over the row's range with 0 included is taken).
+
+The pins do not retype the oracle: closed forms (0 maps to the zero point,
+the row's negative extreme to -128, an all-zero row to scale 1 and codes
+-128), the rounding-error bound of every element, and the product against
+exact Python integers and against numpy's float64 matrix product of the
+dequantised operands.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+
+def _rows(seed, M=6, K=96):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32) * rng.uniform(0.1, 10, (M, 1)).astype(np.float32)
+    x[1] = np.abs(x[1])            # all non-negative: lo = 0
+    x[2] = -np.abs(x[2])           # all non-positive: hi = 0
+    x[3] = 0.0                     # all zero
+    x[4, :] = 0.0
+    x[4, 7] = -3.0                 # a single negative value
+    return x
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_azp_quant_closed_forms(seed):
+    x = _rows(seed)
+    q, s, z = oracle.quant_per_token_azp(x, "f32")
+    qi = q.view(np.int8).astype(np.int64)
+    for m in range(x.shape[0]):
+        lo, hi = min(0.0, float(x[m].min())), max(0.0, float(x[m].max()))
+        if hi == lo:
+            assert s[m] == np.float32(1.0) and z[m] == -128 and (qi[m] == -128).all()
+            continue
+        assert s[m] == np.float32(np.float32(hi - lo) / np.float32(255.0))
+        assert -128 <= z[m] <= 127
+        if lo < 0:
+            assert qi[m, int(np.argmin(x[m]))] == -128   # the negative extreme is the lowest code
+        else:
+            assert z[m] == -128                           # lo = 0 sits on the lowest code
+        zero = x[m] == 0
+        assert (qi[m][zero] == z[m]).all()                # 0 is exactly representable
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_azp_quant_error_bound(seed):
+    """(q - z) * s is within half a step s of x for every element."""
+    x = _rows(seed, M=8, K=512)
+    q, s, z = oracle.quant_per_token_azp(x, "f32")
+    deq = (q.view(np.int8).astype(np.float64) - z[:, None]) * s[:, None].astype(np.float64)
+    err = np.abs(deq - x.astype(np.float64))
+    assert (err <= 0.5 * s[:, None] * (1 + 2.0 ** -12)).all()
+
+
+def test_azp_quant_bf16_input_matches_f32():
+    x = workloads.activations(5, 272, seed=4)
+    xh = workloads.as_u16(x)
+    q1, s1, z1 = oracle.quant_per_token_azp(xh, "bf16")
+    q2, s2, z2 = oracle.quant_per_token_azp(x.float().numpy(), "f32")
+    assert np.array_equal(q1, q2) and np.array_equal(s1, s2) and np.array_equal(z1, z2)
+
+
+def test_colsum_is_the_row_sum():
+    b = workloads.random_codes((37, 160), "int8", seed=3).numpy()
+    assert np.array_equal(oracle.colsum(b), b.view(np.int8).astype(np.int64).sum(axis=1))
+
+
+def test_scaled_mm_azp_against_python_integers():
+    """I32 output = sum_k (a - z) b exactly; f64 output = that times the
+    scales, within two binary64 roundings; per-tensor and per-token zero
+    points."""
+    rng = np.random.default_rng(5)
+    M, N, K = 3, 5, 48
+    a = workloads.random_codes((M, K), "int8", seed=6).numpy()
+    b = workloads.random_codes((N, K), "int8", seed=7).numpy()
+    ai, bi = a.view(np.int8).astype(int), b.view(np.int8).astype(int)
+    sa = rng.uniform(0.001, 0.1, M).astype(np.float32)
+    sb = rng.uniform(0.001, 0.1, N).astype(np.float32)
+    for z in (np.array([17], np.int32), np.array([-128, 0, 127], np.int32)):
+        acc = oracle.scaled_mm_azp(a, b, None, z, None, "i32")
+        d = oracle.scaled_mm_azp(a, b, sa, z, sb, "f64")
+        for m in range(M):
+            zm = int(z[0] if z.size == 1 else z[m])
+            for n in range(N):
+                exact = sum((int(ai[m, k]) - zm) * int(bi[n, k]) for k in range(K))
+                assert acc[m, n] == exact
+                want = Fraction(exact) * Fraction(float(sa[m])) * Fraction(float(sb[n]))
+                assert abs(Fraction(float(d[m, n])) - want) <= abs(want) * Fraction(1, 2 ** 51)
+
+
+def test_scaled_mm_azp_is_the_dequantised_product():
+    """D = ((a - z) s_a) . (b s_b)^T, numpy float64 matmul as the reference;
+    zero points of 0 reduce to the symmetric product."""
+    x = workloads.activations(4, 256, seed=8)
+    a, sa, z = oracle.quant_per_token_azp(workloads.as_u16(x), "bf16")
+    w = workloads.weights(24, 256, seed=9)
+    b, sb = oracle.quant_per_token(workloads.as_u16(w), "int8", xtype="bf16")
+    d = oracle.scaled_mm_azp(a, b, sa, z, sb, "f64")
+    ref = ((a.view(np.int8).astype(np.float64) - z[:, None]) * sa[:, None]) @ \
+          (b.view(np.int8).astype(np.float64) * sb[:, None]).T
+    assert np.allclose(d, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    sym = oracle.scaled_mm(a, b, "int8", sa, sb, "f64")
+    assert np.array_equal(oracle.scaled_mm_azp(a, b, sa, None, sb, "f64"), sym)
