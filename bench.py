@@ -101,7 +101,15 @@ def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
             x = workloads.activations(M, K, seed=seed + 500, device=dev)
             q = torch.empty((M, K), dtype=code_dtype, device=dev)
             out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            if act_scheme == "per_token":
+            cs = z = None
+            if act_scheme == "azp":  # asymmetric per-token int8, weight code sums offline
+                s = torch.empty(M, dtype=torch.float32, device=dev)
+                z = torch.empty(M, dtype=torch.int32, device=dev)
+                cs = w8.w8a8_colsum(wq)
+                qf = (lambda x=x, q=q, s=s, z=z: w8.w8a8_quant_per_token_azp(x, q=q, scales=s, azp=z))
+                n_sa = M
+                qbytes = 3 * M * K + 8 * M
+            elif act_scheme == "per_token":
                 s = torch.empty(M, dtype=torch.float32, device=dev)
                 qf = (lambda x=x, q=q, s=s: w8.w8a8_quant_per_token(x, qtype, q=q, scales=s))
                 n_sa = M
@@ -116,6 +124,9 @@ def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
                 qbytes = 3 * M * K + 4
             mf = (lambda q=q, wq=wq, s=s, wsc=wsc, out=out:
                   w8.w8a8_scaled_mm(q, wq.t(), s, wsc, torch.bfloat16, out=out, workspace=ws))
+            if act_scheme == "azp":
+                mf = (lambda q=q, wq=wq, s=s, z=z, cs=cs, wsc=wsc, out=out:
+                      w8.w8a8_scaled_mm_azp(q, wq.t(), s, z, cs, wsc, torch.bfloat16, out=out))
             fused = (act_scheme == "per_token"
                      and w8.w8a8_quant_scaled_mm_kernel(M, N, K) == "gemm_dynq_kernel")
             if fused:  # one kernel quantises the token and runs the product
@@ -126,12 +137,14 @@ def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
                                        _gemm_bytes(M, N, K, n_sa, N) + qbytes - M * K,
                                        f"quant+gemm M={M} {name} {N}x{K}", "gemm_dynq_kernel"))
             else:
-                qkern = ("quant_rows_kernel" if act_scheme == "per_token" else "quant_tensor_kernel")
+                qkern = {"per_token": "quant_rows_kernel", "azp": "quant_rows_azp_kernel"}.get(
+                    act_scheme, "quant_tensor_kernel")
                 launches.append(Launch("quant", qf, 0, qbytes, f"quant M={M} {name}", qkern))
-                launches.append(Launch("gemm", mf, 2 * M * N * K, _gemm_bytes(M, N, K, n_sa, N),
+                extra = 4 * M + 4 * N if act_scheme == "azp" else 0  # zero points, code sums
+                launches.append(Launch("gemm", mf, 2 * M * N * K, _gemm_bytes(M, N, K, n_sa, N) + extra,
                                        f"gemm M={M} {name} {N}x{K}",
-                                       w8.w8a8_scaled_mm_kernel(M, N, K, workspace=True)))
-            keep += [wq, wsc, x, q, s, out]
+                                       w8.w8a8_scaled_mm_kernel(M, N, K, workspace=act_scheme != "azp")))
+            keep += [wq, wsc, x, q, s, out] + ([z, cs] if act_scheme == "azp" else [])
     return launches, keep
 
 
@@ -216,6 +229,12 @@ WORKLOADS = {
                       "weights, int32 accumulate, bf16 out",
                  layers=workloads.LLAMA3_70B_LAYERS, Ms=workloads.INT8_70B_M, qtype="int8",
                  act="per_token", cpu_n_frac=1),
+    "int8_azp": dict(desc="int8 w8a8 GEMMs with asymmetric activations, Llama-3-70B unsharded "
+                          "QKV/O/gate_up/down at M=1,64,4096: per-token int8 scale + zero point, "
+                          "per-channel int8 weights with precomputed code sums, zero-point term "
+                          "fused in the epilogue, bf16 out",
+                     layers=workloads.LLAMA3_70B_LAYERS, Ms=workloads.INT8_70B_M, qtype="int8",
+                     act="azp", cpu_n_frac=1),
     "kv": dict(desc="scaled fp8 KV cache: per-tensor dynamic quant + dequant of 32 layers of "
                     "K and V [32768,8,128] bf16, plus per-token fp8 quant of [8192,4096]",
                ),
@@ -363,13 +382,17 @@ def cpu_baseline(spec, launches_meta, budget_s: float):
             w = workloads.as_u16(workloads.weights(Ns, K, seed=8))
             b, sb = oracle.quant_per_token(w, spec["qtype"], xtype="bf16")
             t0 = time.perf_counter()
-            if spec["act"] == "per_token":
-                a, sa = oracle.quant_per_token(x, spec["qtype"], xtype="bf16")
+            if spec["act"] == "azp":
+                a, sa, z = oracle.quant_per_token_azp(x, "bf16")
+                oracle.scaled_mm_azp(a, b, sa, z, sb, "bf16")
             else:
-                a, sa = oracle.quant_per_tensor(x, spec["qtype"], scale=np.float32(0.05),
-                                                xtype="bf16")
-                sa = np.array([sa], np.float32)
-            oracle.scaled_mm(a, b, spec["qtype"], sa, sb, "bf16")
+                if spec["act"] == "per_token":
+                    a, sa = oracle.quant_per_token(x, spec["qtype"], xtype="bf16")
+                else:
+                    a, sa = oracle.quant_per_tensor(x, spec["qtype"], scale=np.float32(0.05),
+                                                    xtype="bf16")
+                    sa = np.array([sa], np.float32)
+                oracle.scaled_mm(a, b, spec["qtype"], sa, sb, "bf16")
             dt += time.perf_counter() - t0
             flops += 2 * Ms * Ns * K
             done += 1

@@ -197,6 +197,47 @@ w8a8_status kv_fp8_scaled_dequant(const uint8_t* q, int64_t n, const float* scal
                                   w8a8_dtype xt, hipStream_t stream);
 
 /*
+ * Asymmetric int8 activations [P1: the asymmetric int8 case brings a few
+ * small operations that are fused onto the GEMM instead of sweeping the
+ * output again; the pages give no formula, the textbook scheme is used].
+ * Per row m of x [M, K] (BF16/FP16/F32, row stride ldx elements):
+ *   lo = min(0, min x), hi = max(0, max x)   (0 is representable),
+ *   s = (hi - lo) / 255 (1.0 for an all-zero row),
+ *   z = clamp(rint(-128 - lo / s), -128, 127),
+ *   q = clamp(rint(x / s) + z, -128, 127),
+ * in binary32 with correctly rounded divisions and round-half-even rint, so
+ * that x ~ (q - z) * s. Writes q [M, ldq] int8 codes, scales [M] and
+ * azp [M] (int32), all device memory. Same layout rules as
+ * w8a8_quant_per_token.
+ */
+w8a8_status w8a8_quant_per_token_azp(const void* x, w8a8_dtype xt, int64_t M, int64_t K, int64_t ldx,
+                                     void* q, int64_t ldq, float* scales, int32_t* azp,
+                                     hipStream_t stream);
+
+/*
+ * colsum[n] = sum_k b[n, k] over int8 weight codes b [N, K] (row stride ldb
+ * bytes; the K x N column-major B of the product), int32, device. Computed
+ * once per weight. K and ldb multiples of 16, b 16-byte aligned.
+ */
+w8a8_status w8a8_colsum(const void* b, int64_t ldb, int64_t N, int64_t K, int32_t* colsum,
+                        hipStream_t stream);
+
+/*
+ * The int8 scaled product with activation zero points:
+ *   D[m, n] = a_scale[m or 0] * b_scale[n or 0] * sum_k (A[m, k] - z) B[k, n]
+ * with z = azp[m] (n_azp == M) or azp[0] (n_azp == 1), computed as
+ * acc - z * colsum[n] in the epilogue of the int8 kernels. Arguments and
+ * rules as w8a8_scaled_mm with qt = INT8; I32 output stores the corrected
+ * accumulator. azp == NULL gives the symmetric product. With zero points K
+ * is limited to 65536 (the corrected int32 sum stays exact).
+ */
+w8a8_status w8a8_scaled_mm_azp(void* out, w8a8_dtype ot, int64_t ldo, const void* a, int64_t lda,
+                               const void* b, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                               const float* a_scales, int64_t n_a, const int32_t* azp, int64_t n_azp,
+                               const int32_t* colsum, const float* b_scales, int64_t n_b,
+                               hipStream_t stream);
+
+/*
  * Merged layers [P2: the loader must handle merged QKV / gate_up layers
  * whose shards carry their own weight scales; a review comment on the same
  * page proposes one shared scale]. A merged weight stacks S shards along N:

@@ -57,6 +57,10 @@ SIGNATURES = {
                              _P, _I64, _P, _P],
     "kv_fp8_scaled_quant": [_P, _I, _I64, _P, _P, _I, _P],
     "kv_fp8_scaled_dequant": [_P, _I64, _P, _P, _I, _P],
+    "w8a8_quant_per_token_azp": [_P, _I, _I64, _I64, _I64, _P, _I64, _P, _P, _P],
+    "w8a8_colsum": [_P, _I64, _I64, _I64, _P, _P],
+    "w8a8_scaled_mm_azp": [_P, _I, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64,
+                           _P, _P, _I64, _P],
     "w8a8_expand_shard_scales": [_P, _P, _I64, _P, _P],
     "w8a8_requant_shared_scale": [_P, _I64, _I, _I64, _P, _I64, _P, _P, _I64, _P, _P],
 }
@@ -211,6 +215,70 @@ def kv_fp8_scaled_dequant(q: torch.Tensor, scale: torch.Tensor | None,
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     _call("kv_fp8_scaled_dequant", _ptr(q), q.numel(), _ptr(scale), _ptr(out),
           _dtype(out.dtype), _stream(q))
+    return out
+
+
+# ------------------------------------------------------- asymmetric int8 (azp)
+def w8a8_quant_per_token_azp(x: torch.Tensor, q: torch.Tensor | None = None,
+                             scales: torch.Tensor | None = None, azp: torch.Tensor | None = None):
+    """Asymmetric per-token int8 quantisation of x [M, K] -> (codes int8
+    [M, K], scales fp32 [M], zero points int32 [M]), x ~ (q - z) * s."""
+    _check_cuda(x, q, scales, azp)
+    M, K, ldx = _rows(x, "x")
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty(M, dtype=torch.float32, device=x.device)
+    if azp is None:
+        azp = torch.empty(M, dtype=torch.int32, device=x.device)
+    _, _, ldq = _rows(q, "q")
+    _call("w8a8_quant_per_token_azp", _ptr(x), _dtype(x.dtype), M, K, ldx, _ptr(q), ldq,
+          _ptr(scales), _ptr(azp), _stream(x))
+    return q, scales, azp
+
+
+def w8a8_colsum(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Per-row sums of int8 weight codes w [N, K] (int32 [N])."""
+    _check_cuda(w, out)
+    if w.dtype != torch.int8:
+        raise ValueError("w8a8_colsum takes int8 codes")
+    N, K, ldw = _rows(w, "w")
+    if out is None:
+        out = torch.empty(N, dtype=torch.int32, device=w.device)
+    _call("w8a8_colsum", _ptr(w), ldw, N, K, _ptr(out), _stream(w))
+    return out
+
+
+def w8a8_scaled_mm_azp(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | None,
+                       azp: torch.Tensor | None, colsum: torch.Tensor | None,
+                       b_scales: torch.Tensor | None, out_dtype=torch.bfloat16,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """D = a_scales (x) b_scales * ((a - azp) @ b) for int8 codes; b and the
+    scales as in w8a8_scaled_mm, azp int32 [1] or [M], colsum =
+    w8a8_colsum(weight) for b = weight.t()."""
+    _check_cuda(a, b, a_scales, azp, colsum, b_scales, out)
+    if a.dtype != torch.int8 or b.dtype != torch.int8:
+        raise ValueError("w8a8_scaled_mm_azp takes int8 codes")
+    M, K, lda = _rows(a, "a")
+    if b.dim() != 2 or b.size(0) != K:
+        raise ValueError(f"b must be K x N with K={K}, got shape {tuple(b.shape)}")
+    N = b.size(1)
+    if b.size(0) > 1 and b.stride(0) != 1:
+        raise ValueError("b must be column-major (K x N with stride(0) == 1), e.g. weight.t()")
+    ldb = b.stride(1) if N > 1 else max(K, b.stride(1))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _, _, ldo = _rows(out, "out")
+    sa = None if a_scales is None else a_scales.reshape(-1)
+    sb = None if b_scales is None else b_scales.reshape(-1)
+    z = None if azp is None else azp.reshape(-1)
+    for t, what, dt in ((sa, "a_scales", torch.float32), (sb, "b_scales", torch.float32),
+                        (z, "azp", torch.int32), (colsum, "colsum", torch.int32)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous()):
+            raise ValueError(f"{what} must be a contiguous {dt} tensor")
+    _call("w8a8_scaled_mm_azp", _ptr(out), _dtype(out.dtype), ldo, _ptr(a), lda, _ptr(b), ldb,
+          M, N, K, _ptr(sa), 0 if sa is None else sa.numel(), _ptr(z), 0 if z is None else z.numel(),
+          _ptr(colsum), _ptr(sb), 0 if sb is None else sb.numel(), _stream(a))
     return out
 
 
@@ -381,4 +449,5 @@ __all__ = ["w8a8_quant_per_token", "w8a8_quant_per_tensor", "w8a8_scaled_mm",
            "w8a8_scaled_mm_kernel", "w8a8_scaled_mm_workspace_size", "w8a8_quant_scaled_mm", "w8a8_quant_scaled_mm_kernel",
            "kv_fp8_scaled_quant", "kv_fp8_scaled_dequant", "scaled_mm", "W8A8Error",
            "w8a8_expand_shard_scales", "w8a8_requant_shared_scale",
+           "w8a8_quant_per_token_azp", "w8a8_colsum", "w8a8_scaled_mm_azp",
            "load_library", "version", "LIB_PATH", "SIGNATURES"]

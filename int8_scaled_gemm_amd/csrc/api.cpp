@@ -284,6 +284,62 @@ w8a8_status kv_fp8_scaled_dequant(const uint8_t* q, int64_t n, const float* scal
     return from_hip(w8a8::launch_kv_dequant(q, n, scale, x, xt, stream), fn);
 }
 
+w8a8_status w8a8_quant_per_token_azp(const void* x, w8a8_dtype xt, int64_t M, int64_t K, int64_t ldx,
+                                     void* q, int64_t ldq, float* scales, int32_t* azp,
+                                     hipStream_t stream) {
+    const char* fn = "w8a8_quant_per_token_azp";
+    w8a8_status s = check_quant_io(fn, x, xt, M, K, ldx, q, W8A8_Q_INT8, ldq);
+    if (s != W8A8_OK || M == 0) return s;
+    if (!scales || !azp) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL scales or azp", fn);
+    if ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(azp)) & 3u)
+        return fail(W8A8_ERR_ALIGNMENT, "%s: scales and azp must be 4-byte aligned", fn);
+    return from_hip(w8a8::launch_quant_per_token_azp(xt, x, M, K, ldx, static_cast<uint8_t*>(q), ldq,
+                                                     scales, azp, stream),
+                    fn);
+}
+
+w8a8_status w8a8_colsum(const void* b, int64_t ldb, int64_t N, int64_t K, int32_t* colsum,
+                        hipStream_t stream) {
+    const char* fn = "w8a8_colsum";
+    if (N < 0 || K < 0) return fail(W8A8_ERR_SHAPE, "%s: negative size N=%lld K=%lld", fn, (long long)N, (long long)K);
+    if (N > kMaxDim || K > kMaxDim) return fail(W8A8_ERR_UNSUPPORTED, "%s: N or K above 2^31-1", fn);
+    if (ldb < K) return fail(W8A8_ERR_LAYOUT, "%s: ldb=%lld < K=%lld", fn, (long long)ldb, (long long)K);
+    if (K % 16 || ldb % 16) return fail(W8A8_ERR_ALIGNMENT, "%s: K and ldb must be multiples of 16", fn);
+    if (N == 0) return ok();
+    if (!colsum) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL colsum", fn);
+    if (reinterpret_cast<uintptr_t>(colsum) & 3u) return fail(W8A8_ERR_ALIGNMENT, "%s: colsum must be 4-byte aligned", fn);
+    if (K > 0 && !b) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL b", fn);
+    if (b && !aligned16(b)) return fail(W8A8_ERR_ALIGNMENT, "%s: b must be 16-byte aligned", fn);
+    return from_hip(w8a8::launch_colsum(static_cast<const uint8_t*>(b), ldb, N, K, colsum, stream), fn);
+}
+
+w8a8_status w8a8_scaled_mm_azp(void* out, w8a8_dtype ot, int64_t ldo, const void* a, int64_t lda,
+                               const void* b, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                               const float* a_scales, int64_t n_a, const int32_t* azp, int64_t n_azp,
+                               const int32_t* colsum, const float* b_scales, int64_t n_b,
+                               hipStream_t stream) {
+    const char* fn = "w8a8_scaled_mm_azp";
+    w8a8_status s = scaled_mm_check(fn, out, ot, ldo, a, lda, b, ldb, W8A8_Q_INT8, M, N, K, a_scales,
+                                    n_a, b_scales, n_b);
+    if (s != W8A8_OK) return s;
+    if (azp) {
+        if (n_azp != 1 && n_azp != M)
+            return fail(W8A8_ERR_SHAPE, "%s: azp has %lld entries; need 1 (per tensor) or M=%lld (per token)", fn, (long long)n_azp, (long long)M);
+        if (!colsum) return fail(W8A8_ERR_INVALID_ARG, "%s: zero points need the weights' colsum", fn);
+        if ((reinterpret_cast<uintptr_t>(azp) | reinterpret_cast<uintptr_t>(colsum)) & 3u)
+            return fail(W8A8_ERR_ALIGNMENT, "%s: azp and colsum must be 4-byte aligned", fn);
+        if (K > 65536)
+            return fail(W8A8_ERR_UNSUPPORTED, "%s: K=%lld; with zero points the int32 accumulator holds K <= 65536", fn, (long long)K);
+    }
+    if (M == 0 || N == 0) return s;
+    w8a8::GemmProblem p = make_problem(out, ot, ldo, a, lda, b, ldb, W8A8_Q_INT8, M, N, K, a_scales,
+                                       n_a, b_scales, n_b);
+    p.azp = azp;
+    p.azp_per_row = azp && n_azp == M && M != 1;
+    p.colsum = azp ? colsum : nullptr;
+    return from_hip(w8a8::launch_scaled_mm(p, stream), fn);
+}
+
 static w8a8_status check_shards(const char* fn, const int64_t* rows, int64_t S, int64_t* N) {
     if (S < 1) return fail(W8A8_ERR_SHAPE, "%s: num_shards=%lld must be >= 1", fn, (long long)S);
     if (S > W8A8_MAX_SHARDS)

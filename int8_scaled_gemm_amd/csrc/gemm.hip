@@ -47,6 +47,11 @@ struct GemmArgs {
     // [splits][M][N] to part; a second kernel adds them
     void* part;
     int splits, stages_per_split;
+    // asymmetric int8 activations: zero points (1 or M entries) and the
+    // weights' code sums; NULL azp: symmetric
+    const int32_t* azp;
+    int azp_per_row;
+    const int32_t* colsum;
 };
 
 template <int QT>
@@ -85,8 +90,20 @@ __device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
 }
 
 // Scale, round and store one accumulator element (bounds already checked).
+// Asymmetric int8 activations: the accumulator of (a - z) . b is
+// acc - z[m] * colsum[n], exact in int32 while K <= 65536 (|a - z| <= 255).
+// Float accumulators (fp8) have no zero points.
+template <typename T>
+__device__ __forceinline__ T azp_fix(const GemmArgs& p, int m, int n, T acc) {
+    if constexpr (std::is_integral<T>::value) {
+        if (p.azp) return acc - p.azp[p.azp_per_row ? m : 0] * p.colsum[n];
+    }
+    return acc;
+}
+
 template <int OT, typename T>
 __device__ __forceinline__ void store_out(const GemmArgs& p, int m, int n, T acc) {
+    acc = azp_fix(p, m, n, acc);
     if constexpr (OT == D_I32) {
         static_cast<int32_t*>(p.out)[static_cast<int64_t>(m) * p.ldo + n] = static_cast<int32_t>(acc);
     } else {
@@ -204,15 +221,19 @@ template <int OT, typename Acc>
 __device__ __forceinline__ void store4(const GemmArgs& p, int m, int n, const Acc& acc, int base,
                                        bool vec) {
     if (m >= p.M) return;
+    typedef typename std::remove_cv<typename std::remove_reference<decltype(acc[0])>::type>::type E;
+    E v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = azp_fix(p, m, min(n + r, p.N - 1), static_cast<E>(acc[base + r]));
     if constexpr (OT == D_I32) {
         int32_t* o = static_cast<int32_t*>(p.out) + static_cast<int64_t>(m) * p.ldo + n;
         if (vec && n + 3 < p.N) {
             *reinterpret_cast<i32x4*>(o) =
-                i32x4{static_cast<int>(acc[base]), static_cast<int>(acc[base + 1]),
-                      static_cast<int>(acc[base + 2]), static_cast<int>(acc[base + 3])};
+                i32x4{static_cast<int>(v[0]), static_cast<int>(v[1]),
+                      static_cast<int>(v[2]), static_cast<int>(v[3])};
         } else {
             for (int r = 0; r < 4; ++r)
-                if (n + r < p.N) o[r] = static_cast<int32_t>(acc[base + r]);
+                if (n + r < p.N) o[r] = static_cast<int32_t>(v[r]);
         }
     } else {
         const float sa = p.sa ? p.sa[p.sa_per_row ? m : 0] : 1.0f;
@@ -220,7 +241,7 @@ __device__ __forceinline__ void store4(const GemmArgs& p, int m, int n, const Ac
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float sb = p.sb ? p.sb[p.sb_per_col ? min(n + r, p.N - 1) : 0] : 1.0f;
-            d[r] = static_cast<float>(acc[base + r]) * sa * sb;
+            d[r] = static_cast<float>(v[r]) * sa * sb;
         }
         const int64_t o = static_cast<int64_t>(m) * p.ldo + n;
         if constexpr (OT == D_F32) {
@@ -394,8 +415,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
                     uint16_t h[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float sb = p.sb ? p.sb[p.sb_per_col ? min(n0 + col + r, p.N - 1) : 0] : 1.0f;
-                        const float d = static_cast<float>(acc[i][j][4 * q + r]) * sa * sb;
+                        const int n = min(n0 + col + r, p.N - 1);  // columns past N are never stored
+                        const float sb = p.sb ? p.sb[p.sb_per_col ? n : 0] : 1.0f;
+                        const float d = static_cast<float>(azp_fix(p, m, n, acc[i][j][4 * q + r])) * sa * sb;
                         h[r] = (OT == D_BF16) ? to_bf16_bits(d) : to_fp16_bits(d);
                     }
                     const int slot = (col >> 3) ^ (row % kChunks);
@@ -878,6 +900,9 @@ hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st) {
     a.part = nullptr;
     a.splits = 1;
     a.stages_per_split = 0;
+    a.azp = p.azp;
+    a.azp_per_row = p.azp_per_row ? 1 : 0;
+    a.colsum = p.colsum;
     if (p.workspace) {
         const SplitPlan d = plan_splitk(p.M, p.N, p.K);
         if (d.splits > 1 && p.workspace_bytes >= d.workspace_bytes) {
@@ -928,6 +953,9 @@ hipError_t launch_quant_scaled_mm(const GemmProblem& p, int xt, const void* x, i
     a.tiles_m = a.tiles_n = 0;
     a.vec_out = 0;
     a.vec_row = 0;
+    a.azp = nullptr;
+    a.azp_per_row = 0;
+    a.colsum = nullptr;
     a.part = nullptr;
     a.splits = 1;
     a.stages_per_split = 0;

@@ -17,6 +17,14 @@ hipError_t launch_quant_per_tensor(int xt, const void* x, int64_t M, int64_t K, 
 hipError_t launch_kv_dequant(const uint8_t* q, int64_t n, const float* scale, void* x, int xt,
                              hipStream_t st);
 
+// Asymmetric int8 per-token quantisation (codes, scales, zero points) and
+// the per-row code sums of int8 weights.
+hipError_t launch_quant_per_token_azp(int xt, const void* x, int64_t M, int64_t K, int64_t ldx,
+                                      uint8_t* q, int64_t ldq, float* scales, int32_t* azp,
+                                      hipStream_t st);
+hipError_t launch_colsum(const uint8_t* b, int64_t ldb, int64_t N, int64_t K, int32_t* colsum,
+                         hipStream_t st);
+
 // Merged layers: the most shards one call takes (their row ends travel as
 // kernel arguments).
 constexpr int kMaxShards = 64;
@@ -47,6 +55,10 @@ struct GemmProblem {
     bool sb_per_col;
     void* workspace = nullptr;    // optional: room for split-K partial sums
     int64_t workspace_bytes = 0;
+    // asymmetric int8: zero points (1 or M entries) and the weights' code sums
+    const int32_t* azp = nullptr;
+    bool azp_per_row = false;
+    const int32_t* colsum = nullptr;
 };
 
 // How a decode problem splits K when given a workspace (splits == 1: no split).

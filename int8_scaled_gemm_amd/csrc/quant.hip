@@ -405,6 +405,106 @@ hipError_t launch_quant_per_tensor(int xt, const void* x, int64_t M, int64_t K, 
 }
 
 // ------------------------------------------------------------------------
+// Asymmetric int8 activations [P1: the asymmetric int8 case and its small
+// fused operations; the scheme itself is the textbook one]. One workgroup
+// per row: a read pass for the row's range with 0 included, then a
+// quantising pass over the row again (from L2).
+//   s = (hi - lo) / 255 (1.0 for an all-zero row), z = rint(-128 - lo / s)
+//   clamped to [-128, 127], q = clamp(rint(x / s) + z, -128, 127),
+// every division correctly rounded in binary32 and every rint half-to-even.
+// ------------------------------------------------------------------------
+template <int XT>
+__global__ __launch_bounds__(kBlock) void quant_rows_azp_kernel(const void* __restrict__ x, int64_t ldx,
+                                                               uint8_t* __restrict__ q, int64_t ldq,
+                                                               float* __restrict__ scales,
+                                                               int32_t* __restrict__ azp, int64_t K) {
+    __shared__ float part[2][kBlock / 64];
+    const int64_t row = blockIdx.x;
+    float hi = 0.0f, nlo = 0.0f;  // max(x, 0) and max(-x, 0)
+    for (int64_t k = static_cast<int64_t>(threadIdx.x) * 8; k < K; k += kBlock * 8) {
+        float v[8];
+        load8<XT>(x, row * ldx + k, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            hi = fmaxf(hi, v[j]);
+            nlo = fmaxf(nlo, -v[j]);
+        }
+    }
+    hi = wave_max(hi);
+    nlo = wave_max(nlo);
+    if ((threadIdx.x & 63) == 0) {
+        part[0][threadIdx.x >> 6] = hi;
+        part[1][threadIdx.x >> 6] = nlo;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) {
+        hi = fmaxf(hi, part[0][w]);
+        nlo = fmaxf(nlo, part[1][w]);
+    }
+    const float lo = -nlo;
+    const float d = hi - lo;
+    const float s = d == 0.0f ? 1.0f : d / 255.0f;
+    const double r = 1.0 / static_cast<double>(s);
+    const float zf = fminf(fmaxf(__builtin_rintf(-128.0f - div_rn(lo, r)), -128.0f), 127.0f);
+    if (threadIdx.x == 0) {
+        scales[row] = s;
+        azp[row] = static_cast<int32_t>(zf);
+    }
+    for (int64_t k = static_cast<int64_t>(threadIdx.x) * 8; k < K; k += kBlock * 8) {
+        float v[8];
+        load8<XT>(x, row * ldx + k, v);
+        uint32_t w[2] = {0, 0};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float c = fminf(fmaxf(__builtin_rintf(div_rn(v[j], r)) + zf, -128.0f), 127.0f);
+            w[j >> 2] |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xFFu) << (8 * (j & 3));
+        }
+        *reinterpret_cast<u32x2*>(q + row * ldq + k) = u32x2{w[0], w[1]};
+    }
+}
+
+// Per-row sums of int8 weight codes: one wave per row.
+__global__ __launch_bounds__(kBlock) void colsum_kernel(const uint8_t* __restrict__ b, int64_t ldb,
+                                                       int64_t N, int64_t K, int32_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * (kBlock / 64) + (threadIdx.x >> 6);
+    if (row >= N) return;
+    int sum = 0;
+    for (int64_t k = 16 * lane; k < K; k += 1024) {
+        const u32x4 c = *reinterpret_cast<const u32x4*>(b + row * ldb + k);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum += static_cast<int8_t>(c[j] >> (8 * e));
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+    if (lane == 0) out[row] = sum;
+}
+
+hipError_t launch_quant_per_token_azp(int xt, const void* x, int64_t M, int64_t K, int64_t ldx,
+                                      uint8_t* q, int64_t ldq, float* scales, int32_t* azp,
+                                      hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    const dim3 g(static_cast<unsigned>(M)), blk(kBlock);
+    switch (xt) {
+        case D_BF16: hipLaunchKernelGGL((quant_rows_azp_kernel<D_BF16>), g, blk, 0, st, x, ldx, q, ldq, scales, azp, K); break;
+        case D_FP16: hipLaunchKernelGGL((quant_rows_azp_kernel<D_FP16>), g, blk, 0, st, x, ldx, q, ldq, scales, azp, K); break;
+        default: hipLaunchKernelGGL((quant_rows_azp_kernel<D_F32>), g, blk, 0, st, x, ldx, q, ldq, scales, azp, K); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_colsum(const uint8_t* b, int64_t ldb, int64_t N, int64_t K, int32_t* colsum,
+                         hipStream_t st) {
+    if (N == 0) return hipSuccess;
+    hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>((N + kBlock / 64 - 1) / (kBlock / 64))),
+                       dim3(kBlock), 0, st, b, ldb, N, K, colsum);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------
 // Merged layers [P2]: S shards stacked along N (QKV, gate_up), shard i on
 // rows [end[i-1], end[i]) with its own per-tensor weight scale s_i.
 // ------------------------------------------------------------------------

@@ -204,3 +204,28 @@ def test_merged_layer_validation(lib):
     assert rq(None, 128, 1, 128, r, 2, FAKE, FAKE, 128, FAKE, None) == INVALID
     assert rq(FAKE, 128, 1, -16, r, 2, FAKE, FAKE, 128, FAKE, None) == SHAPE
     assert rq(FAKE, 128, 1, 128, rows(1, -2), 2, FAKE, FAKE, 128, FAKE, None) == SHAPE
+
+
+def test_azp_validation(lib):
+    """Asymmetric int8 calls: host-side checks."""
+    qa = lib.w8a8_quant_per_token_azp
+    assert qa(FAKE, 0, 4, 128, 128, FAKE, 128, FAKE, None, None) == INVALID   # azp is an output
+    assert qa(FAKE, 5, 4, 128, 128, FAKE, 128, FAKE, FAKE, None) == DTYPE
+    assert qa(FAKE, 0, 4, 100, 112, FAKE, 112, FAKE, FAKE, None) == ALIGN
+    assert qa(None, 0, 0, 128, 128, None, 128, None, None, None) == OK
+    cs = lib.w8a8_colsum
+    assert cs(FAKE, 64, 8, 128, FAKE, None) == LAYOUT
+    assert cs(FAKE, 136, 8, 120, FAKE, None) == ALIGN
+    assert cs(FAKE, 128, 8, 128, None, None) == INVALID
+    assert cs(None, 128, 0, 128, None, None) == OK
+    mz = lib.w8a8_scaled_mm_azp
+
+    def f(out=FAKE, ot=0, ldo=64, a=FAKE, lda=128, b=FAKE, ldb=128, M=16, N=64, K=128, sa=None,
+          n_a=1, z=FAKE, n_z=1, cs=FAKE, sb=None, n_b=1):
+        return mz(out, ot, ldo, a, lda, b, ldb, M, N, K, sa, n_a, z, n_z, cs, sb, n_b, None)
+    assert f(n_z=3) == SHAPE                      # neither 1 nor M
+    assert f(cs=None) == INVALID                  # zero points need the code sums
+    assert f(z=FAKE + 2) == ALIGN
+    assert f(K=65552, lda=65552, ldb=65552) == UNSUP
+    assert f(ldb=64) == LAYOUT
+    assert f(M=0, out=None, a=None, b=None) == OK
