@@ -28,12 +28,12 @@ constexpr int kBlock = 256;
 // TPR threads share one row (64: one wavefront, 256: the whole block); each
 // thread holds VPT vectors of 8 elements. One HBM read, one HBM write.
 // ------------------------------------------------------------------------
-template <int XT, int QT, int TPR, int VPT>
-__global__ __launch_bounds__(kBlock) void quant_rows_kernel(const void* __restrict__ x, int64_t ldx,
+template <int XT, int QT, int TPR, int VPT, int BS = kBlock>
+__global__ __launch_bounds__(BS) void quant_rows_kernel(const void* __restrict__ x, int64_t ldx,
                                                             uint8_t* __restrict__ q, int64_t ldq,
                                                             float* __restrict__ scales, int64_t M,
                                                             int64_t K) {
-    constexpr int RPB = kBlock / TPR;
+    constexpr int RPB = BS / TPR;
     const int t = threadIdx.x % TPR;
     const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
     const bool active = row < M;
@@ -54,11 +54,11 @@ __global__ __launch_bounds__(kBlock) void quant_rows_kernel(const void* __restri
     }
     amax = wave_max(amax);
     if constexpr (TPR > 64) {
-        __shared__ float part[kBlock / 64];
+        __shared__ float part[BS / 64];
         if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
         __syncthreads();
 #pragma unroll
-        for (int w = 0; w < kBlock / 64; ++w) amax = fmaxf(amax, part[w]);
+        for (int w = 0; w < BS / 64; ++w) amax = fmaxf(amax, part[w]);
     }
     if (!active) return;
 
@@ -320,7 +320,22 @@ hipError_t per_token_typed(const void* x, int64_t M, int64_t K, int64_t ldx, uin
                            int64_t ldq, float* scales, hipStream_t st) {
     // Fit the row in registers when possible: one wave per row up to 8192
     // elements, one 256-lane block per row up to 32768, else two passes.
-    if (K <= 8192) {
+    // Few rows (decode batches): a whole block per row at every K, so that
+    // each lane's share of the row, and with it the serial load -> divide ->
+    // store chain that bounds these small launches, is four times shorter.
+    if (M <= 256 && K <= 32768) {
+        const int g = static_cast<int>(M);
+        if (K <= 2048)
+            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 256, 1>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
+        else if (K <= 4096)
+            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 256, 2>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
+        else if (K <= 8192)
+            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 256, 4>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
+        else if (K <= 16384)  // 1024 lanes per row: two 8-element groups each
+            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 1024, 2, 1024>), dim3(g), dim3(1024), 0, st, x, ldx, q, ldq, scales, M, K);
+        else
+            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 1024, 4, 1024>), dim3(g), dim3(1024), 0, st, x, ldx, q, ldq, scales, M, K);
+    } else if (K <= 8192) {
         const int g = static_cast<int>((M + 3) / 4);
         if (K <= 1024)
             hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 64, 2>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
