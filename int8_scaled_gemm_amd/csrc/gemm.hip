@@ -402,11 +402,35 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
         static_assert(BM * BN * 2 <= 2 * kStage, "the output tile fits the LDS ring");
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __syncthreads();  // every wave is done reading the ring
+        // The lane's scales, loaded once: its TM row scales and its TN x 16
+        // column scales (rows and columns past the matrix are clamped; they
+        // are never stored).
+        float sav[TM], sbv[TN][16];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sav[i] = 1.0f;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sbv[j][e] = 1.0f;
+        if (p.sa) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                sav[i] = p.sa[p.sa_per_row ? min(m0 + wm * WM + i * 32 + (lane & 31), p.M - 1) : 0];
+        }
+        if (p.sb) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int col = wn * WN + j * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    sbv[j][e] = p.sb[p.sb_per_col ? min(n0 + col, p.N - 1) : 0];
+                }
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int row = wm * WM + i * 32 + (lane & 31);
             const int m = min(m0 + row, p.M - 1);  // rows past M are never stored
-            const float sa = p.sa ? p.sa[p.sa_per_row ? m : 0] : 1.0f;
+            const float sa = sav[i];
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -416,7 +440,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int n = min(n0 + col + r, p.N - 1);  // columns past N are never stored
-                        const float sb = p.sb ? p.sb[p.sb_per_col ? n : 0] : 1.0f;
+                        const float sb = sbv[j][4 * q + r];
                         const float d = static_cast<float>(azp_fix(p, m, n, acc[i][j][4 * q + r])) * sa * sb;
                         h[r] = (OT == D_BF16) ? to_bf16_bits(d) : to_fp16_bits(d);
                     }
