@@ -426,30 +426,56 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
                     sbv[j][e] = p.sb[p.sb_per_col ? min(n0 + col, p.N - 1) : 0];
                 }
         }
+        // asymmetric int8: the lane's zero points and column code sums, also loaded once
+        int zv[TM], csv[TN][16];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int row = wm * WM + i * 32 + (lane & 31);
-            const int m = min(m0 + row, p.M - 1);  // rows past M are never stored
-            const float sa = sav[i];
+        for (int i = 0; i < TM; ++i) zv[i] = 0;
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
-                    uint16_t h[4];
+            for (int e = 0; e < 16; ++e) csv[j][e] = 0;
+        if constexpr (QT == Q_INT8) {
+            if (p.azp) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int n = min(n0 + col + r, p.N - 1);  // columns past N are never stored
-                        const float sb = sbv[j][4 * q + r];
-                        const float d = static_cast<float>(azp_fix(p, m, n, acc[i][j][4 * q + r])) * sa * sb;
-                        h[r] = (OT == D_BF16) ? to_bf16_bits(d) : to_fp16_bits(d);
+                for (int i = 0; i < TM; ++i)
+                    zv[i] = p.azp[p.azp_per_row ? min(m0 + wm * WM + i * 32 + (lane & 31), p.M - 1) : 0];
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int col = wn * WN + j * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                        csv[j][e] = p.colsum[min(n0 + col, p.N - 1)];
                     }
-                    const int slot = (col >> 3) ^ (row % kChunks);
-                    *reinterpret_cast<u32x2*>(smem + row * (BN * 2) + slot * 16 + (col & 7) * 2) =
-                        u32x2{h[0] | (static_cast<uint32_t>(h[1]) << 16),
-                              h[2] | (static_cast<uint32_t>(h[3]) << 16)};
-                }
+            }
         }
+        // The tile into LDS; the zero-point term is compiled in only where used.
+        auto write_tile = [&](auto with_azp) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * WM + i * 32 + (lane & 31);
+                const float sa = sav[i];
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+                        uint16_t h[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            auto a = acc[i][j][4 * q + r];
+                            if constexpr (decltype(with_azp)::value) a -= zv[i] * csv[j][4 * q + r];
+                            const float d = static_cast<float>(a) * sa * sbv[j][4 * q + r];
+                            h[r] = (OT == D_BF16) ? to_bf16_bits(d) : to_fp16_bits(d);
+                        }
+                        const int slot = (col >> 3) ^ (row % kChunks);
+                        *reinterpret_cast<u32x2*>(smem + row * (BN * 2) + slot * 16 + (col & 7) * 2) =
+                            u32x2{h[0] | (static_cast<uint32_t>(h[1]) << 16),
+                                  h[2] | (static_cast<uint32_t>(h[3]) << 16)};
+                    }
+            }
+        };
+        if (QT == Q_INT8 && p.azp) write_tile(std::true_type{});
+        else write_tile(std::false_type{});
         __syncthreads();
         const bool vec = p.vec_row;
 #pragma unroll 4
