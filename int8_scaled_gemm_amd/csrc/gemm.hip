@@ -527,6 +527,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------
 constexpr int kNonTemporal = 2;  // cache-policy operand of the buffer load: nt
 
+// Wait until at most `pending` (<= P) stages of L loads each are still in
+// flight; loads retire in issue order.
+template <int P, int L>
+__device__ __forceinline__ void wait_stages(int pending) {
+    if constexpr (P == 0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+        if (pending >= P) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(P * L) : "memory");
+        else wait_stages<P - 1, L>(pending);
+    }
+}
+
 template <int QT, int OT, int CB, int MT, int CH, int ST>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
     typedef typename AccOf<QT>::type Acc;
@@ -535,16 +547,17 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
     constexpr int WL = CB * CH / 4096, AL = AROWS * CH / 4096;  // loads per wave per stage
     constexpr int LPW = WL + AL;
     constexpr int SL = CH / kBK;  // 128-byte K slices per stage
-    static_assert(CB == 16 || CB == 64, "columns per workgroup");
+    constexpr int NCG = CB / 16, WPG = 4 / NCG;  // 16-column groups; waves per group
+    static_assert(CB == 16 || CB == 32 || CB == 64, "columns per workgroup");
     static_assert(CH % 256 == 0 && WL >= 1 && AL >= 1, "stage shape");
-    static_assert(CB == 64 || SL % 4 == 0, "slices per wave");
+    static_assert(SL % WPG == 0, "slices per wave");
     static_assert(ST >= 2 && LPW * (ST - 2) <= 63, "loads in flight");
     static_assert(ST * STAGE >= 4 * MT * 64 * 16, "room for the wave reduction");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * STAGE];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int S = (CB == 64 && p.splits > 1) ? p.splits : 1;
+    const int S = p.splits > 1 ? p.splits : 1;
     const int sp = blockIdx.x % S;
     const int n0 = (blockIdx.x / S) * CB;
     const int nst_all = (p.K + CH - 1) / CH;
@@ -595,21 +608,15 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
     const int g = lane >> 4, r16 = lane & 15;
     for (int st = 0; st < nst; ++st) {
         // Wait for this stage's loads; later stages' loads stay in flight.
-        const int pending = min(nst - 1 - st, ST - 2);
-        if (ST >= 4 && pending >= 2)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW) : "memory");
-        else if (ST >= 3 && pending >= 1)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_stages<ST - 2, LPW>(min(nst - 1 - st, ST - 2));
         __syncthreads();  // every wave's loads of this stage have landed
         if (st + ST - 1 < nst) issue(st + ST - 1, (st + ST - 1) % ST);  // slot freed last step
         const uint8_t* wb = smem + (st % ST) * STAGE;
         const uint8_t* ab = wb + CB * CH;
-        const uint8_t* wrow = wb + ((CB == 64 ? 16 * wave : 0) + r16) * CH;
+        const uint8_t* wrow = wb + (16 * (wave / WPG) + r16) * CH;
 #pragma unroll
-        for (int uu = 0; uu < (CB == 64 ? SL : SL / 4); ++uu) {
-            const int u = CB == 64 ? uu : 4 * uu + wave;
+        for (int uu = 0; uu < SL / WPG; ++uu) {
+            const int u = WPG * uu + wave % WPG;
             // lane's fragment: K bytes 32g .. 32g+31 of slice u (chunks 8u+2g, 8u+2g+1)
             const int c0 = (8 * u + 2 * g) ^ r16, c1 = (8 * u + 2 * g + 1) ^ r16;
             const i32x8 wf = join(*reinterpret_cast<const u32x4*>(wrow + 16 * c0),
@@ -626,38 +633,40 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
     }
 
     // In a 16 x 16 tile lane l holds rows 4 (l / 16) + r, r < 4, of column l % 16.
-    if constexpr (CB == 64) {
-        typedef typename std::conditional<QT == Q_FP8, float, int32_t>::type Part;
-        Part* part = static_cast<Part*>(p.part) + static_cast<int64_t>(sp) * p.M * p.N;
+    // Each result goes out scaled (no split) or as a plain partial sum of this
+    // workgroup's K range (split K).
+    typedef typename std::conditional<QT == Q_FP8, float, int32_t>::type Part;
+    Part* part = static_cast<Part*>(p.part) + static_cast<int64_t>(sp) * p.M * p.N;
+    auto put = [&](int m, int n, auto v) {
+        if (m < p.M && n < p.N) {
+            if (S > 1) part[static_cast<int64_t>(m) * p.N + n] = static_cast<Part>(v);
+            else store_out<OT>(p, m, n, v);
+        }
+    };
+    if constexpr (WPG == 1) {
         const int n = n0 + 16 * wave + r16;
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             if (i >= mt) break;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = 16 * i + 4 * g + r;
-                if (m < p.M && n < p.N) {
-                    if (S > 1) part[static_cast<int64_t>(m) * p.N + n] = static_cast<Part>(acc[i][r]);
-                    else store_out<OT>(p, m, n, acc[i][r]);
-                }
-            }
+            for (int r = 0; r < 4; ++r) put(16 * i + 4 * g + r, n, acc[i][r]);
         }
     } else {
-        __syncthreads();  // the ring is free: reuse it for the four waves' sums
+        // The WPG waves of a column group hold sums over disjoint K slices:
+        // added through LDS in wave order, a fixed order.
+        __syncthreads();  // the ring is free
         Acc* red = reinterpret_cast<Acc*>(smem);
 #pragma unroll
         for (int i = 0; i < MT; ++i) red[(wave * MT + i) * 64 + lane] = acc[i];
         __syncthreads();
-        const int n = n0 + r16;
-        for (int i = wave; i < mt; i += 4) {
-            Acc s = red[i * 64 + lane];
+        const int cg = wave / WPG, first = cg * WPG;
+        const int n = n0 + 16 * cg + r16;
+        for (int i = wave % WPG; i < mt; i += WPG) {
+            Acc sum = red[(first * MT + i) * 64 + lane];
 #pragma unroll
-            for (int w = 1; w < 4; ++w) s += red[(w * MT + i) * 64 + lane];
+            for (int w = 1; w < WPG; ++w) sum += red[((first + w) * MT + i) * 64 + lane];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = 16 * i + 4 * g + r;
-                if (m < p.M && n < p.N) store_out<OT>(p, m, n, s[r]);
-            }
+            for (int r = 0; r < 4; ++r) put(16 * i + 4 * g + r, n, sum[r]);
         }
     }
 }
@@ -825,7 +834,7 @@ hipError_t run_tile(GemmArgs a, hipStream_t st) {
 
 template <int QT, int OT, int CB, int MT, int CH, int ST>
 hipError_t run_decode(const GemmArgs& a, hipStream_t st) {
-    const int S = (CB == 64 && a.splits > 1) ? a.splits : 1;
+    const int S = a.splits > 1 ? a.splits : 1;
     const int grid = (a.N + CB - 1) / CB * S;
     hipLaunchKernelGGL((gemm_decode_kernel<QT, OT, CB, MT, CH, ST>), dim3(grid), dim3(256), 0, st, a);
     if (S > 1) {
@@ -870,9 +879,13 @@ Config select_config(int64_t M, int64_t N, int64_t K) {
         if (long_k_16(N, K)) return M <= 16 ? kDecode16x16L : kDecode16x64L;
         return M <= 16 ? kDecode16x16 : kDecode16x64;
     }
-    // The largest tile that still gives every CU a block, else the smallest.
+    // The largest tile that still gives every CU a block, else the smallest;
+    // 256 x 256 already from 192 tiles (three quarters of the CUs), where
+    // one round of the large tile beats two of the half-size one (measured
+    // on MI355X: 2048 x 6144 x 4096 52 us against 64, 512 x 28672 x 4096 58
+    // against 70).
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (tiles(256, 256) >= 256) return kTile256x256;
+    if (tiles(256, 256) >= 192) return kTile256x256;
     if (tiles(256, 128) >= 256) return kTile256x128;
     if (tiles(128, 128) >= 256) return kTile128x128;
     return kTile64x64;
