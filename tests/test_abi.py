@@ -132,6 +132,11 @@ def test_kernel_configuration_names(lib):
     assert name(8192, 28672, 4096) == "gemm_tile_kernel<256x256>"
     assert name(2048, 4096, 4096) == "gemm_tile_kernel<256x128>"
     assert name(512, 4096, 4096) == "gemm_tile_kernel<64x64>"
+    # 256 x 256 from 192 tiles: one round of large tiles beats two of 256 x 128
+    assert name(2048, 6144, 4096) == "gemm_tile_kernel<256x256>"   # 8 x 24 = 192 tiles
+    assert name(512, 28672, 4096) == "gemm_tile_kernel<256x256>"   # 2 x 112 = 224 tiles
+    assert name(2048, 5888, 4096) == "gemm_tile_kernel<256x128>"   # 8 x 23 = 184 tiles
+    assert name(1024, 4096, 4096) == "gemm_tile_kernel<128x128>"
     assert name(-1, 4, 4) == ""
 
 
