@@ -21,9 +21,14 @@ their sources on the reference pages are in the C file's header:
   per-shard weight scales, either expanded to per-channel scales or rescaled
   to one shared scale max(s_i) by the ratio s_i / max(s_i).
 
+* "Enable scaled FP8 (e4m3fn) KV cache on ROCm" (the paged-attention kernel
+  reads the fp8 cache with the KV scale): attention of one query token per
+  sequence over the dequantised cache, written in numpy float64 in this file.
+
 Parity pins: every function here is pinned in ``tests/test_oracle_*.py``
 against something other than itself (torch's CPU float8 cast, numpy's
-rounding, exact rational brute force, closed forms). None is unpinned.
+rounding, exact rational brute force, torch's float64 attention, closed
+forms). None is unpinned.
 """
 from __future__ import annotations
 
@@ -343,3 +348,46 @@ def bf16_bits_to_f64(h) -> np.ndarray:
 
 def fp16_bits_to_f64(h) -> np.ndarray:
     return np.asarray(h, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+# ----------------------------------------------------------------- attention
+def decode_attention_fp8kv(q, k_codes, v_codes, seq_starts, k_scale=None, v_scale=None,
+                           sm_scale=None):
+    """Attention of one query token per sequence over an e4m3fn KV cache
+    ("Enable scaled FP8 (e4m3fn) KV cache on ROCm": the paged-attention
+    kernel reads the fp8 cache and dequantises it with the KV scale,
+    x' = fp8_dequant(q) * scale, "Scaling semantics"), in float64.
+
+    q [B, Hq, D]: bf16 bits (uint16) or floats. k_codes, v_codes [T, Hkv, D]
+    uint8 e4m3fn codes; sequence b owns cache rows seq_starts[b] ..
+    seq_starts[b+1]-1. Query head h reads KV head h // (Hq // Hkv) (grouped
+    queries). k_scale, v_scale: None means 1.0. sm_scale: None means
+    1/sqrt(D). For each (b, h):
+        s_t = sm_scale * q[b, h] . (dec(K[t, g]) * k_scale)
+        p = softmax(s) over the sequence's rows,
+        out[b, h] = sum_t p_t * dec(V[t, g]) * v_scale
+    An empty sequence gives zeros. Returns float64 [B, Hq, D].
+    """
+    q = np.asarray(q)
+    qf = bf16_bits_to_f64(q) if q.dtype == np.uint16 else q.astype(np.float64)
+    B, Hq, D = qf.shape
+    Hkv = k_codes.shape[1]
+    G = Hq // Hkv
+    ks = 1.0 if k_scale is None else float(np.float32(k_scale))
+    vs = 1.0 if v_scale is None else float(np.float32(v_scale))
+    sm = 1.0 / np.sqrt(D) if sm_scale is None else float(np.float32(sm_scale))
+    kf = e4m3_decode(k_codes) * ks
+    vf = e4m3_decode(v_codes) * vs
+    starts = np.asarray(seq_starts, dtype=np.int64)
+    out = np.zeros((B, Hq, D), np.float64)
+    for b in range(B):
+        t0, t1 = int(starts[b]), int(starts[b + 1])
+        if t1 <= t0:
+            continue
+        for h in range(Hq):
+            g = h // G
+            s = (kf[t0:t1, g, :] @ qf[b, h]) * sm
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            out[b, h] = p @ vf[t0:t1, g, :]
+    return out
