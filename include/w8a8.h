@@ -273,6 +273,39 @@ w8a8_status w8a8_requant_shared_scale(const void* w, int64_t ldw, w8a8_qtype qt,
                                       float* shared_scale, hipStream_t stream);
 
 /*
+ * Decode attention over an e4m3fn KV cache, the cache dequantised with its
+ * per-tensor scales as it is read [P3: the paged-attention kernel reads the
+ * fp8 cache with the KV scale; "Scaling semantics": x' = fp8_dequant(q) *
+ * scale]. One query token per sequence:
+ *   out[b, h] = sum_t softmax_t(s) * dec(v[t, g]) * v_scale,
+ *   s_t = sm_scale * q[b, h] . (dec(k[t, g]) * k_scale),  g = h / (Hq / Hkv),
+ * over the cache rows t = seq_starts[b] .. seq_starts[b+1]-1 (contiguous
+ * rows per sequence; no block table). An empty sequence gives zeros.
+ *   out, q: device bf16 [B, Hq, D], contiguous.
+ *   k_cache, v_cache: device e4m3fn codes [rows, Hkv, D], contiguous (the
+ *     layout kv_fp8_scaled_quant writes for a [rows, Hkv, D] tensor).
+ *   seq_starts: device int32 [B + 1], non-decreasing; every sequence at most
+ *     max_seq_len rows (host value sizing the row splits; rows past it are
+ *     not read). Rows outside 0 .. rows-1 are never read (they count as
+ *     absent), so bad device offsets cannot fault.
+ *   k_scale, v_scale: device float32 scalars, NULL: 1.0. sm_scale: host
+ *     float, 0: 1/sqrt(D).
+ *   workspace: device memory of at least
+ *     kv_fp8_attention_workspace_size(B, Hq, Hkv, max_seq_len) bytes
+ *     (partial results of the row splits; no initialisation needed).
+ * D must be 128 and Hq / Hkv one of 1, 2, 4, 8 (UNSUPPORTED otherwise). All
+ * arithmetic is float32 (exp by the hardware's exponential), the output
+ * rounded once to bf16. Two kernels; nothing allocated or synchronised.
+ */
+int64_t kv_fp8_attention_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_seq_len);
+
+w8a8_status kv_fp8_decode_attention(void* out, const void* q, int64_t B, int64_t Hq, int64_t Hkv,
+                                    int64_t D, const uint8_t* k_cache, const uint8_t* v_cache,
+                                    int64_t rows, const int32_t* seq_starts, int64_t max_seq_len,
+                                    const float* k_scale, const float* v_scale, float sm_scale,
+                                    void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
  * Name of the kernel configuration w8a8_scaled_mm runs for an M x N x K
  * problem, such as "gemm_decode_kernel<16x16>" or
  * "gemm_tile_kernel<256x256>" (a static string; "" for negative sizes), so

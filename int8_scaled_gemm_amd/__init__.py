@@ -12,6 +12,8 @@ Functions carry the C names:
 * ``w8a8_scaled_mm(a, b, a_scales, b_scales, out_dtype)`` -> ``out``
 * ``kv_fp8_scaled_quant(x, scale=None, dynamic=True)`` -> ``(q, scale)``
 * ``kv_fp8_scaled_dequant(q, scale, out_dtype)`` -> ``x``
+* ``kv_fp8_decode_attention(q, k_cache, v_cache, seq_starts, max_seq_len, k_scale, v_scale)``
+  -> ``out`` (decode attention reading the fp8 cache)
 
 plus ``scaled_mm(a, b, scale_a, scale_b, out_dtype)``, the call shape of
 ``cutlass_scaled_mm_dq`` in "[Kernel] Add w8a8 CUTLASS kernels" (the usage
@@ -63,6 +65,8 @@ SIGNATURES = {
                            _P, _P, _I64, _P],
     "w8a8_expand_shard_scales": [_P, _P, _I64, _P, _P],
     "w8a8_requant_shared_scale": [_P, _I64, _I, _I64, _P, _I64, _P, _P, _I64, _P, _P],
+    "kv_fp8_decode_attention": [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _P,
+                                ctypes.c_float, _P, _I64, _P],
 }
 
 
@@ -105,6 +109,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.w8a8_scaled_mm_ws_kernel.restype = ctypes.c_char_p
     lib.w8a8_scaled_mm_workspace_size.argtypes = [_I64, _I64, _I64]
     lib.w8a8_scaled_mm_workspace_size.restype = ctypes.c_int64
+    lib.kv_fp8_attention_workspace_size.argtypes = [_I64, _I64, _I64, _I64]
+    lib.kv_fp8_attention_workspace_size.restype = ctypes.c_int64
     _lib = lib
     return lib
 
@@ -215,6 +221,43 @@ def kv_fp8_scaled_dequant(q: torch.Tensor, scale: torch.Tensor | None,
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     _call("kv_fp8_scaled_dequant", _ptr(q), q.numel(), _ptr(scale), _ptr(out),
           _dtype(out.dtype), _stream(q))
+    return out
+
+
+def kv_fp8_attention_workspace_size(B: int, Hq: int, Hkv: int, max_seq_len: int) -> int:
+    return load_library().kv_fp8_attention_workspace_size(B, Hq, Hkv, max_seq_len)
+
+
+def kv_fp8_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            seq_starts: torch.Tensor, max_seq_len: int,
+                            k_scale: torch.Tensor | None = None,
+                            v_scale: torch.Tensor | None = None, sm_scale: float = 0.0,
+                            out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention over an e4m3fn KV cache: q [B, Hq, D] bf16, caches
+    [rows, Hkv, D] e4m3fn, seq_starts [B + 1] int32 (sequence b owns cache
+    rows seq_starts[b] .. seq_starts[b+1]-1) -> out [B, Hq, D] bf16."""
+    _check_cuda(q, k_cache, v_cache, seq_starts, k_scale, v_scale, out, workspace)
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"kv_fp8_decode_attention: {name} must be a contiguous 3-d tensor")
+    if q.dtype != torch.bfloat16 or seq_starts.dtype != torch.int32:
+        raise ValueError("kv_fp8_decode_attention: q must be bfloat16 and seq_starts int32")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("kv_fp8_decode_attention: k_cache and v_cache shapes differ")
+    B, Hq, D = q.shape
+    rows, Hkv, Dk = k_cache.shape
+    if Dk != D or seq_starts.numel() != B + 1:
+        raise ValueError("kv_fp8_decode_attention: head dimension or seq_starts length mismatch")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    need = kv_fp8_attention_workspace_size(B, Hq, Hkv, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _call("kv_fp8_decode_attention", _ptr(out), _ptr(q), B, Hq, Hkv, D, _ptr(k_cache),
+          _ptr(v_cache), rows, _ptr(seq_starts), max_seq_len, _ptr(k_scale), _ptr(v_scale),
+          float(sm_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+          _stream(q))
     return out
 
 
@@ -450,4 +493,5 @@ __all__ = ["w8a8_quant_per_token", "w8a8_quant_per_tensor", "w8a8_scaled_mm",
            "kv_fp8_scaled_quant", "kv_fp8_scaled_dequant", "scaled_mm", "W8A8Error",
            "w8a8_expand_shard_scales", "w8a8_requant_shared_scale",
            "w8a8_quant_per_token_azp", "w8a8_colsum", "w8a8_scaled_mm_azp",
+           "kv_fp8_decode_attention", "kv_fp8_attention_workspace_size",
            "load_library", "version", "LIB_PATH", "SIGNATURES"]

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw8a8.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["quant.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "attention.hip", "api.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -396,4 +396,57 @@ w8a8_status w8a8_requant_shared_scale(const void* w, int64_t ldw, w8a8_qtype qt,
                     fn);
 }
 
+int64_t kv_fp8_attention_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_seq_len) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_seq_len < 0 || B > kMaxDim || Hq > kMaxDim || Hkv > kMaxDim)
+        return 0;
+    const int splits = w8a8::attention_splits(B, Hkv, max_seq_len);
+    return B * Hq * splits * (128 + 2) * 4;
+}
+
+w8a8_status kv_fp8_decode_attention(void* out, const void* q, int64_t B, int64_t Hq, int64_t Hkv,
+                                    int64_t D, const uint8_t* k_cache, const uint8_t* v_cache,
+                                    int64_t rows, const int32_t* seq_starts, int64_t max_seq_len,
+                                    const float* k_scale, const float* v_scale, float sm_scale,
+                                    void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    const char* fn = "kv_fp8_decode_attention";
+    if (B < 0 || Hq < 0 || Hkv < 0 || D < 0 || rows < 0 || max_seq_len < 0)
+        return fail(W8A8_ERR_SHAPE, "%s: negative size", fn);
+    if (B == 0 || Hq == 0) return ok();
+    if (Hkv == 0 || Hq % Hkv) return fail(W8A8_ERR_SHAPE, "%s: Hq=%lld is not a multiple of Hkv=%lld", fn, (long long)Hq, (long long)Hkv);
+    const int64_t G = Hq / Hkv;
+    if (D != 128) return fail(W8A8_ERR_UNSUPPORTED, "%s: head dimension %lld (only 128)", fn, (long long)D);
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(W8A8_ERR_UNSUPPORTED, "%s: %lld query heads per KV head (1, 2, 4 or 8)", fn, (long long)G);
+    if (B > 65535 || Hkv > 65535 || Hq > kMaxDim || max_seq_len > kMaxDim || rows > kMaxDim)
+        return fail(W8A8_ERR_UNSUPPORTED, "%s: sizes beyond the launch limits", fn);
+    if (!out || !q || !seq_starts || !workspace) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL out, q, seq_starts or workspace", fn);
+    if (rows > 0 && (!k_cache || !v_cache)) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL cache", fn);
+    if (!aligned16(out) || !aligned16(q) || (k_cache && !aligned16(k_cache)) || (v_cache && !aligned16(v_cache)) ||
+        !aligned16(workspace))
+        return fail(W8A8_ERR_ALIGNMENT, "%s: out, q, caches and workspace must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(seq_starts) | reinterpret_cast<uintptr_t>(k_scale) |
+         reinterpret_cast<uintptr_t>(v_scale)) & 3u)
+        return fail(W8A8_ERR_ALIGNMENT, "%s: seq_starts and scales must be 4-byte aligned", fn);
+    if (workspace_bytes < kv_fp8_attention_workspace_size(B, Hq, Hkv, max_seq_len))
+        return fail(W8A8_ERR_INVALID_ARG, "%s: workspace of %lld bytes, %lld needed", fn, (long long)workspace_bytes,
+                    (long long)kv_fp8_attention_workspace_size(B, Hq, Hkv, max_seq_len));
+    w8a8::AttnArgs a;
+    a.out = static_cast<uint16_t*>(out);
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = k_cache;
+    a.v = v_cache;
+    a.starts = seq_starts;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.sm_scale = sm_scale != 0.0f ? sm_scale : 0.08838834764831845f;  // 1/sqrt(128)
+    a.B = static_cast<int>(B);
+    a.Hq = static_cast<int>(Hq);
+    a.Hkv = static_cast<int>(Hkv);
+    a.rows = rows;
+    a.splits = w8a8::attention_splits(B, Hkv, max_seq_len);
+    a.chunk = w8a8::attention_chunk(max_seq_len, a.splits);
+    a.part = static_cast<float*>(workspace);
+    return from_hip(w8a8::launch_attention(a, stream), fn);
+}
+
 }  // extern "C"

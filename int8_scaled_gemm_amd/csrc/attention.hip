@@ -1,0 +1,190 @@
+// attention.hip -- decode attention over an e4m3fn KV cache, the cache
+// dequantised with its per-tensor scales as it is read ("Enable scaled FP8
+// (e4m3fn) KV cache on ROCm": the paged-attention kernel reads the fp8 cache
+// and dequantises it with the KV scale, x' = fp8_dequant(q) * scale).
+//
+// One query token per sequence, D = 128, grouped-query heads (query head h
+// reads KV head h / G). Sequence b owns cache rows starts[b] .. starts[b+1]-1
+// of K and V [rows, Hkv, D]. Bound by the cache read from HBM (1 byte per
+// element), so the arithmetic is plain fp32 on the vector units:
+//  - attn_split_kernel: workgroup (split s, KV head g, sequence b), one wave
+//    per query head of the group, over the split's rows in blocks of 64.
+//    K and V blocks are staged in LDS (each loaded once for the G heads),
+//    the next block's bytes held in registers while the current one is
+//    consumed. Lane t scores row t of the block (q pre-scaled by
+//    sm_scale * k_scale, so the score is q'.dec(K)), the softmax runs online
+//    (running max m and sum l per wave), and lane l accumulates output
+//    dims 2l, 2l+1 over the block's rows. Writes (o, m, l) per split.
+//  - attn_combine_kernel: per (sequence, head), the splits' partial sums
+//    rescaled to the common maximum, divided by the total weight, times
+//    v_scale, rounded to bf16.
+#include <math.h>
+
+#include <algorithm>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace w8a8 {
+
+namespace {
+
+constexpr int kD = 128;        // head dimension
+constexpr int kRows = 64;      // cache rows per block (one per lane)
+constexpr int kChunks = 2 * kRows * kD / 16;  // 16-byte pieces of one K + V block
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+template <int G>
+__global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
+    constexpr int NT = G * 64;
+    constexpr int PER = kChunks / NT;  // pieces per thread per block
+    static_assert(kChunks % NT == 0, "block pieces per thread");
+    __shared__ float qs[G][kD];
+    __shared__ __attribute__((aligned(16))) uint8_t kb[kRows * kD];
+    __shared__ __attribute__((aligned(16))) uint8_t vb[kRows * kD];
+
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = g * G + w;
+    const int first = p.starts[b];
+    const int len = max(p.starts[b + 1] - first, 0);
+    const int r0 = s * p.chunk, r1 = min(len, r0 + p.chunk);
+    const float ks = p.k_scale ? *p.k_scale : 1.0f;
+    {
+        const uint32_t two = *reinterpret_cast<const uint32_t*>(
+            p.q + (static_cast<int64_t>(b) * p.Hq + h) * kD + 2 * lane);
+        const float f = p.sm_scale * ks;
+        qs[w][2 * lane] = __uint_as_float(two << 16) * f;
+        qs[w][2 * lane + 1] = __uint_as_float(two & 0xFFFF0000u) * f;
+    }
+    // Piece i of a block: K (i < kChunks/2) or V, row (i % 512) / 8, 16-byte
+    // chunk i % 8. Rows past the split, the sequence or the cache read zero.
+    const int64_t rstride = static_cast<int64_t>(p.Hkv) * kD;
+    auto fetch = [&](int base, u32x4* v) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int i = threadIdx.x + NT * j;
+            const int half = i / (kChunks / 2), k = i % (kChunks / 2);
+            const int t = base + k / 8;
+            const int64_t row = static_cast<int64_t>(first) + t;
+            v[j] = u32x4{0, 0, 0, 0};
+            if (t < r1 && row >= 0 && row < p.rows)
+                v[j] = *reinterpret_cast<const u32x4*>((half ? p.v : p.k) + row * rstride +
+                                                       static_cast<int64_t>(g) * kD + 16 * (k % 8));
+        }
+    };
+    // K row t keeps chunk c at slot c ^ (t % 8): the 64 lanes, one row each,
+    // then read 8 different slots per group of 8 rows.
+    auto stash = [&](const u32x4* v) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int i = threadIdx.x + NT * j;
+            const int half = i / (kChunks / 2), k = i % (kChunks / 2);
+            const int t = k / 8, c = k % 8;
+            uint8_t* dst = half ? vb + t * kD + 16 * c : kb + t * kD + 16 * (c ^ (t & 7));
+            *reinterpret_cast<u32x4*>(dst) = v[j];
+        }
+    };
+
+    float m = -INFINITY, l = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    u32x4 nxt[PER];
+    if (r0 < r1) fetch(r0, nxt);
+    for (int base = r0; base < r1; base += kRows) {
+        __syncthreads();  // the previous block is consumed (and qs written)
+        stash(nxt);
+        __syncthreads();
+        if (base + kRows < r1) fetch(base + kRows, nxt);  // in flight during this block
+        // score of row base + lane
+        float sc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + lane * kD + 16 * (c ^ (lane & 7)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float* qd = &qs[w][16 * c + 4 * e];
+                sc = fmaf(qd[0], __builtin_amdgcn_cvt_f32_fp8(kv[e], 0), sc);
+                sc = fmaf(qd[1], __builtin_amdgcn_cvt_f32_fp8(kv[e], 1), sc);
+                sc = fmaf(qd[2], __builtin_amdgcn_cvt_f32_fp8(kv[e], 2), sc);
+                sc = fmaf(qd[3], __builtin_amdgcn_cvt_f32_fp8(kv[e], 3), sc);
+            }
+        }
+        const int64_t row = static_cast<int64_t>(first) + base + lane;
+        const bool valid = base + lane < r1 && row >= 0 && row < p.rows;  // absent rows: no weight
+        const float mn = fmaxf(m, wave_max(valid ? sc : -INFINITY));
+        // A block with no row inside the cache leaves mn = m = -inf: nothing
+        // to add (and -inf - -inf must not reach the exponential).
+        const float alpha = mn == -INFINITY ? 1.0f : __expf(m - mn);  // 0 on the first block
+        const float pt = valid ? __expf(sc - mn) : 0.0f;
+        l = l * alpha + wave_sum(pt);
+        o0 *= alpha;
+        o1 *= alpha;
+#pragma unroll 16
+        for (int t = 0; t < kRows; ++t) {
+            const float pw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pt), t));
+            const uint32_t two = *reinterpret_cast<const uint16_t*>(vb + t * kD + 2 * lane);
+            o0 = fmaf(pw, __builtin_amdgcn_cvt_f32_fp8(two, 0), o0);
+            o1 = fmaf(pw, __builtin_amdgcn_cvt_f32_fp8(two, 1), o1);
+        }
+        m = mn;
+    }
+    float* dst = p.part + ((static_cast<int64_t>(b) * p.Hq + h) * p.splits + s) * (kD + 2);
+    dst[2 * lane] = o0;
+    dst[2 * lane + 1] = o1;
+    if (lane == 0) {
+        dst[kD] = m;
+        dst[kD + 1] = l;
+    }
+}
+
+__global__ __launch_bounds__(kD) void attn_combine_kernel(AttnArgs p) {
+    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const float* part = p.part + (static_cast<int64_t>(b) * p.Hq + h) * p.splits * (kD + 2);
+    float mx = -INFINITY;
+    for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, part[s * (kD + 2) + kD]);
+    float tot = 0.0f, acc = 0.0f;
+    for (int s = 0; s < p.splits; ++s) {
+        const float ls = part[s * (kD + 2) + kD + 1];
+        if (ls > 0.0f) {  // splits with no rows carry no weight
+            const float f = __expf(part[s * (kD + 2) + kD] - mx);
+            tot = fmaf(ls, f, tot);
+            acc = fmaf(part[s * (kD + 2) + d], f, acc);
+        }
+    }
+    const float vs = p.v_scale ? *p.v_scale : 1.0f;
+    const float o = tot > 0.0f ? acc / tot * vs : 0.0f;  // an empty sequence gives zeros
+    p.out[(static_cast<int64_t>(b) * p.Hq + h) * kD + d] = to_bf16_bits(o);
+}
+
+}  // namespace
+
+int attention_splits(int64_t B, int64_t Hkv, int64_t max_rows) {
+    // At least 256 rows per split, and enough workgroups for two per CU.
+    const int64_t by_rows = (max_rows + 255) / 256;
+    const int64_t by_grid = (1024 + B * Hkv - 1) / (B * Hkv);
+    return static_cast<int>(std::max<int64_t>(1, std::min(by_rows, by_grid)));
+}
+
+int attention_chunk(int64_t max_rows, int splits) {
+    const int64_t c = (max_rows + splits - 1) / splits;
+    return static_cast<int>(std::max<int64_t>(kRows, (c + kRows - 1) / kRows * kRows));
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
+    const dim3 grid(a.splits, a.Hkv, a.B);
+    switch (a.Hq / a.Hkv) {
+        case 1: hipLaunchKernelGGL((attn_split_kernel<1>), grid, dim3(64), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((attn_split_kernel<2>), grid, dim3(128), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((attn_split_kernel<4>), grid, dim3(256), 0, st, a); break;
+        default: hipLaunchKernelGGL((attn_split_kernel<8>), grid, dim3(512), 0, st, a); break;
+    }
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(a.Hq, a.B), dim3(kD), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace w8a8

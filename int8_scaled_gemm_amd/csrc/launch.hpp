@@ -81,4 +81,23 @@ bool quant_scaled_mm_fused(int64_t M, int64_t N, int64_t K);
 // Name of the kernel configuration a problem runs with.
 const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K, bool workspace);
 
+// Decode attention over an e4m3fn KV cache (attention.hip).
+struct AttnArgs {
+    uint16_t* out;           // [B, Hq, 128] bf16
+    const uint16_t* q;       // [B, Hq, 128] bf16
+    const uint8_t* k;        // [rows, Hkv, 128] e4m3fn
+    const uint8_t* v;
+    const int32_t* starts;   // [B + 1] (device)
+    const float* k_scale;    // NULL: 1.0
+    const float* v_scale;
+    float sm_scale;
+    int B, Hq, Hkv;
+    int64_t rows;            // cache rows (reads past them are skipped)
+    int splits, chunk;       // row splits per sequence, rows per split (multiple of 64)
+    float* part;             // [B, Hq, splits, 130] partial sums, maxima and weights
+};
+int attention_splits(int64_t B, int64_t Hkv, int64_t max_rows);
+int attention_chunk(int64_t max_rows, int splits);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+
 }  // namespace w8a8

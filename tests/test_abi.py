@@ -112,6 +112,28 @@ def test_quant_validation(lib):
     assert d(None, 0, None, None, 0, None) == OK
 
 
+def test_attention_validation(lib):
+    ws = lib.kv_fp8_attention_workspace_size(2, 32, 8, 1000)
+    assert ws == 2 * 32 * 4 * 130 * 4  # four 256-row splits of (o, m, l) per head
+
+    def call(out=FAKE, q=FAKE, B=2, Hq=32, Hkv=8, D=128, k=FAKE, v=FAKE, rows=100, st=FAKE,
+             max_len=1000, ks=None, vs=None, sm=0.0, w=FAKE, wb=ws):
+        return lib.kv_fp8_decode_attention(out, q, B, Hq, Hkv, D, k, v, rows, st, max_len, ks, vs,
+                                           sm, w, wb, None)
+    assert call(D=64) == UNSUP
+    assert call(Hq=24) == UNSUP        # 3 query heads per KV head
+    assert call(Hq=30) == SHAPE        # not a multiple of Hkv
+    assert call(B=-1) == SHAPE
+    assert call(wb=ws - 1) == INVALID
+    assert call(w=None) == INVALID
+    assert call(st=None) == INVALID
+    assert call(k=None) == INVALID
+    assert call(out=FAKE + 2) == ALIGN
+    assert call(st=FAKE + 2) == ALIGN
+    assert call(B=0, out=None, q=None, w=None) == OK  # nothing to do
+    assert lib.kv_fp8_attention_workspace_size(-1, 32, 8, 10) == 0
+
+
 def test_binding_layout_errors_are_python_errors():
     import torch
     # the binding refuses host tensors and wrong layouts before calling the library

@@ -115,6 +115,32 @@ def kv_tensor(layer: int, which: str, shape=KV_SHAPE, p_outlier: float = 1e-3,
     return x.to(torch.bfloat16)
 
 
+# Decode attention over the fp8 KV cache: Llama-3-8B heads (32 query heads,
+# 8 KV heads, head dimension 128); one layer's cache holds KV_SHAPE[0] rows,
+# split into ATTN_SEQUENCES sequences of seeded, uneven lengths (a length mix
+# standing in for the pages' ShareGPT serving runs).
+ATTN_HEADS = (32, 8, 128)
+ATTN_SEQUENCES = 16
+ATTN_LEN_SEED = 3
+
+
+def attention_seq_starts(total: int = KV_SHAPE[0], n: int = ATTN_SEQUENCES,
+                         seed: int = ATTN_LEN_SEED) -> torch.Tensor:
+    """Row offsets [n + 1] (int32) of n sequences filling `total` cache rows,
+    lengths proportional to seeded uniform weights in [0.25, 1.25)."""
+    g = _gen(seed)
+    w = torch.rand(n, generator=g, dtype=torch.float64) + 0.25
+    lens = torch.floor(w / w.sum() * total).to(torch.int64)
+    lens[-1] += total - int(lens.sum())
+    return torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(lens, 0)]).to(torch.int32)
+
+
+def attention_queries(B: int, Hq: int = ATTN_HEADS[0], D: int = ATTN_HEADS[2], seed: int = 0,
+                      device="cpu") -> torch.Tensor:
+    """One query token per sequence [B, Hq, D]: bf16 N(0, 1)."""
+    return normal_bf16((B, Hq, D), std=1.0, seed=seed, device=device)
+
+
 def random_codes(shape, qtype: str, seed: int = 0, device="cpu") -> torch.Tensor:
     """Uniformly random valid 8-bit codes, as uint8.
 
