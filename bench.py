@@ -20,6 +20,9 @@ nothing, so a whole step captures). Workloads:
   kv      scaled fp8 KV cache: per-tensor dynamic quant + dequant of 32
           layers of K and V [32768, 8, 128] bf16, plus the standalone
           per-token fp8 quantisation of [8192, 4096] bf16.
+  attn    decode attention over each of 32 layers' fp8 KV caches [32768,
+          8, 128] (16 sequences of uneven length, 32 query heads over 8 KV
+          heads), K and V dequantised with their scales as they are read.
 
 Weights are quantised once before timing (offline preparation). Every
 (M, layer) GEMM has its own weight copy, so one step streams 0.65 GB (decode)
@@ -213,6 +216,43 @@ def build_merge_workload(dev):
     return launches, keep
 
 
+ATTN_KERNELS = "attn_split_kernel+attn_combine_kernel"
+
+
+def build_attn_workload(dev, layers=workloads.KV_LAYERS):
+    """Decode attention of one query token per sequence over each layer's
+    fp8 KV cache: the layer's K and V [32768, 8, 128] quantised offline
+    (kv_fp8_scaled_quant, not timed), 16 sequences of uneven length, 32
+    query heads over 8 KV heads. Each layer reads its own cache."""
+    launches, keep = [], []
+    hq, hkv, d = workloads.ATTN_HEADS
+    starts = workloads.attention_seq_starts()
+    B = starts.numel() - 1
+    max_len = int((starts[1:] - starts[:-1]).max())
+    rows = workloads.KV_SHAPE[0]
+    starts_d = starts.to(dev)
+    ws = torch.empty(w8.kv_fp8_attention_workspace_size(B, hq, hkv, max_len), dtype=torch.uint8,
+                     device=dev)
+    keep += [starts_d, ws]
+    for layer in range(layers):
+        cache = []
+        for which in ("k", "v"):
+            x = workloads.kv_tensor(layer, which, device=dev)
+            q8, sc = w8.kv_fp8_scaled_quant(x)
+            del x
+            cache += [q8.view(torch.uint8), sc]
+        kc, ks, vc, vs = cache
+        q = workloads.attention_queries(B, hq, d, seed=200 + layer, device=dev)
+        out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
+        nbytes = 2 * rows * hkv * d + 2 * 2 * B * hq * d + 4 * (B + 1) + 8
+        launches.append(Launch("attn", lambda q=q, kc=kc, vc=vc, ks=ks, vs=vs, out=out:
+                               w8.kv_fp8_decode_attention(q, kc, vc, starts_d, max_len, ks, vs,
+                                                          out=out, workspace=ws),
+                               4 * rows * hq * d, nbytes, f"attention L{layer}", ATTN_KERNELS))
+        keep += [kc, ks, vc, vs, q, out]
+    return launches, keep
+
+
 WORKLOADS = {
     "decode": dict(desc="fp8 e4m3 decode GEMMs, Llama-3-8B QKV/O/gate_up/down at M=1,16,64: "
                         "dynamic per-token activation quant + scaled_mm, per-channel weights, "
@@ -238,6 +278,10 @@ WORKLOADS = {
     "kv": dict(desc="scaled fp8 KV cache: per-tensor dynamic quant + dequant of 32 layers of "
                     "K and V [32768,8,128] bf16, plus per-token fp8 quant of [8192,4096]",
                ),
+    "attn": dict(desc="decode attention over the scaled fp8 KV cache: 32 layers, each one query "
+                      "token for 16 sequences of uneven length (32768 cache rows), 32 query heads "
+                      "over 8 KV heads, head dim 128, K and V dequantised with their per-tensor "
+                      "scales as they are read, bf16 out"),
     "merge": dict(desc="merged-layer weight scales: per-shard scales of the merged QKV and "
                        "gate_up weights (Llama-3-8B fp8, Llama-3-70B int8) expanded to "
                        "per-channel scales, and the codes rescaled to one shared scale"),
@@ -350,6 +394,29 @@ def cpu_baseline(spec, launches_meta, budget_s: float):
                 "kind": "oracle",
                 "sample": f"expansion + requantisation of {done} of the step's "
                           f"{len(workloads.MERGED_LAYERS)} merged weights ({dt:.1f} s)"}
+    if spec is WORKLOADS["attn"]:   # the oracle's attention over whole layers
+        hq, hkv, d = workloads.ATTN_HEADS
+        starts = workloads.attention_seq_starts().numpy()
+        B = starts.size - 1
+        dt, nbytes, done = 0.0, 0, 0
+        for layer in range(4):   # drawing and quantising a layer's cache costs more than its attention
+            codes = []
+            for which in ("k", "v"):   # the offline quantisation is not timed
+                xh = workloads.as_u16(workloads.kv_tensor(layer, which)).reshape(-1)
+                c, sc = oracle.kv_quant(xh, xtype="bf16")
+                codes += [c.reshape(workloads.KV_SHAPE), sc]
+            qh = workloads.as_u16(workloads.attention_queries(B, hq, d, seed=200 + layer))
+            t0 = time.perf_counter()
+            oracle.decode_attention_fp8kv(qh, codes[0], codes[2], starts, codes[1], codes[3])
+            dt += time.perf_counter() - t0
+            nbytes += 2 * codes[0].size + 4 * B * hq * d
+            done += 1
+            if dt > budget_s:
+                break
+        return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+                "kind": "oracle",
+                "sample": f"attention over {done} of the step's {workloads.KV_LAYERS} layer caches "
+                          f"({dt:.1f} s; the offline cache quantisation not timed)"}
     if spec.get("layers") is None:   # kv: quant + dequant of whole layer tensors
         n = 1
         for d in workloads.KV_SHAPE:
@@ -447,6 +514,8 @@ def main():
     log(f"[bench] workload {args.workload}: building inputs")
     if args.workload == "kv":
         launches, keep = build_kv_workload(dev)
+    elif args.workload == "attn":
+        launches, keep = build_attn_workload(dev)
     elif args.workload == "merge":
         launches, keep = build_merge_workload(dev)
     else:
@@ -481,6 +550,10 @@ def main():
         value = per_step_bytes / (step_ms / 1e3) / 1e9
         metric, unit = "scaled fp8 KV cache quant+dequant GB/s (algorithmic bytes)", "GB/s"
         dtype = "fp8e4m3"
+    elif args.workload == "attn":
+        value = per_step_bytes / (step_ms / 1e3) / 1e9
+        metric, unit = "fp8 KV cache decode attention GB/s (algorithmic bytes)", "GB/s"
+        dtype = "fp8e4m3 cache, f32 arithmetic"
     elif args.workload == "merge":
         value = per_step_bytes / (step_ms / 1e3) / 1e9
         metric, unit = "merged-layer scale expansion + shared-scale requant GB/s (algorithmic bytes)", "GB/s"
@@ -507,7 +580,7 @@ def main():
     # most time per step; the small per-token quantizations of decode batches
     # are latency-bound (a few KB each) and are listed with their latency only.
     kinds = {L.kernel: L.kind for L in launches}
-    main_kind = {"kv": "kv_quant", "merge": "merge_requant"}.get(args.workload, "gemm")
+    main_kind = {"kv": "kv_quant", "merge": "merge_requant", "attn": "attn"}.get(args.workload, "gemm")
     dom = max((k for k in kernels if kinds[k] == main_kind),
               key=lambda k: kernels[k]["avg_s"] * kernels[k]["launches"])
     roof = roofline(dom, kernels[dom], spec, args.workload)
@@ -533,8 +606,10 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic (seeded; Llama-3 layer shapes, bf16 N(0,1) activations with 1% "
-                "outlier channels x20, N(0,0.02) weights)" if args.workload not in ("kv", "merge") else
+                "outlier channels x20, N(0,0.02) weights)" if args.workload not in ("kv", "merge", "attn") else
                 "synthetic (seeded; N(0,1) K/V with 0.1% outliers x10)" if args.workload == "kv" else
+                "synthetic (seeded; N(0,1) K/V with 0.1% outliers x10 quantised to e4m3fn, "
+                "N(0,1) bf16 queries, sequence lengths from seeded weights)" if args.workload == "attn" else
                 "synthetic (seeded; uniformly random valid codes, shard scales U(2e-4, 4e-3))",
         "config": {"workload": spec["desc"], "mode": "hip-graph replay, inputs resident in HBM",
                    "step_bytes": per_step_bytes, "step_flops": per_step_flops,

@@ -13,8 +13,10 @@
 //    the next block's bytes held in registers while the current one is
 //    consumed. Lane t scores row t of the block (q pre-scaled by
 //    sm_scale * k_scale, so the score is q'.dec(K)), the softmax runs online
-//    (running max m and sum l per wave), and lane l accumulates output
-//    dims 2l, 2l+1 over the block's rows. Writes (o, m, l) per split.
+//    (running max m and sum l per wave), and lane l accumulates output dims
+//    8 (l % 16) .. +7 over rows l / 16, +4, +8, ... of each block (the
+//    weights through LDS); the four row groups are added once per split.
+//    Writes (o, m, l) per split.
 //  - attn_combine_kernel: per (sequence, head), the splits' partial sums
 //    rescaled to the common maximum, divided by the total weight, times
 //    v_scale, rounded to bf16.
@@ -44,7 +46,8 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
     constexpr int NT = G * 64;
     constexpr int PER = kChunks / NT;  // pieces per thread per block
     static_assert(kChunks % NT == 0, "block pieces per thread");
-    __shared__ float qs[G][kD];
+    __shared__ __attribute__((aligned(16))) float qs[G][kD];
+    __shared__ __attribute__((aligned(16))) float ps[G][kRows];
     __shared__ __attribute__((aligned(16))) uint8_t kb[kRows * kD];
     __shared__ __attribute__((aligned(16))) uint8_t vb[kRows * kD];
 
@@ -80,19 +83,23 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
         }
     };
     // K row t keeps chunk c at slot c ^ (t % 8): the 64 lanes, one row each,
-    // then read 8 different slots per group of 8 rows.
+    // then read 8 different slots per group of 8 rows. V row t keeps it at
+    // slot c ^ (t / 16), so that the four 16-row groups read apart.
     auto stash = [&](const u32x4* v) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int i = threadIdx.x + NT * j;
             const int half = i / (kChunks / 2), k = i % (kChunks / 2);
             const int t = k / 8, c = k % 8;
-            uint8_t* dst = half ? vb + t * kD + 16 * c : kb + t * kD + 16 * (c ^ (t & 7));
+            uint8_t* dst = half ? vb + t * kD + 16 * (c ^ (t >> 4)) : kb + t * kD + 16 * (c ^ (t & 7));
             *reinterpret_cast<u32x4*>(dst) = v[j];
         }
     };
 
-    float m = -INFINITY, l = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const int grp = lane >> 4, d0 = 8 * (lane & 15);  // value rows grp, grp+4, ...; dims d0..d0+7
+    float m = -INFINITY, l = 0.0f;
+    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     u32x4 nxt[PER];
     if (r0 < r1) fetch(r0, nxt);
     for (int base = r0; base < r1; base += kRows) {
@@ -107,11 +114,13 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
             const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + lane * kD + 16 * (c ^ (lane & 7)));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float* qd = &qs[w][16 * c + 4 * e];
-                sc = fmaf(qd[0], __builtin_amdgcn_cvt_f32_fp8(kv[e], 0), sc);
-                sc = fmaf(qd[1], __builtin_amdgcn_cvt_f32_fp8(kv[e], 1), sc);
-                sc = fmaf(qd[2], __builtin_amdgcn_cvt_f32_fp8(kv[e], 2), sc);
-                sc = fmaf(qd[3], __builtin_amdgcn_cvt_f32_fp8(kv[e], 3), sc);
+                const f32x4 qd = *reinterpret_cast<const f32x4*>(&qs[w][16 * c + 4 * e]);
+                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(kv[e], false);
+                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(kv[e], true);
+                sc = fmaf(qd[0], lo[0], sc);
+                sc = fmaf(qd[1], lo[1], sc);
+                sc = fmaf(qd[2], hi[0], sc);
+                sc = fmaf(qd[3], hi[1], sc);
             }
         }
         const int64_t row = static_cast<int64_t>(first) + base + lane;
@@ -122,20 +131,48 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
         const float alpha = mn == -INFINITY ? 1.0f : __expf(m - mn);  // 0 on the first block
         const float pt = valid ? __expf(sc - mn) : 0.0f;
         l = l * alpha + wave_sum(pt);
-        o0 *= alpha;
-        o1 *= alpha;
-#pragma unroll 16
-        for (int t = 0; t < kRows; ++t) {
-            const float pw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pt), t));
-            const uint32_t two = *reinterpret_cast<const uint16_t*>(vb + t * kD + 2 * lane);
-            o0 = fmaf(pw, __builtin_amdgcn_cvt_f32_fp8(two, 0), o0);
-            o1 = fmaf(pw, __builtin_amdgcn_cvt_f32_fp8(two, 1), o1);
+        ps[w][lane] = pt;  // read back by the lanes of this wave only
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= alpha;
+#pragma unroll
+        for (int i4 = 0; i4 < kRows / 16; i4 += 1) {
+            // rows t = 16 grp + 4 i4 .. +3 of the block
+            const int t0 = 16 * grp + 4 * i4;
+            const f32x4 pw = *reinterpret_cast<const f32x4*>(&ps[w][t0]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = t0 + r;
+                const u32x2 vv = *reinterpret_cast<const u32x2*>(
+                    vb + t * kD + 16 * ((d0 >> 4) ^ grp) + (d0 & 15));
+                const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(vv[0], false);
+                const f32x2 b2 = __builtin_amdgcn_cvt_pk_f32_fp8(vv[0], true);
+                const f32x2 c2 = __builtin_amdgcn_cvt_pk_f32_fp8(vv[1], false);
+                const f32x2 d2 = __builtin_amdgcn_cvt_pk_f32_fp8(vv[1], true);
+                o[0] = fmaf(pw[r], a[0], o[0]);
+                o[1] = fmaf(pw[r], a[1], o[1]);
+                o[2] = fmaf(pw[r], b2[0], o[2]);
+                o[3] = fmaf(pw[r], b2[1], o[3]);
+                o[4] = fmaf(pw[r], c2[0], o[4]);
+                o[5] = fmaf(pw[r], c2[1], o[5]);
+                o[6] = fmaf(pw[r], d2[0], o[6]);
+                o[7] = fmaf(pw[r], d2[1], o[7]);
+            }
         }
+        __builtin_amdgcn_wave_barrier();  // ps is rewritten by the next block
         m = mn;
     }
+    // add the four row groups (lanes l, l+16, l+32, l+48 hold the same dims)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        o[e] += __shfl_xor(o[e], 16, 64);
+        o[e] += __shfl_xor(o[e], 32, 64);
+    }
     float* dst = p.part + ((static_cast<int64_t>(b) * p.Hq + h) * p.splits + s) * (kD + 2);
-    dst[2 * lane] = o0;
-    dst[2 * lane + 1] = o1;
+    if (lane < 16) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[d0 + e] = o[e];
+    }
     if (lane == 0) {
         dst[kD] = m;
         dst[kD + 1] = l;
