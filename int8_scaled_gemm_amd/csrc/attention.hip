@@ -179,18 +179,33 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
     }
 }
 
+constexpr int kMaxSplits = 1024;  // attention_splits never gives more
+
 __global__ __launch_bounds__(kD) void attn_combine_kernel(AttnArgs p) {
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     const float* part = p.part + (static_cast<int64_t>(b) * p.Hq + h) * p.splits * (kD + 2);
+    // every split's maximum and weight, loaded side by side into LDS
+    __shared__ float sm[kMaxSplits], sl[kMaxSplits];
+    __shared__ float red[kD / 64];
     float mx = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, part[s * (kD + 2) + kD]);
+    for (int s = d; s < p.splits; s += kD) {
+        sm[s] = part[s * (kD + 2) + kD];
+        sl[s] = part[s * (kD + 2) + kD + 1];
+        mx = fmaxf(mx, sm[s]);
+    }
+    mx = wave_max(mx);
+    if ((d & 63) == 0) red[d >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(red[0], red[1]);
     float tot = 0.0f, acc = 0.0f;
+#pragma unroll 8
     for (int s = 0; s < p.splits; ++s) {
-        const float ls = part[s * (kD + 2) + kD + 1];
+        const float ls = sl[s];
+        const float v = part[s * (kD + 2) + d];
         if (ls > 0.0f) {  // splits with no rows carry no weight
-            const float f = __expf(part[s * (kD + 2) + kD] - mx);
+            const float f = __expf(sm[s] - mx);
             tot = fmaf(ls, f, tot);
-            acc = fmaf(part[s * (kD + 2) + d], f, acc);
+            acc = fmaf(v, f, acc);
         }
     }
     const float vs = p.v_scale ? *p.v_scale : 1.0f;
@@ -203,7 +218,7 @@ __global__ __launch_bounds__(kD) void attn_combine_kernel(AttnArgs p) {
 int attention_splits(int64_t B, int64_t Hkv, int64_t max_rows) {
     // At least 256 rows per split, and enough workgroups for two per CU.
     const int64_t by_rows = (max_rows + 255) / 256;
-    const int64_t by_grid = (1024 + B * Hkv - 1) / (B * Hkv);
+    const int64_t by_grid = (1024 + B * Hkv - 1) / (B * Hkv);  // <= 1024 (kMaxSplits)
     return static_cast<int>(std::max<int64_t>(1, std::min(by_rows, by_grid)));
 }
 
