@@ -11,8 +11,10 @@
 //    per query head of the group, over the split's rows in blocks of 64.
 //    K and V blocks are staged in LDS (each loaded once for the G heads),
 //    the next block's bytes held in registers while the current one is
-//    consumed. Lane t scores row t of the block (q pre-scaled by
-//    sm_scale * k_scale, so the score is q'.dec(K)), the softmax runs online
+//    consumed. The block's scores for all G heads are bf16 MFMAs (codes
+//    converted exactly to bf16, the query's own bf16 values, float32
+//    sums), scaled by sm_scale * k_scale; lane t of wave w then holds row
+//    t's score for head w, and the softmax runs online
 //    (running max m and sum l per wave), and lane l accumulates output dims
 //    8 (l % 16) .. +7 over rows l / 16, +4, +8, ... of each block (the
 //    weights through LDS); the four row groups are added once per split.
@@ -35,6 +37,9 @@ constexpr int kD = 128;        // head dimension
 constexpr int kRows = 64;      // cache rows per block (one per lane)
 constexpr int kChunks = 2 * kRows * kD / 16;  // 16-byte pieces of one K + V block
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
@@ -46,7 +51,7 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
     constexpr int NT = G * 64;
     constexpr int PER = kChunks / NT;  // pieces per thread per block
     static_assert(kChunks % NT == 0, "block pieces per thread");
-    __shared__ __attribute__((aligned(16))) float qs[G][kD];
+    __shared__ __attribute__((aligned(16))) float ss[G][kRows];  // scores of the block
     __shared__ __attribute__((aligned(16))) float ps[G][kRows];
     __shared__ __attribute__((aligned(16))) uint8_t kb[kRows * kD];
     __shared__ __attribute__((aligned(16))) uint8_t vb[kRows * kD];
@@ -58,13 +63,17 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
     const int first = p.starts[b];
     const int len = max(p.starts[b + 1] - first, 0);
     const int r0 = s * p.chunk, r1 = min(len, r0 + p.chunk);
-    const float ks = p.k_scale ? *p.k_scale : 1.0f;
-    {
-        const uint32_t two = *reinterpret_cast<const uint32_t*>(
-            p.q + (static_cast<int64_t>(b) * p.Hq + h) * kD + 2 * lane);
-        const float f = p.sm_scale * ks;
-        qs[w][2 * lane] = __uint_as_float(two << 16) * f;
-        qs[w][2 * lane + 1] = __uint_as_float(two & 0xFFFF0000u) * f;
+    const float qscale = p.sm_scale * (p.k_scale ? *p.k_scale : 1.0f);
+    // The group's queries as the second operand of 16 x 16 x 32 bf16 MFMAs:
+    // lane l holds query head l % 16 of the group (zeros past G), dims
+    // 32 ks + 8 (l / 16) .. +7 for ks = 0..3, the query's own bf16 values.
+    u32x4 qf[kD / 32];
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ++ks) {
+        qf[ks] = u32x4{0, 0, 0, 0};
+        if ((lane & 15) < G)
+            qf[ks] = *reinterpret_cast<const u32x4*>(
+                p.q + (static_cast<int64_t>(b) * p.Hq + g * G + (lane & 15)) * kD + 32 * ks + 8 * (lane >> 4));
     }
     // Piece i of a block: K (i < kChunks/2) or V, row (i % 512) / 8, 16-byte
     // chunk i % 8. Rows past the split, the sequence or the cache read zero.
@@ -96,33 +105,48 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
         }
     };
 
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
     const int grp = lane >> 4, d0 = 8 * (lane & 15);  // value rows grp, grp+4, ...; dims d0..d0+7
     float m = -INFINITY, l = 0.0f;
     float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     u32x4 nxt[PER];
     if (r0 < r1) fetch(r0, nxt);
     for (int base = r0; base < r1; base += kRows) {
-        __syncthreads();  // the previous block is consumed (and qs written)
+        __syncthreads();  // the previous block is consumed
         stash(nxt);
         __syncthreads();
         if (base + kRows < r1) fetch(base + kRows, nxt);  // in flight during this block
-        // score of row base + lane
-        float sc = 0.0f;
+        // Scores of the block's 64 rows for the G heads: 16-row tiles, each
+        // dec(K) [16 x 128] . Q^T [128 x 16] as four bf16 MFMAs (the e4m3
+        // codes convert exactly to bf16; the products are exact in float32).
+        // Lane l of a tile reads row l % 16, dims 32 ks + 8 (l / 16) .. +7.
+        for (int tile = w; tile < kRows / 16; tile += G) {
+            f32x4 acc = f32x4{0, 0, 0, 0};
+            const int r = 16 * tile + (lane & 15);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + lane * kD + 16 * (c ^ (lane & 7)));
+            for (int ks = 0; ks < kD / 32; ++ks) {
+                const int c = 2 * ks + (lane >> 5);
+                const u32x2 raw = *reinterpret_cast<const u32x2*>(
+                    kb + r * kD + 16 * (c ^ (r & 7)) + 8 * ((lane >> 4) & 1));
+                const f32x2 x[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(raw[0], false),
+                                    __builtin_amdgcn_cvt_pk_f32_fp8(raw[0], true),
+                                    __builtin_amdgcn_cvt_pk_f32_fp8(raw[1], false),
+                                    __builtin_amdgcn_cvt_pk_f32_fp8(raw[1], true)};
+                u32x4 a;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const f32x4 qd = *reinterpret_cast<const f32x4*>(&qs[w][16 * c + 4 * e]);
-                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(kv[e], false);
-                const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(kv[e], true);
-                sc = fmaf(qd[0], lo[0], sc);
-                sc = fmaf(qd[1], lo[1], sc);
-                sc = fmaf(qd[2], hi[0], sc);
-                sc = fmaf(qd[3], hi[1], sc);
+                for (int e = 0; e < 4; ++e)
+                    a[e] = (__float_as_uint(x[e][0]) >> 16) | (__float_as_uint(x[e][1]) & 0xFFFF0000u);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                              __builtin_bit_cast(bf16x8, qf[ks]), acc,
+                                                              0, 0, 0);
+            }
+            // lane l holds rows 16 tile + 4 (l / 16) + i of head l % 16
+            if ((lane & 15) < G) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ss[lane & 15][16 * tile + 4 * (lane >> 4) + i] = acc[i];
             }
         }
+        __syncthreads();
+        const float sc = ss[w][lane] * qscale;  // score of row base + lane for head h
         const int64_t row = static_cast<int64_t>(first) + base + lane;
         const bool valid = base + lane < r1 && row >= 0 && row < p.rows;  // absent rows: no weight
         const float mn = fmaxf(m, wave_max(valid ? sc : -INFINITY));
