@@ -240,10 +240,11 @@ __global__ __launch_bounds__(kD) void attn_combine_kernel(AttnArgs p) {
 }  // namespace
 
 int attention_splits(int64_t B, int64_t Hkv, int64_t max_rows) {
-    // At least 256 rows per split, and enough workgroups for two per CU.
+    // At least 256 rows per split, and enough workgroups for eight per CU
+    // (sequences shorter than the longest leave their later splits empty).
     const int64_t by_rows = (max_rows + 255) / 256;
-    const int64_t by_grid = (1024 + B * Hkv - 1) / (B * Hkv);  // <= 1024 (kMaxSplits)
-    return static_cast<int>(std::max<int64_t>(1, std::min(by_rows, by_grid)));
+    const int64_t by_grid = (2048 + B * Hkv - 1) / (B * Hkv);
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(std::min(by_rows, by_grid), 1024)));
 }
 
 int attention_chunk(int64_t max_rows, int splits) {
