@@ -397,7 +397,9 @@ w8a8_status w8a8_requant_shared_scale(const void* w, int64_t ldw, w8a8_qtype qt,
 }
 
 int64_t kv_fp8_attention_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_seq_len) {
-    if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_seq_len < 0 || B > kMaxDim || Hq > kMaxDim || Hkv > kMaxDim)
+    // beyond the launch limits kv_fp8_decode_attention refuses the call (and
+    // the product below could overflow)
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_seq_len < 0 || B > 65535 || Hq > 65535 || Hkv > 65535)
         return 0;
     const int splits = w8a8::attention_splits(B, Hkv, max_seq_len);
     return B * Hq * splits * (128 + 2) * 4;
@@ -417,7 +419,7 @@ w8a8_status kv_fp8_decode_attention(void* out, const void* q, int64_t B, int64_t
     if (D != 128) return fail(W8A8_ERR_UNSUPPORTED, "%s: head dimension %lld (only 128)", fn, (long long)D);
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(W8A8_ERR_UNSUPPORTED, "%s: %lld query heads per KV head (1, 2, 4 or 8)", fn, (long long)G);
-    if (B > 65535 || Hkv > 65535 || Hq > kMaxDim || max_seq_len > kMaxDim || rows > kMaxDim)
+    if (B > 65535 || Hkv > 65535 || Hq > 65535 || max_seq_len > kMaxDim || rows > kMaxDim)
         return fail(W8A8_ERR_UNSUPPORTED, "%s: sizes beyond the launch limits", fn);
     if (!out || !q || !seq_starts || !workspace) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL out, q, seq_starts or workspace", fn);
     if (rows > 0 && (!k_cache || !v_cache)) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL cache", fn);

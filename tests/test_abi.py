@@ -132,6 +132,8 @@ def test_attention_validation(lib):
     assert call(st=FAKE + 2) == ALIGN
     assert call(B=0, out=None, q=None, w=None) == OK  # nothing to do
     assert lib.kv_fp8_attention_workspace_size(-1, 32, 8, 10) == 0
+    assert lib.kv_fp8_attention_workspace_size(2**40, 2**40, 8, 10) == 0  # no overflow
+    assert call(Hq=65536 * 8, Hkv=65536) == UNSUP
 
 
 def test_binding_layout_errors_are_python_errors():
