@@ -5,8 +5,8 @@
 //
 // One query token per sequence, D = 128, grouped-query heads (query head h
 // reads KV head h / G). Sequence b owns cache rows starts[b] .. starts[b+1]-1
-// of K and V [rows, Hkv, D]. Bound by the cache read from HBM (1 byte per
-// element), so the arithmetic is plain fp32 on the vector units:
+// of K and V [rows, Hkv, D]. The cache is read once (1 byte per element);
+// the scores run on the matrix cores, the rest in fp32 on the vector units:
 //  - attn_split_kernel: workgroup (split s, KV head g, sequence b), one wave
 //    per query head of the group, over the split's rows in blocks of 64.
 //    K and V blocks are staged in LDS (each loaded once for the G heads),
@@ -14,11 +14,10 @@
 //    consumed. The block's scores for all G heads are bf16 MFMAs (codes
 //    converted exactly to bf16, the query's own bf16 values, float32
 //    sums), scaled by sm_scale * k_scale; lane t of wave w then holds row
-//    t's score for head w, and the softmax runs online
-//    (running max m and sum l per wave), and lane l accumulates output dims
-//    8 (l % 16) .. +7 over rows l / 16, +4, +8, ... of each block (the
-//    weights through LDS); the four row groups are added once per split.
-//    Writes (o, m, l) per split.
+//    t's score for head w. The softmax runs online (running max m and sum l
+//    per wave), and lane l accumulates output dims 8 (l % 16) .. +7 over
+//    rows 16 (l / 16) .. +15 of each block (the weights through LDS); the
+//    four row groups are added once per split. Writes (o, m, l) per split.
 //  - attn_combine_kernel: per (sequence, head), the splits' partial sums
 //    rescaled to the common maximum, divided by the total weight, times
 //    v_scale, rounded to bf16.
