@@ -19,8 +19,9 @@
 //    rows 16 (l / 16) .. +15 of each block (the weights through LDS); the
 //    four row groups are added once per split. Writes (o, m, l) per split.
 //  - attn_combine_kernel: per (sequence, head), the splits' partial sums
-//    rescaled to the common maximum, divided by the total weight, times
-//    v_scale, rounded to bf16.
+//    rescaled to the common maximum (kept as a running maximum in one pass
+//    over the splits), divided by the total weight, times v_scale, rounded
+//    to bf16.
 #include <math.h>
 
 #include <algorithm>
@@ -35,6 +36,7 @@ namespace {
 constexpr int kD = 128;        // head dimension
 constexpr int kRows = 64;      // cache rows per block (one per lane)
 constexpr int kChunks = 2 * kRows * kD / 16;  // 16-byte pieces of one K + V block
+constexpr int kMaxSplits = 1024;  // row splits per sequence at most
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -62,6 +64,14 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
     const int first = p.starts[b];
     const int len = max(p.starts[b + 1] - first, 0);
     const int r0 = s * p.chunk, r1 = min(len, r0 + p.chunk);
+    float* dst = p.part + ((static_cast<int64_t>(b) * p.Hq + h) * p.splits + s) * (kD + 2);
+    if (r0 >= r1) {  // past the end of the sequence: no weight
+        if (lane == 0) {
+            dst[kD] = -INFINITY;
+            dst[kD + 1] = 0.0f;
+        }
+        return;
+    }
     const float qscale = p.sm_scale * (p.k_scale ? *p.k_scale : 1.0f);
     // The group's queries as the second operand of 16 x 16 x 32 bf16 MFMAs:
     // lane l holds query head l % 16 of the group (zeros past G), dims
@@ -108,7 +118,7 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
     float m = -INFINITY, l = 0.0f;
     float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     u32x4 nxt[PER];
-    if (r0 < r1) fetch(r0, nxt);
+    fetch(r0, nxt);
     for (int base = r0; base < r1; base += kRows) {
         __syncthreads();  // the previous block is consumed
         stash(nxt);
@@ -191,7 +201,6 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
         o[e] += __shfl_xor(o[e], 16, 64);
         o[e] += __shfl_xor(o[e], 32, 64);
     }
-    float* dst = p.part + ((static_cast<int64_t>(b) * p.Hq + h) * p.splits + s) * (kD + 2);
     if (lane < 16) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) dst[d0 + e] = o[e];
@@ -202,34 +211,24 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
     }
 }
 
-constexpr int kMaxSplits = 1024;  // attention_splits never gives more
-
 __global__ __launch_bounds__(kD) void attn_combine_kernel(AttnArgs p) {
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     const float* part = p.part + (static_cast<int64_t>(b) * p.Hq + h) * p.splits * (kD + 2);
-    // every split's maximum and weight, loaded side by side into LDS
-    __shared__ float sm[kMaxSplits], sl[kMaxSplits];
-    __shared__ float red[kD / 64];
-    float mx = -INFINITY;
-    for (int s = d; s < p.splits; s += kD) {
-        sm[s] = part[s * (kD + 2) + kD];
-        sl[s] = part[s * (kD + 2) + kD + 1];
-        mx = fmaxf(mx, sm[s]);
-    }
-    mx = wave_max(mx);
-    if ((d & 63) == 0) red[d >> 6] = mx;
-    __syncthreads();
-    mx = fmaxf(red[0], red[1]);
-    float tot = 0.0f, acc = 0.0f;
+    // One pass with a running maximum: the sums so far and each split's are
+    // rescaled to the larger of the two maxima as they are added. Splits with
+    // no weight are skipped (their partial sums may be unset).
+    float mx = -INFINITY, tot = 0.0f, acc = 0.0f;
 #pragma unroll 8
     for (int s = 0; s < p.splits; ++s) {
-        const float ls = sl[s];
-        const float v = part[s * (kD + 2) + d];
-        if (ls > 0.0f) {  // splits with no rows carry no weight
-            const float f = __expf(sm[s] - mx);
-            tot = fmaf(ls, f, tot);
-            acc = fmaf(v, f, acc);
-        }
+        const float* ps = part + s * (kD + 2);
+        const float ms = ps[kD], ls = ps[kD + 1], v = ps[d];
+        const bool live = ls > 0.0f;
+        const float mn = live ? fmaxf(mx, ms) : mx;
+        const float a = live ? __expf(mx - mn) : 1.0f;  // 0 while nothing is summed
+        const float f = live ? __expf(ms - mn) : 0.0f;
+        tot = live ? fmaf(ls, f, tot * a) : tot;
+        acc = live ? fmaf(v, f, acc * a) : acc;
+        mx = mn;
     }
     const float vs = p.v_scale ? *p.v_scale : 1.0f;
     const float o = tot > 0.0f ? acc / tot * vs : 0.0f;  // an empty sequence gives zeros
@@ -243,7 +242,7 @@ int attention_splits(int64_t B, int64_t Hkv, int64_t max_rows) {
     // (sequences shorter than the longest leave their later splits empty).
     const int64_t by_rows = (max_rows + 255) / 256;
     const int64_t by_grid = (2048 + B * Hkv - 1) / (B * Hkv);
-    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(std::min(by_rows, by_grid), 1024)));
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(std::min(by_rows, by_grid), kMaxSplits)));
 }
 
 int attention_chunk(int64_t max_rows, int splits) {
