@@ -546,12 +546,15 @@ __global__ __launch_bounds__(kBlock) void expand_shard_scales_kernel(const float
 }
 
 // One wave per row at a time (the row's shard, and so its ratio, is uniform
-// across the wave), 8 KB of the row in flight per wave. The shared scale is
+// across the wave), 2 KB of the row in flight per wave: the int8 encode keeps
+// many registers live, and the smaller unroll leaves room for more waves per
+// CU, which streams faster than more bytes per wave. The codes are written
+// with non-temporal stores (nothing reads them back soon). The shared scale is
 // the largest shard scale; the row's ratio t = s_i / s is rounded once to
 // binary32 (the double quotient of two binary32 values rounds to the same
 // binary32 value as the exact one: 53 >= 2 * 24 + 2 bits), and every code
 // becomes enc(fl32(dec(c) * t)).
-constexpr int kRequantUnroll = 8;  // 16-byte chunks per lane in flight
+constexpr int kRequantUnroll = 2;  // 16-byte chunks per lane in flight
 
 template <int QT>
 __device__ __forceinline__ uint32_t requant4(uint32_t c, float ratio) {
@@ -608,7 +611,7 @@ __global__ __launch_bounds__(kBlock) void requant_shared_kernel(const uint8_t* _
                 u32x4 q;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) q[j] = requant4<QT>(c[u][j], ratio);
-                *reinterpret_cast<u32x4*>(dst + k0 + 1024 * u) = q;
+                __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(dst + k0 + 1024 * u));
             }
         }
     }
