@@ -374,8 +374,10 @@ hipError_t per_tensor_typed(const void* x, int64_t M, int64_t K, int64_t ldx, ui
         const int64_t tail_len = (4 * static_cast<int64_t>(tail.parts) + 15) / 16 * 16;
         tail.start = total <= 65536 ? 0 : total - tail_len;
         hipLaunchKernelGGL((absmax_kernel<XT>), dim3(tail.parts), dim3(kBlock), 0, st, x, ldx, u, K, q, ldq, tail);
+        // at most 8 workgroups per CU: each reduces the partials once, then
+        // strides over the units
         if (tail.start > 0)
-            hipLaunchKernelGGL((quant_tensor_kernel<XT, QT, true>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, static_cast<const float*>(scale), u, K, tail);
+            hipLaunchKernelGGL((quant_tensor_kernel<XT, QT, true>), dim3(std::min(g, 2048)), dim3(kBlock), 0, st, x, ldx, q, ldq, static_cast<const float*>(scale), u, K, tail);
         hipLaunchKernelGGL((finish_tail_kernel<XT, QT>), dim3(1), dim3(kBlock), 0, st, x, ldx, q, ldq, scale, M, K, tail);
     } else {
         hipLaunchKernelGGL((quant_tensor_kernel<XT, QT, false>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, static_cast<const float*>(scale), u, K, Tail{0, 0});
