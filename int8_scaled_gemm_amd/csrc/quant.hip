@@ -244,45 +244,49 @@ __global__ __launch_bounds__(kBlock) void finish_tail_kernel(const void* __restr
 }
 
 // ------------------------------------------------------------------------
-// KV dequant: 16 codes per lane (one 16-byte load), product in float32,
-// rounded once into the output type.
+// KV dequant: 8 codes per lane (one 8-byte load), product in float32,
+// rounded once into the output type. A 2-byte output is one 16-byte
+// non-temporal store per lane, so that each store instruction of a wave
+// writes 1 KB of whole cache lines (16 codes per lane wrote two 16-byte
+// pieces 32 bytes apart, each instruction leaving every other piece to the
+// next); float32 output is two 16-byte stores per lane, cached.
 // ------------------------------------------------------------------------
 template <int XT>
 __global__ __launch_bounds__(kBlock) void kv_dequant_kernel(const uint8_t* __restrict__ q,
                                                             int64_t n,
                                                             const float* __restrict__ scale,
                                                             void* __restrict__ x) {
+    constexpr int U = 2 * kUnroll;  // 8-byte loads in flight per lane
     const float s = scale ? *scale : 1.0f;
-    const int64_t nvec = n / 16;
-    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * kUnroll + threadIdx.x;
-         base < nvec; base += static_cast<int64_t>(gridDim.x) * kBlock * kUnroll) {
-        u32x4 c[kUnroll];
+    const int64_t nvec = n / 8;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * U + threadIdx.x;
+         base < nvec; base += static_cast<int64_t>(gridDim.x) * kBlock * U) {
+        u32x2 c[U];
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
+        for (int j = 0; j < U; ++j) {
             const int64_t i = base + j * kBlock;
-            if (i < nvec) c[j] = reinterpret_cast<const u32x4*>(q)[i];
+            if (i < nvec) c[j] = reinterpret_cast<const u32x2*>(q)[i];
         }
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
+        for (int j = 0; j < U; ++j) {
             const int64_t i = base + j * kBlock;
             if (i >= nvec) continue;
-            float f[16];
+            float f[8];
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < 2; ++w) {
                 f[4 * w + 0] = __builtin_amdgcn_cvt_f32_fp8(c[j][w], 0) * s;
                 f[4 * w + 1] = __builtin_amdgcn_cvt_f32_fp8(c[j][w], 1) * s;
                 f[4 * w + 2] = __builtin_amdgcn_cvt_f32_fp8(c[j][w], 2) * s;
                 f[4 * w + 3] = __builtin_amdgcn_cvt_f32_fp8(c[j][w], 3) * s;
             }
             if constexpr (XT == D_F32) {
-                f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(x) + i * 16);
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    o[w] = f32x4{f[4 * w], f[4 * w + 1], f[4 * w + 2], f[4 * w + 3]};
+                f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(x) + i * 8);
+                o[0] = f32x4{f[0], f[1], f[2], f[3]};
+                o[1] = f32x4{f[4], f[5], f[6], f[7]};
             } else {
-                u32x4 o[2];
+                u32x4 o;
 #pragma unroll
-                for (int w = 0; w < 8; ++w) {
+                for (int w = 0; w < 4; ++w) {
                     uint32_t lo, hi;
                     if constexpr (XT == D_BF16) {
                         lo = to_bf16_bits(f[2 * w]);
@@ -291,11 +295,9 @@ __global__ __launch_bounds__(kBlock) void kv_dequant_kernel(const uint8_t* __res
                         lo = to_fp16_bits(f[2 * w]);
                         hi = to_fp16_bits(f[2 * w + 1]);
                     }
-                    o[w / 4][w % 4] = lo | (hi << 16);
+                    o[w] = lo | (hi << 16);
                 }
-                u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(x) + i * 16);
-                dst[0] = o[0];
-                dst[1] = o[1];
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(x) + i * 8));
             }
         }
     }
