@@ -212,6 +212,23 @@ def test_kv_dequant_all_codes(otype):
         assert np.isnan(y.float().cpu().numpy()[nan]).all()
 
 
+@pytest.mark.parametrize("otype", ["bf16", "fp16", "f32"])
+def test_kv_dequant_ragged_length(otype):
+    """Random valid codes, a length that ends part-way through a workgroup
+    step (16 x 12347 codes), every output type: bit-exact."""
+    n = 16 * 12347
+    codes = workloads.random_codes((n,), "fp8", seed=31).numpy()
+    qd = torch.from_numpy(codes).to(DEV).view(torch.float8_e4m3fn)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "f32": torch.float32}[otype]
+    st = torch.tensor([0.0371], dtype=torch.float32, device=DEV)
+    y = w8.kv_fp8_scaled_dequant(qd, st, tdt)
+    torch.cuda.synchronize()
+    y_ref = oracle.kv_dequant(codes, np.float32(0.0371), otype)
+    if otype == "f32":
+        y_ref = y_ref.view(np.uint32)
+    assert np.array_equal(bits(y), y_ref)
+
+
 def test_kv_static_scale_and_fp16_input():
     x = workloads.kv_tensor(3, "v", shape=(64, 8, 128)).to(torch.float16)
     xh = x.view(torch.int16).numpy().view(np.uint16).reshape(-1)
