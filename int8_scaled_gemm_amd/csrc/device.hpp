@@ -33,25 +33,28 @@ struct QMax<Q_INT8> {
 // ------------------------------------------------------------------ loads
 // Eight consecutive high-precision elements starting at element `idx`
 // (16-byte aligned for 2-byte types, 32-byte for float32), widened to float.
-template <int XT>
+// NT: non-temporal loads, for data read once (the stream does not evict
+// reused lines); else cached, for data that a later pass reads again.
+template <typename T>
+__device__ __forceinline__ T load16(const T* p, bool nt) {
+    return nt ? __builtin_nontemporal_load(p) : *p;
+}
+template <int XT, bool NT = true>
 __device__ __forceinline__ void load8(const void* base, int64_t idx, float v[8]) {
     if constexpr (XT == D_BF16) {
-        // read once: non-temporal, so the stream does not evict reused lines
-        u32x4 r = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + idx));
+        u32x4 r = load16(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + idx), NT);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             v[2 * i] = __uint_as_float(r[i] << 16);
             v[2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
         }
     } else if constexpr (XT == D_FP16) {
-        h16x8 h = __builtin_nontemporal_load(
-            reinterpret_cast<const h16x8*>(static_cast<const uint16_t*>(base) + idx));
+        h16x8 h = load16(reinterpret_cast<const h16x8*>(static_cast<const uint16_t*>(base) + idx), NT);
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = static_cast<float>(h[i]);
     } else {
         const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
-        f32x4 lo = __builtin_nontemporal_load(p), hi = __builtin_nontemporal_load(p + 1);
+        f32x4 lo = load16(p, NT), hi = load16(p + 1, NT);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             v[i] = lo[i];

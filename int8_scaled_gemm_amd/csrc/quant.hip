@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kBlock) void absmax_kernel(const void* __restrict__
         for (int j = 0; j < kAbsUnroll; ++j) {
             int64_t row, k;
             ok[j] = unit_coords(u, base + j, K, row, k);
-            if (ok[j]) load8<XT>(x, row * ldx + k, v[j]);
+            if (ok[j]) load8<XT, false>(x, row * ldx + k, v[j]);  // cached: read again next
         }
 #pragma unroll
         for (int j = 0; j < kAbsUnroll; ++j)
