@@ -34,7 +34,10 @@ scaled-product kernel (KV: the quant call) that takes the most time per step
 events on the launch stream), the same figures for every kernel, and the CPU
 oracle timed on a bounded sample of the same workload. The roofline's `traffic` is the HBM traffic per launch from
 the rocprofv3 FETCH_SIZE / WRITE_SIZE record under profiles/, when that record
-was taken from the current kernel sources (else null).
+was taken from the current kernel sources (else null). `clock` is the graphics
+clock (amdsmi) while the roofline kernel's launches replay back to back; an
+MFMA-bound roofline entry is also given against the peak scaled to that clock
+(`peak_at_clock`, `frac_at_clock`).
 
     python bench.py --copy-calibration
 
@@ -47,6 +50,7 @@ import argparse
 import json
 import os
 import sys
+import threading
 import time
 
 import torch
@@ -61,6 +65,7 @@ import workloads  # noqa: E402
 METRIC = "scaled_mm TFLOP/s (fp8/int8) at Llama-3-8B shapes; % of MFMA / HBM roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "int8": 5000.0}
+SPEC_GFX_MHZ = 2400.0  # the clock the published matrix-core peaks are quoted at
 
 
 def log(*a):
@@ -313,6 +318,90 @@ def time_graph(g, stream, reps):
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) / reps, time.perf_counter() - t0
+
+
+def gfx_clock_reader():
+    """A function returning (refresh counter, graphics clocks in MHz, one per
+    XCD) of the GPU torch sees as device 0, from the power management
+    metrics table read through amdsmi, and a function that closes amdsmi;
+    None where amdsmi or the device is not available."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+    except Exception:
+        return None
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+        pick = [h for h in handles
+                if bus is not None and int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == int(bus)]
+        h = pick[0] if pick else (handles[0] if len(handles) == 1 else None)
+        if h is None:
+            amdsmi.amdsmi_shut_down()
+            return None
+
+        def read():
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            clks = m.get("current_gfxclks")
+            clks = clks if isinstance(clks, list) else [m.get("current_gfxclk")]
+            return (m.get("system_clock_counter"),
+                    [float(c) for c in clks if isinstance(c, (int, float)) and 0 < c < 10000])
+        read()
+        return read, amdsmi.amdsmi_shut_down
+    except Exception:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+        return None
+
+
+def clock_under_load(g, stream, replay_s, seconds=2.5, settle_s=0.3, period_s=0.02):
+    """Graphics clock while graph `g` replays back to back for `seconds`.
+    The metrics table behind it is refreshed about once a second, so the
+    reading is the mean over the XCDs of each distinct refresh first seen at
+    least `settle_s` after the load started. None without amdsmi or without
+    such a refresh."""
+    rc = gfx_clock_reader()
+    if rc is None:
+        return None
+    read, close = rc
+    refreshes, seen, stop = [], set(), threading.Event()
+    t_start = time.perf_counter()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                counter, clks = read()
+            except Exception:
+                return
+            if counter not in seen:
+                seen.add(counter)
+                if clks and time.perf_counter() - t_start >= settle_s:
+                    refreshes.append(sum(clks) / len(clks))
+            time.sleep(period_s)
+
+    seen.add(read()[0])  # the table as it stood before the load
+    batch = max(1, int(0.02 / max(replay_s, 1e-6)))  # about 20 ms of replays per batch
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    try:
+        while time.perf_counter() - t_start < seconds:
+            for _ in range(batch):
+                g.replay()
+            stream.synchronize()
+    finally:
+        stop.set()
+        th.join()
+        close()
+    if not refreshes:
+        return None
+    return {"gfx_mhz_mean": round(sum(refreshes) / len(refreshes), 1),
+            "gfx_mhz_min": round(min(refreshes), 1), "gfx_mhz_max": round(max(refreshes), 1),
+            "refreshes": len(refreshes), "spec_mhz": SPEC_GFX_MHZ,
+            "source": "amdsmi gpu metrics current_gfxclks (mean over the XCDs), each refresh of the "
+                      "table (about 1 per second) taken from 0.3 s after the roofline kernel's "
+                      "launches began replaying back to back, over 2.5 s"}
 
 
 def source_digest():
@@ -584,6 +673,15 @@ def main():
     dom = max((k for k in kernels if kinds[k] == main_kind),
               key=lambda k: kernels[k]["avg_s"] * kernels[k]["launches"])
     roof = roofline(dom, kernels[dom], spec, args.workload)
+    # The clock the roofline kernel runs at: the matrix-core peak scales with
+    # it (HBM bandwidth does not), so an MFMA-bound entry is also given
+    # against the peak at the measured clock.
+    g_dom = capture([L for L in launches if L.kernel == dom], stream)
+    g_dom.replay()
+    clock = clock_under_load(g_dom, stream, kernels[dom]["avg_s"] * kernels[dom]["launches"])
+    if clock is not None and roof["bound"] == "mfma":
+        peak_clk = roof["peak"] * clock["gfx_mhz_mean"] / SPEC_GFX_MHZ
+        roof.update(peak_at_clock=round(peak_clk, 1), frac_at_clock=round(roof["achieved"] / peak_clk, 4))
 
     if args.detail:
         # per-launch times: each launch alone, graph of 10 back-to-back copies
@@ -615,6 +713,7 @@ def main():
                    "step_bytes": per_step_bytes, "step_flops": per_step_flops,
                    "launches_per_step": len(launches), "parallelism": "single GPU"},
         "roofline": roof,
+        "clock": clock,
         "kernels": {n: {"launches_per_step": k["launches"],
                         "avg_launch_us": round(k["avg_s"] * 1e6, 3),
                         "hbm_frac": round(k["nbytes"] / k["avg_s"] / 1e9 / HBM_PEAK_GBS, 4),
