@@ -400,8 +400,8 @@ def clock_under_load(g, stream, replay_s, seconds=2.5, settle_s=0.3, period_s=0.
             "gfx_mhz_min": round(min(refreshes), 1), "gfx_mhz_max": round(max(refreshes), 1),
             "refreshes": len(refreshes), "spec_mhz": SPEC_GFX_MHZ,
             "source": "amdsmi gpu metrics current_gfxclks (mean over the XCDs), each refresh of the "
-                      "table (about 1 per second) taken from 0.3 s after the roofline kernel's "
-                      "launches began replaying back to back, over 2.5 s"}
+                      "table (about 1 per second) taken from %.1f s after the roofline kernel's "
+                      "launches began replaying back to back, over %.1f s" % (settle_s, seconds)}
 
 
 def source_digest():
@@ -574,6 +574,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0: skip)")
     ap.add_argument("--detail", action="store_true", help="per-launch times on stderr")
+    ap.add_argument("--clock-seconds", type=float, default=2.5,
+                    help="seconds of back-to-back replays of the roofline kernel during which "
+                         "the graphics clock is read (0: no clock reading)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 256 MiB on the device 4 times (counter calibration)")
     args = ap.parse_args()
@@ -676,9 +679,11 @@ def main():
     # The clock the roofline kernel runs at: the matrix-core peak scales with
     # it (HBM bandwidth does not), so an MFMA-bound entry is also given
     # against the peak at the measured clock.
-    g_dom = capture([L for L in launches if L.kernel == dom], stream)
-    g_dom.replay()
-    clock = clock_under_load(g_dom, stream, kernels[dom]["avg_s"] * kernels[dom]["launches"])
+    g_dom = capture([L for L in launches if L.kernel == dom], stream) if args.clock_seconds > 0 else None
+    if g_dom is not None:
+        g_dom.replay()
+    clock = None if args.clock_seconds <= 0 else clock_under_load(
+        g_dom, stream, kernels[dom]["avg_s"] * kernels[dom]["launches"], seconds=args.clock_seconds)
     if clock is not None and roof["bound"] == "mfma":
         peak_clk = roof["peak"] * clock["gfx_mhz_mean"] / SPEC_GFX_MHZ
         roof.update(peak_at_clock=round(peak_clk, 1), frac_at_clock=round(roof["achieved"] / peak_clk, 4))
