@@ -19,9 +19,10 @@
  *    "Scaling semantics": scale = absmax / 448 (the e4m3 max-norm),
  *    q = fp8_quant(x / scale), x' = fp8_dequant(q) * scale, per tensor; and
  *    the review answers on the same page: no scale given means scale 1.0.
- *  - the same page's note that the asymmetric int8 case needs small
- *    operations fused onto the GEMM: zero points per token, the weights'
- *    code sums, D = s_a s_b (acc - z colsum) (textbook asymmetric scheme).
+ *  - "[Kernel] Add w8a8 CUTLASS kernels" again, its remark that the
+ *    asymmetric int8 case needs small operations fused onto the GEMM: zero
+ *    points per token or per tensor, the weights' code sums,
+ *    D = s_a s_b (acc - z colsum) (the textbook asymmetric scheme).
  *  - "[Kernel] Support Fp8 Checkpoints (Dynamic + Static)" (vLLM PR 4332):
  *    merged layers (QKV, gate_up) whose shards carry their own weight
  *    scales; a review comment there proposes one shared scale max(s_i) with

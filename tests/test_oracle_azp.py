@@ -108,3 +108,74 @@ def test_scaled_mm_azp_is_the_dequantised_product():
     assert np.allclose(d, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
     sym = oracle.scaled_mm(a, b, "int8", sa, sb, "f64")
     assert np.array_equal(oracle.scaled_mm_azp(a, b, sa, None, sb, "f64"), sym)
+
+
+# Rows whose range hi - lo is 255 * 2^j make the scale the power of two 2^j
+# exactly, so x / s and -128 - lo / s are exact and can be placed on a tie
+# (a value half-way between two integers). The codes below are worked out by
+# hand with round-half-to-even at each tie; rounding half away from zero
+# gives a different zero point or code in every row.
+TIE_ROWS = [
+    # (row values, scale, zero point, codes)
+    # lo = -127.5, hi = 127.5: s = 1, -128 - lo / s = -0.5 -> z = 0 (away: -1)
+    ([-127.5, 127.5, 2.5, -0.5, 1.5, 3.5, 0.5, -2.5],
+     1.0, 0, [-128, 127, 2, 0, 2, 4, 0, -2]),
+    # lo = -64, hi = 191: s = 1, z = -64 exactly; ties in x / s only
+    ([-64.0, 191.0, 2.5, -0.5, 0.5, 1.5, -1.5, 0.0],
+     1.0, -64, [-128, 127, -62, -64, -64, -62, -66, -64]),
+    # lo = -255, hi = 255: s = 2, -128 - lo / s = -0.5 -> z = 0; x / s ties
+    ([-255.0, 255.0, 5.0, 3.0, -1.0, 1.0, -3.0, 7.0],
+     2.0, 0, [-128, 127, 2, 2, 0, 0, -2, 4]),
+    # lo = -31.875, hi = 0: s = 0.125, -128 - lo / s = -128 + 255 = 127 -> z = 127;
+    # x / s = -0.5 -> 0 -> code 127, -1.5 -> -2 -> 125, -126.5 -> -126 -> 1
+    ([-31.875, 0.0, -0.0625, -0.1875, -0.3125, -15.8125, -0.125, -8.0625],
+     0.125, 127, [-128, 127, 127, 125, 125, 1, 126, 63]),
+]
+
+
+@pytest.mark.parametrize("row", range(len(TIE_ROWS)))
+@pytest.mark.parametrize("xtype", ["f32", "bf16"])
+def test_azp_quant_ties_round_half_even(row, xtype):
+    vals, s, z, codes = TIE_ROWS[row]
+    x = np.array([vals], np.float32)
+    if xtype == "bf16":
+        # every value above has at most 8 significant bits: bf16 holds it exactly
+        h = (x.view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal((h.astype(np.uint32) << 16).view(np.float32), x)
+        q, sc, zp = oracle.quant_per_token_azp(h, "bf16")
+    else:
+        q, sc, zp = oracle.quant_per_token_azp(x, "f32")
+    assert sc[0] == np.float32(s)
+    assert zp[0] == z
+    assert q.view(np.int8)[0].tolist() == codes
+
+
+def test_colsum_closed_forms():
+    """Rows with a closed-form sum: a constant row c sums to c * K, the ramp
+    -64..63 repeated sums to -K / 2 (each 128-code period sums to -64), a row
+    and its negation sum to 0, and the extremes -128 and 127 do not wrap."""
+    K = 4096
+    rows = np.zeros((6, K), np.int8)
+    rows[0] = 7
+    rows[1] = -128
+    rows[2] = 127
+    rows[3] = (np.arange(K) % 128 - 64).astype(np.int8)
+    rows[4] = workloads.random_codes((1, K), "int8", seed=11).numpy().view(np.int8)[0]
+    rows[4][rows[4] == -128] = -127
+    rows[5] = -rows[4]
+    cs = oracle.colsum(rows.view(np.uint8))
+    assert cs[0] == 7 * K and cs[1] == -128 * K and cs[2] == 127 * K
+    assert cs[3] == -(K // 2)
+    assert cs[4] + cs[5] == 0
+
+
+def test_colsum_brute_force_tiny():
+    """Small weights summed one code at a time in Python integers."""
+    b = workloads.random_codes((5, 48), "int8", seed=12).numpy()
+    cs = oracle.colsum(b)
+    for n in range(5):
+        total = 0
+        for k in range(48):
+            c = int(b[n, k])
+            total += c - 256 if c >= 128 else c
+        assert cs[n] == total
