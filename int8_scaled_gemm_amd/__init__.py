@@ -15,7 +15,9 @@ Functions carry the C names:
 * ``kv_fp8_decode_attention(q, k_cache, v_cache, seq_starts, max_seq_len, k_scale, v_scale)``
   -> ``out`` (decode attention reading the fp8 cache)
 
-plus ``scaled_mm(a, b, scale_a, scale_b, out_dtype)``, the call shape of
+plus the short names ``quant_per_token(x, qtype)``, ``quant_per_tensor(x,
+qtype, scale, dynamic)``, ``kv_quant(x)``, ``kv_dequant(q, scale)`` and
+``scaled_mm(a, b, scale_a, scale_b, out_dtype)``, the call shape of
 ``cutlass_scaled_mm_dq`` in "[Kernel] Add w8a8 CUTLASS kernels" (the usage
 snippet of its misaligned-address report), where ``b`` is a K x N
 column-major view such as ``weight.t()``.
@@ -136,6 +138,34 @@ def _check_cuda(*ts):
             raise ValueError("libw8a8 operates on GPU tensors only")
 
 
+def _same_device(ref: torch.Tensor, *ts):
+    for t in ts:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"libw8a8: tensors on {ref.device} and {t.device}")
+
+
+def _want(t, what: str, *, shape=None, numel=None, dtypes=None, contiguous: bool = False):
+    """Check a caller-supplied tensor before its pointer goes to the C ABI,
+    which cannot see its size: an undersized or mistyped buffer would be
+    written past its end by the kernels."""
+    if t is None:
+        return
+    if dtypes is not None and t.dtype not in dtypes:
+        names = ", ".join(str(d) for d in dtypes)
+        raise ValueError(f"{what} must have dtype {names}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() not in ((numel,) if isinstance(numel, int) else numel):
+        raise ValueError(f"{what} must have {numel} elements, got {t.numel()}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+_F32, _I32 = (torch.float32,), (torch.int32,)
+_OUT_DTYPES = (torch.bfloat16, torch.float16, torch.float32, torch.int32)
+_X_DTYPES = (torch.bfloat16, torch.float16, torch.float32)
+
+
 def _rows(t: torch.Tensor, what: str):
     """(rows, cols, leading dimension) of a 2-D tensor with unit column stride."""
     if t.dim() != 2:
@@ -166,9 +196,13 @@ def _dtype(dt) -> int:
 def w8a8_quant_per_token(x: torch.Tensor, qtype="fp8", q: torch.Tensor | None = None,
                          scales: torch.Tensor | None = None):
     """Dynamic per-token quantisation of x [M, K] -> (codes [M, K], scales fp32 [M])."""
-    _check_cuda(x, q, scales)
     qt = _qtype(qtype)
     M, K, ldx = _rows(x, "x")
+    _want(x, "x", dtypes=_X_DTYPES)
+    _want(q, "q", shape=(M, K), dtypes=(CODE_DTYPE[qt],))
+    _want(scales, "scales", numel=M, dtypes=_F32, contiguous=True)
+    _check_cuda(x, q, scales)
+    _same_device(x, q, scales)
     if q is None:
         q = torch.empty((M, K), dtype=CODE_DTYPE[qt], device=x.device)
     if scales is None:
@@ -183,9 +217,13 @@ def w8a8_quant_per_tensor(x: torch.Tensor, qtype="fp8", scale: torch.Tensor | No
                           dynamic: bool = False, q: torch.Tensor | None = None):
     """Per-tensor quantisation. Static (dynamic=False) uses ``scale`` (None means 1.0);
     dynamic computes absmax/Qmax into ``scale`` (allocated when None)."""
-    _check_cuda(x, q, scale)
     qt = _qtype(qtype)
     M, K, ldx = _rows(x, "x")
+    _want(x, "x", dtypes=_X_DTYPES)
+    _want(q, "q", shape=(M, K), dtypes=(CODE_DTYPE[qt],))
+    _want(scale, "scale", numel=1, dtypes=_F32)
+    _check_cuda(x, q, scale)
+    _same_device(x, q, scale)
     if q is None:
         q = torch.empty((M, K), dtype=CODE_DTYPE[qt], device=x.device)
     if dynamic and scale is None:
@@ -199,9 +237,13 @@ def w8a8_quant_per_tensor(x: torch.Tensor, qtype="fp8", scale: torch.Tensor | No
 def kv_fp8_scaled_quant(x: torch.Tensor, scale: torch.Tensor | None = None,
                         dynamic: bool = True, q: torch.Tensor | None = None):
     """Scaled fp8 KV-cache quantisation of a contiguous tensor (any shape)."""
-    _check_cuda(x, q, scale)
     if not x.is_contiguous():
         raise ValueError("kv_fp8_scaled_quant needs a contiguous tensor")
+    _want(x, "x", dtypes=_X_DTYPES)
+    _want(q, "q", numel=x.numel(), dtypes=(torch.float8_e4m3fn,), contiguous=True)
+    _want(scale, "scale", numel=1, dtypes=_F32)
+    _check_cuda(x, q, scale)
+    _same_device(x, q, scale)
     if q is None:
         q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
     if dynamic and scale is None:
@@ -214,9 +256,13 @@ def kv_fp8_scaled_quant(x: torch.Tensor, scale: torch.Tensor | None = None,
 def kv_fp8_scaled_dequant(q: torch.Tensor, scale: torch.Tensor | None,
                           out_dtype=torch.bfloat16, out: torch.Tensor | None = None):
     """x' = dequant(q) * scale, rounded into out_dtype."""
-    _check_cuda(q, scale, out)
     if not q.is_contiguous():
         raise ValueError("kv_fp8_scaled_dequant needs a contiguous tensor")
+    _want(q, "q", dtypes=(torch.float8_e4m3fn, torch.uint8))
+    _want(scale, "scale", numel=1, dtypes=_F32)
+    _want(out, "out", numel=q.numel(), dtypes=_X_DTYPES, contiguous=True)
+    _check_cuda(q, scale, out)
+    _same_device(q, scale, out)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     _call("kv_fp8_scaled_dequant", _ptr(q), q.numel(), _ptr(scale), _ptr(out),
@@ -237,7 +283,6 @@ def kv_fp8_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     """Decode attention over an e4m3fn KV cache: q [B, Hq, D] bf16, caches
     [rows, Hkv, D] e4m3fn, seq_starts [B + 1] int32 (sequence b owns cache
     rows seq_starts[b] .. seq_starts[b+1]-1) -> out [B, Hq, D] bf16."""
-    _check_cuda(q, k_cache, v_cache, seq_starts, k_scale, v_scale, out, workspace)
     for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         if t.dim() != 3 or not t.is_contiguous():
             raise ValueError(f"kv_fp8_decode_attention: {name} must be a contiguous 3-d tensor")
@@ -249,11 +294,23 @@ def kv_fp8_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     rows, Hkv, Dk = k_cache.shape
     if Dk != D or seq_starts.numel() != B + 1:
         raise ValueError("kv_fp8_decode_attention: head dimension or seq_starts length mismatch")
+    _want(k_cache, "k_cache", dtypes=(torch.float8_e4m3fn, torch.uint8))
+    _want(v_cache, "v_cache", dtypes=(torch.float8_e4m3fn, torch.uint8))
+    _want(seq_starts, "seq_starts", contiguous=True)
+    _want(k_scale, "k_scale", numel=1, dtypes=_F32)
+    _want(v_scale, "v_scale", numel=1, dtypes=_F32)
+    _want(out, "out", shape=(B, Hq, D), dtypes=(torch.bfloat16,), contiguous=True)
+    _want(workspace, "workspace", contiguous=True)
+    _check_cuda(q, k_cache, v_cache, seq_starts, k_scale, v_scale, out, workspace)
+    _same_device(q, k_cache, v_cache, seq_starts, k_scale, v_scale, out, workspace)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
     need = kv_fp8_attention_workspace_size(B, Hq, Hkv, max_seq_len)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                         f"the call needs {need}")
     _call("kv_fp8_decode_attention", _ptr(out), _ptr(q), B, Hq, Hkv, D, _ptr(k_cache),
           _ptr(v_cache), rows, _ptr(seq_starts), max_seq_len, _ptr(k_scale), _ptr(v_scale),
           float(sm_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -266,8 +323,13 @@ def w8a8_quant_per_token_azp(x: torch.Tensor, q: torch.Tensor | None = None,
                              scales: torch.Tensor | None = None, azp: torch.Tensor | None = None):
     """Asymmetric per-token int8 quantisation of x [M, K] -> (codes int8
     [M, K], scales fp32 [M], zero points int32 [M]), x ~ (q - z) * s."""
-    _check_cuda(x, q, scales, azp)
     M, K, ldx = _rows(x, "x")
+    _want(x, "x", dtypes=_X_DTYPES)
+    _want(q, "q", shape=(M, K), dtypes=(torch.int8,))
+    _want(scales, "scales", numel=M, dtypes=_F32, contiguous=True)
+    _want(azp, "azp", numel=M, dtypes=_I32, contiguous=True)
+    _check_cuda(x, q, scales, azp)
+    _same_device(x, q, scales, azp)
     if q is None:
         q = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if scales is None:
@@ -282,10 +344,12 @@ def w8a8_quant_per_token_azp(x: torch.Tensor, q: torch.Tensor | None = None,
 
 def w8a8_colsum(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Per-row sums of int8 weight codes w [N, K] (int32 [N])."""
-    _check_cuda(w, out)
     if w.dtype != torch.int8:
         raise ValueError("w8a8_colsum takes int8 codes")
     N, K, ldw = _rows(w, "w")
+    _want(out, "out", numel=N, dtypes=_I32, contiguous=True)
+    _check_cuda(w, out)
+    _same_device(w, out)
     if out is None:
         out = torch.empty(N, dtype=torch.int32, device=w.device)
     _call("w8a8_colsum", _ptr(w), ldw, N, K, _ptr(out), _stream(w))
@@ -299,7 +363,6 @@ def w8a8_scaled_mm_azp(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor 
     """D = a_scales (x) b_scales * ((a - azp) @ b) for int8 codes; b and the
     scales as in w8a8_scaled_mm, azp int32 [1] or [M], colsum =
     w8a8_colsum(weight) for b = weight.t()."""
-    _check_cuda(a, b, a_scales, azp, colsum, b_scales, out)
     if a.dtype != torch.int8 or b.dtype != torch.int8:
         raise ValueError("w8a8_scaled_mm_azp takes int8 codes")
     M, K, lda = _rows(a, "a")
@@ -309,6 +372,14 @@ def w8a8_scaled_mm_azp(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor 
     if b.size(0) > 1 and b.stride(0) != 1:
         raise ValueError("b must be column-major (K x N with stride(0) == 1), e.g. weight.t()")
     ldb = b.stride(1) if N > 1 else max(K, b.stride(1))
+    _want(out, "out", shape=(M, N), dtypes=_OUT_DTYPES)
+    _want(a_scales, "a_scales", numel=(1, M))
+    _want(b_scales, "b_scales", numel=(1, N))
+    _want(azp, "azp", numel=(1, M))
+    if azp is not None:
+        _want(colsum, "colsum", numel=N, dtypes=_I32, contiguous=True)
+    _check_cuda(a, b, a_scales, azp, colsum, b_scales, out)
+    _same_device(a, b, a_scales, azp, colsum, b_scales, out)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     _, _, ldo = _rows(out, "out")
@@ -335,10 +406,12 @@ def w8a8_expand_shard_scales(shard_scales: torch.Tensor, shard_rows,
                              out: torch.Tensor | None = None) -> torch.Tensor:
     """Per-channel weight scales of a merged layer: shard i's scale on each of
     its shard_rows[i] rows (float32 [N] on the device)."""
-    _check_cuda(shard_scales, out)
     rows, S, N = _shard_rows(shard_rows)
     if shard_scales.dtype != torch.float32 or not shard_scales.is_contiguous() or shard_scales.numel() != S:
         raise ValueError("shard_scales must be a contiguous float32 tensor with one entry per shard")
+    _want(out, "out", numel=N, dtypes=_F32, contiguous=True)
+    _check_cuda(shard_scales, out)
+    _same_device(shard_scales, out)
     if out is None:
         out = torch.empty(N, dtype=torch.float32, device=shard_scales.device)
     _call("w8a8_expand_shard_scales", _ptr(shard_scales), rows, S, _ptr(out), _stream(shard_scales))
@@ -351,7 +424,6 @@ def w8a8_requant_shared_scale(w: torch.Tensor, shard_rows, shard_scales: torch.T
     """Codes of a merged weight [N, K] (float8_e4m3fn or int8) rescaled to one
     shared scale max(shard_scales). out may be w (in place). Returns
     (out, shared_scale) with shared_scale a float32 [1] device tensor."""
-    _check_cuda(w, shard_scales, out, shared_scale)
     qt = _qtype(w.dtype)
     N, K, ldw = _rows(w, "w")
     rows, S, n = _shard_rows(shard_rows)
@@ -363,6 +435,9 @@ def w8a8_requant_shared_scale(w: torch.Tensor, shard_rows, shard_scales: torch.T
         out = torch.empty((N, K), dtype=w.dtype, device=w.device)
     if out.dtype != w.dtype or tuple(out.shape) != (N, K):
         raise ValueError("out must match w in dtype and shape")
+    _want(shared_scale, "shared_scale", numel=1, dtypes=_F32)
+    _check_cuda(w, shard_scales, out, shared_scale)
+    _same_device(w, shard_scales, out, shared_scale)
     _, _, ldo = _rows(out, "out")
     if K == 0:
         ldw = ldo = 0  # no columns: the strides are never used
@@ -394,7 +469,6 @@ def w8a8_scaled_mm(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | No
     w8a8_scaled_mm_workspace_size(M, N, K) bytes the call goes through
     w8a8_scaled_mm_ws and may split K.
     """
-    _check_cuda(a, b, a_scales, b_scales, out)
     qt = _qtype(a.dtype)
     if b.dtype != a.dtype:
         raise ValueError(f"a and b must share a code type, got {a.dtype} and {b.dtype}")
@@ -405,6 +479,12 @@ def w8a8_scaled_mm(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | No
     if b.size(0) > 1 and b.stride(0) != 1:
         raise ValueError("b must be column-major (K x N with stride(0) == 1), e.g. weight.t()")
     ldb = b.stride(1) if N > 1 else max(K, b.stride(1))
+    _want(out, "out", shape=(M, N), dtypes=_OUT_DTYPES)
+    _want(a_scales, "a_scales", numel=(1, M))
+    _want(b_scales, "b_scales", numel=(1, N))
+    _want(workspace, "workspace", contiguous=True)
+    _check_cuda(a, b, a_scales, b_scales, out, workspace)
+    _same_device(a, b, a_scales, b_scales, out, workspace)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     _, _, ldo = _rows(out, "out")
@@ -419,7 +499,6 @@ def w8a8_scaled_mm(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | No
     if workspace is None:
         _call("w8a8_scaled_mm", *args, _stream(a))
     else:
-        _check_cuda(workspace)
         _call("w8a8_scaled_mm_ws", *args, _ptr(workspace),
               workspace.numel() * workspace.element_size(), _stream(a))
     return out
@@ -436,7 +515,6 @@ def w8a8_quant_scaled_mm(x: torch.Tensor, b: torch.Tensor, b_scales: torch.Tenso
     q ([M, K] codes) and a_scales (fp32 [M]) receive the quantised
     activations; they are allocated when not given. Returns out.
     """
-    _check_cuda(x, b, b_scales, out, q, a_scales)
     qt = _qtype(qtype)
     if b.dtype != CODE_DTYPE[qt]:
         raise ValueError(f"b must hold {CODE_DTYPE[qt]} codes, got {b.dtype}")
@@ -447,6 +525,13 @@ def w8a8_quant_scaled_mm(x: torch.Tensor, b: torch.Tensor, b_scales: torch.Tenso
     if b.size(0) > 1 and b.stride(0) != 1:
         raise ValueError("b must be column-major (K x N with stride(0) == 1), e.g. weight.t()")
     ldb = b.stride(1) if N > 1 else max(K, b.stride(1))
+    _want(x, "x", dtypes=_X_DTYPES)
+    _want(out, "out", shape=(M, N), dtypes=_OUT_DTYPES)
+    _want(q, "q", shape=(M, K), dtypes=(CODE_DTYPE[qt],))
+    _want(a_scales, "a_scales", numel=M, dtypes=_F32, contiguous=True)
+    _want(b_scales, "b_scales", numel=(1, N))
+    _check_cuda(x, b, b_scales, out, q, a_scales)
+    _same_device(x, b, b_scales, out, q, a_scales)
     if q is None:
         q = torch.empty((M, K), dtype=CODE_DTYPE[qt], device=x.device)
     if a_scales is None:
@@ -484,6 +569,30 @@ def w8a8_scaled_mm_kernel(M: int, N: int, K: int, workspace: bool = False) -> st
     return f(M, N, K).decode()
 
 
+# Short names of the Python layer: the calls of the C ABI without the
+# library prefix, in the call shapes of "[Kernel] Add w8a8 CUTLASS kernels"
+# (scaled_mm above) and of the quantizers that feed it.
+def quant_per_token(x: torch.Tensor, qtype="fp8"):
+    """Dynamic per-token quantisation: (codes [M, K], scales fp32 [M])."""
+    return w8a8_quant_per_token(x, qtype)
+
+
+def quant_per_tensor(x: torch.Tensor, qtype="fp8", scale: torch.Tensor | None = None,
+                     dynamic: bool = False):
+    """Static (given scale, None = 1.0) or dynamic per-tensor quantisation: (codes, scale)."""
+    return w8a8_quant_per_tensor(x, qtype, scale, dynamic)
+
+
+def kv_quant(x: torch.Tensor, scale: torch.Tensor | None = None, dynamic: bool = True):
+    """Scaled e4m3fn KV-cache quantisation: (codes, scale), scale = absmax / 448 when dynamic."""
+    return kv_fp8_scaled_quant(x, scale, dynamic)
+
+
+def kv_dequant(q: torch.Tensor, scale: torch.Tensor | None, out_dtype=torch.bfloat16):
+    """x' = fp8_dequant(q) * scale in out_dtype."""
+    return kv_fp8_scaled_dequant(q, scale, out_dtype)
+
+
 def version() -> str:
     return load_library().w8a8_version().decode()
 
@@ -494,4 +603,5 @@ __all__ = ["w8a8_quant_per_token", "w8a8_quant_per_tensor", "w8a8_scaled_mm",
            "w8a8_expand_shard_scales", "w8a8_requant_shared_scale",
            "w8a8_quant_per_token_azp", "w8a8_colsum", "w8a8_scaled_mm_azp",
            "kv_fp8_decode_attention", "kv_fp8_attention_workspace_size",
+           "quant_per_token", "quant_per_tensor", "kv_quant", "kv_dequant",
            "load_library", "version", "LIB_PATH", "SIGNATURES"]
