@@ -78,21 +78,54 @@ def log(*a):
 # names the kernel family, and units are its algorithmic flops and bytes.
 # --------------------------------------------------------------------------
 class Launch:
-    """One library call of a step. `kernel` names the kernel configuration it
-    runs (several calls of one step can share it); `flops` and `nbytes` are
-    its algorithmic work: 2*M*N*K, and every operand, scale and output byte
-    read or written once."""
+    """One library call of a step: call(*args). `kernel` names the kernel
+    configuration it runs (several calls of one step can share it); `flops`
+    and `nbytes` are its algorithmic work: 2*M*N*K, and every operand, scale
+    and output byte read or written once."""
 
-    def __init__(self, kind, fn, flops, nbytes, label, kernel):
-        self.kind, self.fn, self.flops, self.nbytes = kind, fn, flops, nbytes
-        self.label, self.kernel = label, kernel
+    def __init__(self, kind, call, args, flops, nbytes, label, kernel):
+        self.kind, self.call, self.args = kind, call, tuple(args)
+        self.flops, self.nbytes, self.label, self.kernel = flops, nbytes, label, kernel
+
+    def fn(self):
+        return self.call(*self.args)
+
+    def copy(self):
+        """The same call on its own copies of every device buffer (for timing
+        a kernel over more distinct bytes than the last-level cache holds)."""
+        args = [a.clone() if isinstance(a, torch.Tensor) else a for a in self.args]
+        return Launch(self.kind, self.call, args, self.flops, self.nbytes, self.label, self.kernel)
 
 
 def _gemm_bytes(M, N, K, n_sa, n_sb, out_bytes=2):
     return M * K + N * K + 4 * n_sa + 4 * n_sb + out_bytes * M * N
 
 
-def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
+def _quant_call(qtype, x, q, s):
+    return w8.w8a8_quant_per_token(x, qtype, q=q, scales=s)
+
+
+def _azp_quant_call(x, q, s, z):
+    return w8.w8a8_quant_per_token_azp(x, q=q, scales=s, azp=z)
+
+
+def _static_quant_call(qtype, x, q, s):
+    return w8.w8a8_quant_per_tensor(x, qtype, scale=s, q=q)
+
+
+def _mm_call(otype, q, wq, s, wsc, out, ws):
+    return w8.w8a8_scaled_mm(q, wq.t(), s, wsc, otype, out=out, workspace=ws)
+
+
+def _mm_azp_call(otype, q, wq, s, z, cs, wsc, out):
+    return w8.w8a8_scaled_mm_azp(q, wq.t(), s, z, cs, wsc, otype, out=out)
+
+
+def _fused_call(qtype, otype, x, wq, wsc, out, q, s):
+    return w8.w8a8_quant_scaled_mm(x, wq.t(), wsc, qtype, otype, out=out, q=q, a_scales=s)
+
+
+def build_gemm_workload(layers, Ms, qtype, act_scheme, dev, otype=torch.bfloat16):
     launches, keep = [], []
     code_dtype = torch.float8_e4m3fn if qtype == "fp8" else torch.int8
     # one workspace for the step's split-K problems (they run one after another)
@@ -108,18 +141,18 @@ def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
             del w
             x = workloads.activations(M, K, seed=seed + 500, device=dev)
             q = torch.empty((M, K), dtype=code_dtype, device=dev)
-            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            out = torch.empty((M, N), dtype=otype, device=dev)
             cs = z = None
             if act_scheme == "azp":  # asymmetric per-token int8, weight code sums offline
                 s = torch.empty(M, dtype=torch.float32, device=dev)
                 z = torch.empty(M, dtype=torch.int32, device=dev)
                 cs = w8.w8a8_colsum(wq)
-                qf = (lambda x=x, q=q, s=s, z=z: w8.w8a8_quant_per_token_azp(x, q=q, scales=s, azp=z))
+                qcall, qargs = _azp_quant_call, (x, q, s, z)
                 n_sa = M
                 qbytes = 3 * M * K + 8 * M
             elif act_scheme == "per_token":
                 s = torch.empty(M, dtype=torch.float32, device=dev)
-                qf = (lambda x=x, q=q, s=s: w8.w8a8_quant_per_token(x, qtype, q=q, scales=s))
+                qcall, qargs = _quant_call, (qtype, x, q, s)
                 n_sa = M
                 qbytes = 3 * M * K + 4 * M
             else:  # static per-tensor scale from a seeded calibration batch
@@ -127,29 +160,27 @@ def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
                                               seed=workloads.CALIBRATION_SEED, device=dev)
                 _, s = w8.w8a8_quant_per_tensor(calib, qtype, dynamic=True)
                 del calib
-                qf = (lambda x=x, q=q, s=s: w8.w8a8_quant_per_tensor(x, qtype, scale=s, q=q))
+                qcall, qargs = _static_quant_call, (qtype, x, q, s)
                 n_sa = 1
                 qbytes = 3 * M * K + 4
-            mf = (lambda q=q, wq=wq, s=s, wsc=wsc, out=out:
-                  w8.w8a8_scaled_mm(q, wq.t(), s, wsc, torch.bfloat16, out=out, workspace=ws))
+            mcall, margs = _mm_call, (otype, q, wq, s, wsc, out, ws)
             if act_scheme == "azp":
-                mf = (lambda q=q, wq=wq, s=s, z=z, cs=cs, wsc=wsc, out=out:
-                      w8.w8a8_scaled_mm_azp(q, wq.t(), s, z, cs, wsc, torch.bfloat16, out=out))
+                mcall, margs = _mm_azp_call, (otype, q, wq, s, z, cs, wsc, out)
             fused = (act_scheme == "per_token"
                      and w8.w8a8_quant_scaled_mm_kernel(M, N, K) == "gemm_dynq_kernel")
+            obytes = torch.tensor([], dtype=otype).element_size()
             if fused:  # one kernel quantises the token and runs the product
-                ff = (lambda x=x, wq=wq, wsc=wsc, out=out, q=q, s=s:
-                      w8.w8a8_quant_scaled_mm(x, wq.t(), wsc, qtype, torch.bfloat16, out=out,
-                                              q=q, a_scales=s))
-                launches.append(Launch("gemm", ff, 2 * M * N * K,
-                                       _gemm_bytes(M, N, K, n_sa, N) + qbytes - M * K,
+                launches.append(Launch("gemm", _fused_call, (qtype, otype, x, wq, wsc, out, q, s),
+                                       2 * M * N * K,
+                                       _gemm_bytes(M, N, K, n_sa, N, obytes) + qbytes - M * K,
                                        f"quant+gemm M={M} {name} {N}x{K}", "gemm_dynq_kernel"))
             else:
                 qkern = {"per_token": "quant_rows_kernel", "azp": "quant_rows_azp_kernel"}.get(
                     act_scheme, "quant_tensor_kernel")
-                launches.append(Launch("quant", qf, 0, qbytes, f"quant M={M} {name}", qkern))
+                launches.append(Launch("quant", qcall, qargs, 0, qbytes, f"quant M={M} {name}", qkern))
                 extra = 4 * M + 4 * N if act_scheme == "azp" else 0  # zero points, code sums
-                launches.append(Launch("gemm", mf, 2 * M * N * K, _gemm_bytes(M, N, K, n_sa, N) + extra,
+                launches.append(Launch("gemm", mcall, margs, 2 * M * N * K,
+                                       _gemm_bytes(M, N, K, n_sa, N, obytes) + extra,
                                        f"gemm M={M} {name} {N}x{K}",
                                        w8.w8a8_scaled_mm_kernel(M, N, K, workspace=act_scheme != "azp")))
             keep += [wq, wsc, x, q, s, out] + ([z, cs] if act_scheme == "azp" else [])
@@ -160,6 +191,14 @@ def build_gemm_workload(layers, Ms, qtype, act_scheme, dev):
 # absmax pass (partial maxima), the quantisation, and the scale plus the last
 # few KB of codes.
 KV_QUANT_KERNELS = "absmax_kernel+quant_tensor_kernel+finish_tail_kernel"
+
+
+def _kv_quant_call(x, q, s):
+    return w8.kv_fp8_scaled_quant(x, scale=s, q=q)
+
+
+def _kv_dequant_call(q, s, y):
+    return w8.kv_fp8_scaled_dequant(q, s, out=y)
 
 
 def build_kv_workload(dev, layers=workloads.KV_LAYERS):
@@ -173,12 +212,10 @@ def build_kv_workload(dev, layers=workloads.KV_LAYERS):
             q = torch.empty(workloads.KV_SHAPE, dtype=torch.float8_e4m3fn, device=dev)
             s = torch.empty(1, dtype=torch.float32, device=dev)
             y = torch.empty(workloads.KV_SHAPE, dtype=torch.bfloat16, device=dev)
-            launches.append(Launch("kv_quant",
-                                   lambda x=x, q=q, s=s: w8.kv_fp8_scaled_quant(x, scale=s, q=q),
+            launches.append(Launch("kv_quant", _kv_quant_call, (x, q, s),
                                    0, 2 * n + n + 2 * n, f"kv quant L{layer}{which}",
                                    KV_QUANT_KERNELS))
-            launches.append(Launch("kv_dequant",
-                                   lambda q=q, s=s, y=y: w8.kv_fp8_scaled_dequant(q, s, out=y),
+            launches.append(Launch("kv_dequant", _kv_dequant_call, (q, s, y),
                                    0, n + 2 * n, f"kv dequant L{layer}{which}",
                                    "kv_dequant_kernel"))
             keep += [x, q, s, y]
@@ -186,7 +223,7 @@ def build_kv_workload(dev, layers=workloads.KV_LAYERS):
     x = workloads.activations(M, K, seed=0, device=dev)
     q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
     s = torch.empty(M, dtype=torch.float32, device=dev)
-    launches.append(Launch("quant", lambda: w8.w8a8_quant_per_token(x, "fp8", q=q, scales=s),
+    launches.append(Launch("quant", _quant_call, ("fp8", x, q, s),
                            0, 3 * M * K + 4 * M, "per-token quant 8192x4096",
                            "quant_rows_kernel"))
     keep += [x, q, s]
@@ -196,6 +233,14 @@ def build_kv_workload(dev, layers=workloads.KV_LAYERS):
 def shard_scales(S: int, seed: int) -> torch.Tensor:
     g = torch.Generator().manual_seed(seed)
     return torch.rand(S, generator=g) * 3.8e-3 + 2e-4
+
+
+def _expand_call(s, rows, sb):
+    return w8.w8a8_expand_shard_scales(s, rows, out=sb)
+
+
+def _requant_call(w, rows, s, out, sh):
+    return w8.w8a8_requant_shared_scale(w, rows, s, out=out, shared_scale=sh)
 
 
 def build_merge_workload(dev):
@@ -210,18 +255,19 @@ def build_merge_workload(dev):
         sb = torch.empty(N, dtype=torch.float32, device=dev)
         out = torch.empty_like(w)
         sh = torch.empty(1, dtype=torch.float32, device=dev)
-        launches.append(Launch("merge_expand",
-                               lambda s=s, rows=rows, sb=sb: w8.w8a8_expand_shard_scales(s, rows, out=sb),
+        launches.append(Launch("merge_expand", _expand_call, (s, rows, sb),
                                0, 4 * S + 4 * N, f"expand {name}", "expand_shard_scales_kernel"))
-        launches.append(Launch("merge_requant",
-                               lambda w=w, rows=rows, s=s, out=out, sh=sh:
-                               w8.w8a8_requant_shared_scale(w, rows, s, out=out, shared_scale=sh),
+        launches.append(Launch("merge_requant", _requant_call, (w, rows, s, out, sh),
                                0, 2 * N * K + 4 * S + 4, f"requant {name}", "requant_shared_kernel"))
         keep += [w, s, sb, out, sh]
     return launches, keep
 
 
 ATTN_KERNELS = "attn_split_kernel+attn_combine_kernel"
+
+
+def _attn_call(q, kc, vc, starts, max_len, ks, vs, out, ws):
+    return w8.kv_fp8_decode_attention(q, kc, vc, starts, max_len, ks, vs, out=out, workspace=ws)
 
 
 def build_attn_workload(dev, layers=workloads.KV_LAYERS):
@@ -250,9 +296,7 @@ def build_attn_workload(dev, layers=workloads.KV_LAYERS):
         q = workloads.attention_queries(B, hq, d, seed=200 + layer, device=dev)
         out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
         nbytes = 2 * rows * hkv * d + 2 * 2 * B * hq * d + 4 * (B + 1) + 8
-        launches.append(Launch("attn", lambda q=q, kc=kc, vc=vc, ks=ks, vs=vs, out=out:
-                               w8.kv_fp8_decode_attention(q, kc, vc, starts_d, max_len, ks, vs,
-                                                          out=out, workspace=ws),
+        launches.append(Launch("attn", _attn_call, (q, kc, vc, starts_d, max_len, ks, vs, out, ws),
                                4 * rows * hq * d, nbytes, f"attention L{layer}", ATTN_KERNELS))
         keep += [kc, ks, vc, vs, q, out]
     return launches, keep
@@ -455,8 +499,10 @@ def roofline(name, k, spec, workload):
                 avg_launch_us=round(k["avg_s"] * 1e6, 3),
                 algorithmic_bytes_per_launch=round(k["nbytes"]),
                 algorithmic_flops_per_launch=round(k["flops"]),
-                timing="the step's launches of this kernel captured alone, replayed, "
-                       "HIP events on the launch stream")
+                rotated_bytes=round(k["rotated_bytes"]), copies=k["copies"],
+                timing="the step's launches of this kernel captured alone (with copies on their "
+                       "own buffers up to >= 512 MiB of distinct bytes), replayed, HIP events on "
+                       "the launch stream")
     return roof
 
 
@@ -565,12 +611,140 @@ def cpu_baseline(spec, launches_meta, budget_s: float):
                       f"{dt:.1f} s)"}
 
 
+ROTATE_BYTES = 512 << 20   # twice the 256 MB last-level cache
+MAX_COPIES = 16
+
+
+def build(name, spec, dev, otype):
+    if name == "kv":
+        return build_kv_workload(dev)
+    if name == "attn":
+        return build_attn_workload(dev)
+    if name == "merge":
+        return build_merge_workload(dev)
+    return build_gemm_workload(spec["layers"], spec["Ms"], spec["qtype"], spec["act"], dev, otype)
+
+
+def time_kernels(launches, stream, reps):
+    """Per kernel configuration: the step's launches of that kernel captured
+    alone and replayed `reps` times, timed with HIP events on the launch
+    stream. Where those launches touch fewer than ROTATE_BYTES of distinct
+    algorithmic bytes, copies of them on their own buffers are added (up to
+    MAX_COPIES in all), so that the replay streams from HBM rather than from
+    the last-level cache; per-token quantisations of decode batches (a few KB,
+    latency-bound) are timed as they are."""
+    kernels = {}
+    for name in dict.fromkeys(L.kernel for L in launches):
+        group = [L for L in launches if L.kernel == name]
+        per_copy = sum(L.nbytes for L in group)
+        copies = 1
+        if group[0].kind != "quant" and per_copy > 0:
+            copies = min(MAX_COPIES, max(1, -(-ROTATE_BYTES // per_copy)))
+        timed = list(group)
+        for _ in range(copies - 1):
+            timed += [L.copy() for L in group]
+        g = capture(timed, stream)
+        g.replay()
+        ms, _ = time_graph(g, stream, reps)
+        kernels[name] = dict(launches=len(group), avg_s=ms / 1e3 / len(timed),
+                             nbytes=per_copy / len(group),
+                             flops=sum(L.flops for L in group) / len(group),
+                             rotated_bytes=per_copy * copies, copies=copies, graph=g,
+                             replay_s=ms / 1e3, buffers=timed)  # alive while the graph is
+    return kernels
+
+
+def measure(name, args, dev, stream, otype, detail=False):
+    """Build one workload, time its step, every kernel configuration, and the
+    clock under the dominant kernel; returns the figures and the launches."""
+    spec = WORKLOADS[name]
+    log(f"[bench] workload {name}: building inputs")
+    launches, keep = build(name, spec, dev, otype)
+    torch.cuda.synchronize()
+    # eager warm-up of every launch (also validates arguments before capture)
+    with torch.cuda.stream(stream):
+        for L in launches:
+            L.fn()
+    torch.cuda.synchronize()
+    graph = capture(launches, stream)
+    with torch.cuda.stream(stream):
+        log(f"[bench] {name}: warmup {args.warmup} steps")
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        log(f"[bench] {name}: timing {args.steps} steps")
+        step_ms, wall = time_graph(graph, stream, args.steps)
+        log(f"[bench] {name}: timing each kernel's launches")
+        kernels = time_kernels(launches, stream, args.steps)
+        # The roofline entry is for the scaled-product (or KV) kernel that takes
+        # the most time per step; the small per-token quantizations of decode
+        # batches are latency-bound (a few KB each) and are listed with their
+        # latency only.
+        kinds = {L.kernel: L.kind for L in launches}
+        main_kind = {"kv": "kv_quant", "merge": "merge_requant", "attn": "attn"}.get(name, "gemm")
+        dom = max((k for k in kernels if kinds[k] == main_kind),
+                  key=lambda k: kernels[k]["avg_s"] * kernels[k]["launches"])
+        roof = roofline(dom, kernels[dom], spec, name)
+        # The clock the roofline kernel runs at: the matrix-core peak scales
+        # with it (HBM bandwidth does not), so an MFMA-bound entry is also
+        # given against the peak at the measured clock.
+        clock = None
+        if args.clock_seconds > 0:
+            clock = clock_under_load(kernels[dom]["graph"], stream, kernels[dom]["replay_s"],
+                                     seconds=args.clock_seconds)
+        if clock is not None and roof["bound"] == "mfma":
+            peak_clk = roof["peak"] * clock["gfx_mhz_mean"] / SPEC_GFX_MHZ
+            roof.update(peak_at_clock=round(peak_clk, 1),
+                        frac_at_clock=round(roof["achieved"] / peak_clk, 4))
+        if detail:
+            # per-launch times: each launch alone, graph of 10 back-to-back copies
+            for L in launches:
+                g3 = capture([L] * 10, stream)
+                g3.replay()
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(5):
+                    g3.replay()
+                b.record(stream)
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) * 1e3 / 50
+                log(f"[bench]   {L.label:40s} {us:9.2f} us  {L.nbytes / us / 1e3:8.1f} GB/s  "
+                    f"{L.flops / us / 1e6:9.1f} TFLOP/s")
+    per_step_flops = sum(L.flops for L in launches)
+    per_step_bytes = sum(L.nbytes for L in launches)
+    for k in kernels.values():
+        del k["graph"], k["buffers"]
+    del graph, keep
+    return dict(spec=spec, step_ms=step_ms, wall=wall, kernels=kernels, roof=roof, clock=clock,
+                flops=per_step_flops, nbytes=per_step_bytes, n_launches=len(launches),
+                launches=launches)
+
+
+def kernel_table(kernels, spec):
+    return {n: {"launches_per_step": k["launches"],
+                "avg_launch_us": round(k["avg_s"] * 1e6, 3),
+                "hbm_frac": round(k["nbytes"] / k["avg_s"] / 1e9 / HBM_PEAK_GBS, 4),
+                "mfma_frac": round(k["flops"] / k["avg_s"] / 1e12
+                                   / MFMA_PEAK_TFLOPS.get(spec.get("qtype"), 5000.0), 4),
+                "rotated_bytes": round(k["rotated_bytes"])}
+            for n, k in kernels.items()}
+
+
+OUT_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
+    ap.add_argument("--out-dtype", choices=sorted(OUT_DTYPES), default="bf16",
+                    help="output type of the GEMM workloads (the prefill configuration has both)")
+    ap.add_argument("--mfma-workload", choices=["prefill", "int8", "none"], default="prefill",
+                    help="with --workload decode: the MFMA-bound workload whose roofline entry "
+                         "is added to the line as roofline_mfma (none: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0: skip)")
     ap.add_argument("--detail", action="store_true", help="per-launch times on stderr")
@@ -601,109 +775,32 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
         return
 
-    spec = WORKLOADS[args.workload]
     w8.load_library()
-    log(f"[bench] workload {args.workload}: building inputs")
-    if args.workload == "kv":
-        launches, keep = build_kv_workload(dev)
-    elif args.workload == "attn":
-        launches, keep = build_attn_workload(dev)
-    elif args.workload == "merge":
-        launches, keep = build_merge_workload(dev)
-    else:
-        launches, keep = build_gemm_workload(spec["layers"], spec["Ms"], spec["qtype"],
-                                             spec["act"], dev)
-    torch.cuda.synchronize()
     stream = torch.cuda.Stream()
-
-    # eager warm-up of every launch (also validates arguments before capture)
-    with torch.cuda.stream(stream):
-        for L in launches:
-            L.fn()
-    torch.cuda.synchronize()
-
-    graph = capture(launches, stream)
-
-    # Every replay and every timing event below goes to `stream` (a graph
-    # replays on the current stream).
-    stream_ctx = torch.cuda.stream(stream)
-    stream_ctx.__enter__()
-    log(f"[bench] warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-
-    log(f"[bench] timing {args.steps} steps")
-    step_ms, wall = time_graph(graph, stream, args.steps)
-
-    per_step_flops = sum(L.flops for L in launches)
-    per_step_bytes = sum(L.nbytes for L in launches)
+    otype = OUT_DTYPES[args.out_dtype]
+    r = measure(args.workload, args, dev, stream, otype, detail=args.detail)
+    spec = r["spec"]
+    step_ms = r["step_ms"]
     if args.workload == "kv":
-        value = per_step_bytes / (step_ms / 1e3) / 1e9
+        value = r["nbytes"] / (step_ms / 1e3) / 1e9
         metric, unit = "scaled fp8 KV cache quant+dequant GB/s (algorithmic bytes)", "GB/s"
         dtype = "fp8e4m3"
     elif args.workload == "attn":
-        value = per_step_bytes / (step_ms / 1e3) / 1e9
+        value = r["nbytes"] / (step_ms / 1e3) / 1e9
         metric, unit = "fp8 KV cache decode attention GB/s (algorithmic bytes)", "GB/s"
         dtype = "fp8e4m3 cache, f32 arithmetic"
     elif args.workload == "merge":
-        value = per_step_bytes / (step_ms / 1e3) / 1e9
+        value = r["nbytes"] / (step_ms / 1e3) / 1e9
         metric, unit = "merged-layer scale expansion + shared-scale requant GB/s (algorithmic bytes)", "GB/s"
         dtype = "u8 codes (fp8e4m3, int8), f32 arithmetic"
     else:
-        value = per_step_flops / (step_ms / 1e3) / 1e12
+        value = r["flops"] / (step_ms / 1e3) / 1e12
         metric, unit = METRIC, "TFLOP/s"
         dtype = "fp8e4m3" if spec["qtype"] == "fp8" else "int8"
 
-    # Per kernel: the step's launches of that kernel, captured alone and
-    # replayed `steps` times, timed with events on the launch stream.
-    log("[bench] timing each kernel's launches")
-    kernels = {}
-    for name in dict.fromkeys(L.kernel for L in launches):
-        group = [L for L in launches if L.kernel == name]
-        g = capture(group, stream)
-        g.replay()
-        ms, _ = time_graph(g, stream, args.steps)
-        avg_s = ms / 1e3 / len(group)
-        kernels[name] = dict(launches=len(group), avg_s=avg_s,
-                             nbytes=sum(L.nbytes for L in group) / len(group),
-                             flops=sum(L.flops for L in group) / len(group))
-    # The roofline entry is for the scaled-product (or KV) kernel that takes the
-    # most time per step; the small per-token quantizations of decode batches
-    # are latency-bound (a few KB each) and are listed with their latency only.
-    kinds = {L.kernel: L.kind for L in launches}
-    main_kind = {"kv": "kv_quant", "merge": "merge_requant", "attn": "attn"}.get(args.workload, "gemm")
-    dom = max((k for k in kernels if kinds[k] == main_kind),
-              key=lambda k: kernels[k]["avg_s"] * kernels[k]["launches"])
-    roof = roofline(dom, kernels[dom], spec, args.workload)
-    # The clock the roofline kernel runs at: the matrix-core peak scales with
-    # it (HBM bandwidth does not), so an MFMA-bound entry is also given
-    # against the peak at the measured clock.
-    g_dom = capture([L for L in launches if L.kernel == dom], stream) if args.clock_seconds > 0 else None
-    if g_dom is not None:
-        g_dom.replay()
-    clock = None if args.clock_seconds <= 0 else clock_under_load(
-        g_dom, stream, kernels[dom]["avg_s"] * kernels[dom]["launches"], seconds=args.clock_seconds)
-    if clock is not None and roof["bound"] == "mfma":
-        peak_clk = roof["peak"] * clock["gfx_mhz_mean"] / SPEC_GFX_MHZ
-        roof.update(peak_at_clock=round(peak_clk, 1), frac_at_clock=round(roof["achieved"] / peak_clk, 4))
-
-    if args.detail:
-        # per-launch times: each launch alone, graph of 10 back-to-back copies
-        for L in launches:
-            g3 = capture([L] * 10, stream)
-            g3.replay()
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(5):
-                g3.replay()
-            b.record(stream)
-            torch.cuda.synchronize()
-            us = a.elapsed_time(b) * 1e3 / 50
-            log(f"[bench]   {L.label:40s} {us:9.2f} us  {L.nbytes / us / 1e3:8.1f} GB/s  "
-                f"{L.flops / us / 1e6:9.1f} TFLOP/s")
-
+    desc = spec["desc"]
+    if spec.get("layers") is not None and args.out_dtype != "bf16":
+        desc = desc.replace("bf16 out", f"{args.out_dtype} out")
     result = {
         "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
@@ -714,25 +811,34 @@ def main():
                 "synthetic (seeded; N(0,1) K/V with 0.1% outliers x10 quantised to e4m3fn, "
                 "N(0,1) bf16 queries, sequence lengths from seeded weights)" if args.workload == "attn" else
                 "synthetic (seeded; uniformly random valid codes, shard scales U(2e-4, 4e-3))",
-        "config": {"workload": spec["desc"], "mode": "hip-graph replay, inputs resident in HBM",
-                   "step_bytes": per_step_bytes, "step_flops": per_step_flops,
-                   "launches_per_step": len(launches), "parallelism": "single GPU"},
-        "roofline": roof,
-        "clock": clock,
-        "kernels": {n: {"launches_per_step": k["launches"],
-                        "avg_launch_us": round(k["avg_s"] * 1e6, 3),
-                        "hbm_frac": round(k["nbytes"] / k["avg_s"] / 1e9 / HBM_PEAK_GBS, 4),
-                        "mfma_frac": round(k["flops"] / k["avg_s"] / 1e12
-                                           / MFMA_PEAK_TFLOPS.get(spec.get("qtype"), 5000.0), 4)}
-                    for n, k in kernels.items()},
+        "config": {"workload": desc, "mode": "hip-graph replay, inputs resident in HBM",
+                   "step_bytes": r["nbytes"], "step_flops": r["flops"],
+                   "launches_per_step": r["n_launches"], "parallelism": "single GPU"},
+        "roofline": r["roof"],
+        "clock": r["clock"],
+        "kernels": kernel_table(r["kernels"], spec),
     }
+    launches = r.pop("launches")
+    if args.workload == "decode" and args.mfma_workload != "none":
+        # The metric's other half: the MFMA-bound roofline of the prefill (or
+        # int8) GEMMs, measured in the same run the same way.
+        del launches
+        torch.cuda.empty_cache()
+        m = measure(args.mfma_workload, args, dev, stream, torch.bfloat16)
+        m.pop("launches")
+        mroof = dict(m["roof"])
+        mroof.update(workload=m["spec"]["desc"], clock=m["clock"],
+                     step_value=round(m["flops"] / (m["step_ms"] / 1e3) / 1e12, 3),
+                     step_unit="TFLOP/s", step_ms=round(m["step_ms"], 4))
+        result["roofline_mfma"] = mroof
+        result["kernels_mfma"] = kernel_table(m["kernels"], m["spec"])
+        torch.cuda.empty_cache()
     if args.cpu_budget > 0:
         log("[bench] cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(spec, launches, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(spec, None, args.cpu_budget)
     else:
         result["cpu_baseline"] = None
-    stream_ctx.__exit__(None, None, None)
-    log(f"[bench] wall {wall:.3f}s for the timed loop")
+    log(f"[bench] wall {r['wall']:.3f}s for the timed loop")
     print(json.dumps(result), flush=True)
 
 

@@ -21,7 +21,7 @@ import torch
 import int8_scaled_gemm_amd as w8
 import oracle
 import workloads
-from tests.gpu_util import DEV, bits, check_scaled_mm_rows, f32_bits
+from tests.gpu_util import DEV, TORCH_OF, bits, check_scaled_mm_rows, f32_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +49,7 @@ def _weights_checked(N, K, qtype, seed):
     return w, wq, ws, wq_h, ws.cpu().numpy()
 
 
-def _check_layer(M, N, K, qtype, act, seed):
+def _check_layer(M, N, K, qtype, act, seed, otype="bf16"):
     w, wq, ws, wq_h, ws_h = _weights_checked(N, K, qtype, seed)
     del w
     x = workloads.activations(M, K, seed=seed + 500, device=DEV)
@@ -60,7 +60,7 @@ def _check_layer(M, N, K, qtype, act, seed):
     if act == "per_token" and w8.w8a8_quant_scaled_mm_kernel(M, N, K) == "gemm_dynq_kernel":
         xq = torch.empty((M, K), dtype=wq.dtype, device=DEV)
         xs = torch.empty(M, dtype=torch.float32, device=DEV)
-        out = w8.w8a8_quant_scaled_mm(x, wq.t(), ws, qtype, torch.bfloat16, q=xq, a_scales=xs)
+        out = w8.w8a8_quant_scaled_mm(x, wq.t(), ws, qtype, TORCH_OF[otype], q=xq, a_scales=xs)
     else:
         if act == "per_token":
             xq, xs = w8.w8a8_quant_per_token(x, qtype)
@@ -69,7 +69,7 @@ def _check_layer(M, N, K, qtype, act, seed):
                                           seed=workloads.CALIBRATION_SEED, device=DEV)
             _, xs = w8.w8a8_quant_per_tensor(calib, qtype, dynamic=True)
             xq, _ = w8.w8a8_quant_per_tensor(x, qtype, scale=xs)
-        out = w8.w8a8_scaled_mm(xq, wq.t(), xs, ws, torch.bfloat16, workspace=workspace)
+        out = w8.w8a8_scaled_mm(xq, wq.t(), xs, ws, TORCH_OF[otype], workspace=workspace)
     torch.cuda.synchronize()
     rows = _sample_rows(M, seed + 1, 16 if M > 64 else M)
     # activation codes on the sampled rows against the oracle
@@ -83,7 +83,7 @@ def _check_layer(M, N, K, qtype, act, seed):
     assert np.array_equal(xq_h[rows], q_ref)
     sa = xs.cpu().numpy()
     info = check_scaled_mm_rows(out, rows, xq_h, wq_h, qtype, sa if sa.size > 1 else sa[:1], ws_h,
-                                "bf16")
+                                otype)
     assert info["exact_frac"] > 0.9, info
     return info
 
@@ -95,11 +95,13 @@ def test_fp8_decode_full(M, name, N, K):
     _check_layer(M, N, K, "fp8", "per_token", seed=10 * M + N % 97)
 
 
+@pytest.mark.parametrize("otype", ["bf16", "fp16"])
 @pytest.mark.parametrize("name,N,K", workloads.LLAMA3_8B_LAYERS)
 @pytest.mark.parametrize("M", workloads.FP8_PREFILL_M)
-def test_fp8_prefill_full(M, name, N, K):
-    print(f"fp8 prefill M={M} {name} {N}x{K}", flush=True)
-    _check_layer(M, N, K, "fp8", "per_tensor_static", seed=11 * M + N % 89)
+def test_fp8_prefill_full(M, name, N, K, otype):
+    """The prefill configuration with both of its output types, bf16 and fp16."""
+    print(f"fp8 prefill M={M} {name} {N}x{K} {otype}", flush=True)
+    _check_layer(M, N, K, "fp8", "per_tensor_static", seed=11 * M + N % 89, otype=otype)
 
 
 @pytest.mark.parametrize("name,N,K", workloads.LLAMA3_70B_LAYERS)

@@ -62,15 +62,19 @@ TILE_SHAPES = [(4096 + 37, 4096 + 48, 384 + 16), (2048, 4096 + 16, 272), (1024 +
                (200, 300, 1040)]
 
 
+@pytest.mark.parametrize("otype", ["bf16", "fp16"])
 @pytest.mark.parametrize("qtype", ["fp8", "int8"])
 @pytest.mark.parametrize("M,N,K", TILE_SHAPES)
-def test_tile_configs_sampled_rows(qtype, M, N, K):
+def test_tile_configs_sampled_rows(qtype, M, N, K, otype):
+    """Both 2-byte outputs of the prefill configuration (bf16 and fp16, "[Kernel]
+    Add w8a8 CUTLASS kernels", PR description) on every block tile, whose
+    epilogue rounds into LDS and stores whole rows."""
     a, sa, b, sb = _quantized(M, N, K, qtype, seed=M + 2 * N + K)
-    got = _run(a, b, qtype, sa, sb, "bf16")
+    got = _run(a, b, qtype, sa, sb, otype)
     rng = np.random.default_rng(M)
     rows = [0, 1, 15, 16, 255, 256, M - 1, M - 2] + list(rng.integers(0, M, 40))
     rows = [r for r in rows if r < M]
-    info = check_scaled_mm_rows(got, rows, a, b, qtype, sa, sb, "bf16")
+    info = check_scaled_mm_rows(got, rows, a, b, qtype, sa, sb, otype)
     assert info["exact_frac"] > 0.9, info
 
 

@@ -41,8 +41,8 @@ def _weights(N, K, qtype, seed):
     return oracle.quant_per_token(w.view(torch.int16).numpy().view(np.uint16), qtype, xtype="bf16")
 
 
-def _check(M, N, K, qtype, xtype="bf16", otype="bf16", gran="channel", seed=0):
-    x = _x(M, K, seed + 11, xtype)
+def _check(M, N, K, qtype, xtype="bf16", otype="bf16", gran="channel", seed=0, x_mul=1.0):
+    x = _x(M, K, seed + 11, xtype) * x_mul  # a power of two: exact in every input type
     b, sb = _weights(N, K, qtype, seed + 12)
     if gran == "tensor":
         sb = sb[:1]
@@ -79,9 +79,11 @@ def test_quant_scaled_mm_parity(qtype, M, N, K):
 @pytest.mark.parametrize("gran", ["channel", "tensor", "none"])
 def test_quant_scaled_mm_types_and_granularities(xtype, otype, gran):
     qtype = "fp8"
-    if otype == "fp16" and gran == "none":
-        pytest.skip("unscaled fp8 products of N(0,1) activations exceed the fp16 range")
-    _check(1, 272, 2048, qtype, xtype=xtype, otype=otype, gran=gran, seed=5)
+    # Without weight scales the output is sum_k x_k * b_k with weight codes up
+    # to 448: N(0,1) activations with outliers reach past the fp16 range, so
+    # that case takes activations 2^-8 as large (same codes, scale / 256).
+    x_mul = 2.0 ** -8 if (otype == "fp16" and gran == "none") else 1.0
+    _check(1, 272, 2048, qtype, xtype=xtype, otype=otype, gran=gran, seed=5, x_mul=x_mul)
 
 
 def test_quant_scaled_mm_zero_row_and_saturation():
