@@ -49,6 +49,18 @@ def test_model_reproduces_measured_cases():
     assert _dot_model(vec({0: one, 1: p7}), vec({0: one, 1: p7})) == 1.0
     assert _dot_model(vec({0: one, 8: p7}), vec({0: one, 8: p7})) == 1 + 2.0 ** -14
     assert _dot_model(vec({5: p7}), vec({5: p7})) == 2.0 ** -14
+    s6, p625 = 0.75 * p6, 1.25 * p6
+    assert _dot_model(vec({0: one, 1: s6}), vec({0: one, 1: p7})) == 1.0
+    assert _dot_model(vec({0: one, 1: p625}), vec({0: one, 1: p7})) == 1 + 2.0 ** -13
+    assert _dot_model(vec({0: one, 1: -p7}), vec({0: one, 1: p7})) == 1.0
+    assert _dot_model(vec({0: one, 1: -p7}), vec({0: one, 1: s6})) == 1.0
+    assert _dot_model(vec({0: one, 1: -p7}), vec({0: one, 1: p6})) == 1 - 2.0 ** -13
+    seven = {k: (one if k == 0 else p7) for k in range(8)}
+    assert _dot_model(vec(seven), vec(seven)) == 1.0
+    assert _dot_model(vec({0: -one, 1: p7}), vec({0: one, 1: p7})) == -1.0
+    assert _dot_model(vec({0: 1.5, 1: p7}), vec({0: one, 1: p7})) == 1.5
+    assert _dot_model(vec({4: one, 9: p7}), vec({4: one, 9: p7})) == 1 + 2.0 ** -14
+    assert _dot_model(vec({3: one, 4: p7}), vec({3: one, 4: p7})) == 1.0
 
 
 def test_group_rel_bounds_random_groups():

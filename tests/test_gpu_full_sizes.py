@@ -21,7 +21,7 @@ import torch
 import int8_scaled_gemm_amd as w8
 import oracle
 import workloads
-from tests.gpu_util import DEV, TORCH_OF, bits, check_scaled_mm_rows, f32_bits
+from tests.gpu_util import DEV, TORCH_OF, assert_close_fraction, bits, check_scaled_mm_rows, f32_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -84,7 +84,7 @@ def _check_layer(M, N, K, qtype, act, seed, otype="bf16"):
     sa = xs.cpu().numpy()
     info = check_scaled_mm_rows(out, rows, xq_h, wq_h, qtype, sa if sa.size > 1 else sa[:1], ws_h,
                                 otype)
-    assert info["exact_frac"] > 0.9, info
+    assert_close_fraction(info, qtype, otype)
     return info
 
 

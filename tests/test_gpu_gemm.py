@@ -12,8 +12,8 @@ import torch
 import int8_scaled_gemm_amd as w8
 import oracle
 import workloads
-from tests.gpu_util import (DEV, TORCH_OF, bits, check_scaled_mm, check_scaled_mm_rows,
-                            codes_to_dev)
+from tests.gpu_util import (DEV, TORCH_OF, assert_close_fraction, bits, check_scaled_mm,
+                            check_scaled_mm_rows, codes_to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -75,7 +75,7 @@ def test_tile_configs_sampled_rows(qtype, M, N, K, otype):
     rows = [0, 1, 15, 16, 255, 256, M - 1, M - 2] + list(rng.integers(0, M, 40))
     rows = [r for r in rows if r < M]
     info = check_scaled_mm_rows(got, rows, a, b, qtype, sa, sb, otype)
-    assert info["exact_frac"] > 0.9, info
+    assert_close_fraction(info, qtype, otype)
 
 
 @pytest.mark.parametrize("qtype", ["fp8", "int8"])
