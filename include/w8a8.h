@@ -154,6 +154,27 @@ w8a8_status w8a8_scaled_mm_ws(void* out, w8a8_dtype ot, int64_t ldo, const void*
                               hipStream_t stream);
 
 /*
+ * w8a8_scaled_mm for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc. Same operation, arguments and results as w8a8_scaled_mm_ws
+ * given a large enough workspace, with the split-K partial sums kept in a
+ * static device array of the library (16 MiB, held on each GPU the library
+ * runs on until the process ends) instead of a caller workspace. The call
+ * allocates and frees nothing and does not synchronise. Every split plan
+ * fits the array; a problem that needed more would be refused with
+ * W8A8_ERR_UNSUPPORTED. Calls share the current device's array: calls that
+ * overlap on one GPU (several streams or threads at once) race on it, so the
+ * caller orders them; the array needs no clearing between calls (every
+ * partial sum read was written by the same call). `stream` must belong to
+ * the current device (else W8A8_ERR_INVALID_ARG).
+ */
+w8a8_status w8a8_scaled_mm_noalloc(void* out, w8a8_dtype ot, int64_t ldo, const void* a,
+                                   int64_t lda, const void* b, int64_t ldb, w8a8_qtype qt,
+                                   int64_t M, int64_t N, int64_t K, const float* a_scales,
+                                   int64_t n_a, const float* b_scales, int64_t n_b,
+                                   hipStream_t stream);
+
+/*
  * Dynamic per-token quantisation followed by the scaled matrix multiply, the
  * decode step of a w8a8 linear layer [P1 bullet list: per-token activation
  * scales with per-channel weight scales; P2: dynamic activation scales]:

@@ -57,6 +57,8 @@ SIGNATURES = {
                        _I64, _P],
     "w8a8_scaled_mm_ws": [_P, _I, _I64, _P, _I64, _P, _I64, _I, _I64, _I64, _I64, _P, _I64, _P,
                           _I64, _P, _I64, _P],
+    "w8a8_scaled_mm_noalloc": [_P, _I, _I64, _P, _I64, _P, _I64, _I, _I64, _I64, _I64, _P, _I64,
+                               _P, _I64, _P],
     "w8a8_quant_scaled_mm": [_P, _I, _I64, _P, _I, _I64, _P, _I64, _I, _I64, _I64, _I64, _P, _I64,
                              _P, _I64, _P, _P],
     "kv_fp8_scaled_quant": [_P, _I, _I64, _P, _P, _I, _P],
@@ -467,7 +469,8 @@ def w8a8_scaled_mm(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | No
     int8 accumulator, scales must be None).
     workspace: optional uint8 device tensor; with at least
     w8a8_scaled_mm_workspace_size(M, N, K) bytes the call goes through
-    w8a8_scaled_mm_ws and may split K.
+    w8a8_scaled_mm_ws and may split K. "static": w8a8_scaled_mm_noalloc
+    (split K through the library's static device scratch).
     """
     qt = _qtype(a.dtype)
     if b.dtype != a.dtype:
@@ -482,9 +485,12 @@ def w8a8_scaled_mm(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | No
     _want(out, "out", shape=(M, N), dtypes=_OUT_DTYPES)
     _want(a_scales, "a_scales", numel=(1, M))
     _want(b_scales, "b_scales", numel=(1, N))
-    _want(workspace, "workspace", contiguous=True)
-    _check_cuda(a, b, a_scales, b_scales, out, workspace)
-    _same_device(a, b, a_scales, b_scales, out, workspace)
+    ws_t = workspace if isinstance(workspace, torch.Tensor) else None
+    if workspace is not None and ws_t is None and workspace != "static":
+        raise ValueError("workspace must be a device tensor, None, or 'static'")
+    _want(ws_t, "workspace", contiguous=True)
+    _check_cuda(a, b, a_scales, b_scales, out, ws_t)
+    _same_device(a, b, a_scales, b_scales, out, ws_t)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     _, _, ldo = _rows(out, "out")
@@ -496,12 +502,24 @@ def w8a8_scaled_mm(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | No
     args = (_ptr(out), _dtype(out.dtype), ldo, _ptr(a), lda, _ptr(b), ldb, qt, M, N, K,
             _ptr(sa), 0 if sa is None else sa.numel(), _ptr(sb),
             0 if sb is None else sb.numel())
-    if workspace is None:
+    if workspace == "static":
+        _call("w8a8_scaled_mm_noalloc", *args, _stream(a))
+    elif workspace is None:
         _call("w8a8_scaled_mm", *args, _stream(a))
     else:
         _call("w8a8_scaled_mm_ws", *args, _ptr(workspace),
               workspace.numel() * workspace.element_size(), _stream(a))
     return out
+
+
+def w8a8_scaled_mm_noalloc(a: torch.Tensor, b: torch.Tensor, a_scales: torch.Tensor | None,
+                           b_scales: torch.Tensor | None, out_dtype=torch.bfloat16,
+                           out: torch.Tensor | None = None) -> torch.Tensor:
+    """w8a8_scaled_mm with split K through the library's static device
+    scratch instead of a workspace (the C call allocates nothing; pass `out`
+    to allocate nothing here either). Calls that overlap on one GPU race on
+    the scratch."""
+    return w8a8_scaled_mm(a, b, a_scales, b_scales, out_dtype, out, workspace="static")
 
 
 def w8a8_quant_scaled_mm(x: torch.Tensor, b: torch.Tensor, b_scales: torch.Tensor | None,
@@ -598,6 +616,7 @@ def version() -> str:
 
 
 __all__ = ["w8a8_quant_per_token", "w8a8_quant_per_tensor", "w8a8_scaled_mm",
+           "w8a8_scaled_mm_noalloc",
            "w8a8_scaled_mm_kernel", "w8a8_scaled_mm_workspace_size", "w8a8_quant_scaled_mm", "w8a8_quant_scaled_mm_kernel",
            "kv_fp8_scaled_quant", "kv_fp8_scaled_dequant", "scaled_mm", "W8A8Error",
            "w8a8_expand_shard_scales", "w8a8_requant_shared_scale",

@@ -256,6 +256,30 @@ w8a8_status w8a8_scaled_mm_ws(void* out, w8a8_dtype ot, int64_t ldo, const void*
     return from_hip(w8a8::launch_scaled_mm(p, stream), fn);
 }
 
+w8a8_status w8a8_scaled_mm_noalloc(void* out, w8a8_dtype ot, int64_t ldo, const void* a,
+                                   int64_t lda, const void* b, int64_t ldb, w8a8_qtype qt,
+                                   int64_t M, int64_t N, int64_t K, const float* a_scales,
+                                   int64_t n_a, const float* b_scales, int64_t n_b,
+                                   hipStream_t stream) {
+    const char* fn = "w8a8_scaled_mm_noalloc";
+    w8a8_status s = scaled_mm_check(fn, out, ot, ldo, a, lda, b, ldb, qt, M, N, K, a_scales, n_a,
+                                    b_scales, n_b);
+    if (s != W8A8_OK || M == 0 || N == 0) return s;
+    w8a8::GemmProblem p = make_problem(out, ot, ldo, a, lda, b, ldb, qt, M, N, K, a_scales, n_a,
+                                       b_scales, n_b);
+    int64_t needed = 0;
+    const hipError_t e = w8a8::launch_scaled_mm_noalloc(p, stream, &needed);
+    if (needed > 0)
+        return fail(W8A8_ERR_UNSUPPORTED,
+                    "%s: M=%lld N=%lld K=%lld needs %lld bytes of split-K scratch, the library "
+                    "holds %lld", fn, (long long)M, (long long)N, (long long)K, (long long)needed,
+                    (long long)w8a8::scaled_mm_noalloc_scratch_bytes());
+    if (e == hipErrorInvalidDevice)
+        return fail(W8A8_ERR_INVALID_ARG, "%s: the stream must belong to the current device (whose "
+                    "scratch the call uses)", fn);
+    return from_hip(e, fn);
+}
+
 w8a8_status kv_fp8_scaled_quant(const void* x, w8a8_dtype xt, int64_t n, uint8_t* q, float* scale,
                                 int dynamic, hipStream_t stream) {
     const char* fn = "kv_fp8_scaled_quant";

@@ -20,6 +20,9 @@
 // The epilogue is fused: scales applied in fp32 and the result rounded to
 // nearest even into bf16/fp16 in registers, then stored once.
 
+#include <atomic>
+#include <mutex>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -976,6 +979,82 @@ hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st) {
     }
     if (p.qt == Q_FP8) return dispatch_ot<Q_FP8>(p.ot, a, st);
     return dispatch_ot<Q_INT8>(p.ot, a, st);
+}
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Scratch for callers that cannot allocate (code under HIP graph capture,
+// serving loops, harnesses that forbid allocation): the split-K partial sums
+// of w8a8_scaled_mm_noalloc live in this file-scope device array instead of a
+// caller workspace. Each GPU the library runs on holds its own copy until the
+// process ends. In host code `scratch` names a host-side stand-in, not the
+// device address: the address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and only that pointer is
+// handed to kernels. Every call on one GPU shares that GPU's array; the split
+// kernels overwrite every partial sum they later read, so nothing has to be
+// cleared between calls, but calls that overlap on one GPU (concurrent
+// streams, threads) race on it.
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchBytes = int64_t(16) << 20;
+// The largest split plan (M = 64, N = 16320, 4 splits of 4-byte sums) fits.
+static_assert(int64_t(4) * 64 * 16320 * 4 <= kScratchBytes, "scratch holds every split plan");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the current device (looked up once).
+hipError_t scratch_on_current_device(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
+}  // namespace
+
+int64_t scaled_mm_noalloc_scratch_bytes() { return kScratchBytes; }
+
+hipError_t launch_scaled_mm_noalloc(const GemmProblem& p, hipStream_t st, int64_t* needed) {
+    *needed = 0;
+    if (p.M == 0 || p.N == 0) return hipSuccess;
+    GemmProblem q = p;
+    q.workspace = nullptr;
+    q.workspace_bytes = 0;
+    const SplitPlan d = plan_splitk(p.M, p.N, p.K);
+    if (d.splits > 1) {
+        if (d.workspace_bytes > kScratchBytes) {
+            *needed = d.workspace_bytes;
+            return hipErrorInvalidValue;
+        }
+        if (st) {  // the scratch used is the current device's: the stream must be on it
+            int cur = -1;
+            hipDevice_t sd = -1;
+            hipError_t e = hipGetDevice(&cur);
+            if (e == hipSuccess) e = hipStreamGetDevice(st, &sd);
+            if (e != hipSuccess) return e;
+            if (sd != cur) return hipErrorInvalidDevice;
+        }
+        hipError_t e = scratch_on_current_device(&q.workspace);
+        if (e != hipSuccess) return e;
+        q.workspace_bytes = kScratchBytes;
+    }
+    return launch_scaled_mm(q, st);
 }
 
 // Measured on MI355X (Llama-3-8B decode shapes): the fused kernel saves the

@@ -71,6 +71,12 @@ SplitPlan plan_splitk(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st);
 
+// launch_scaled_mm with split K through the library's static device scratch
+// (no caller workspace, no allocation); *needed is set to the scratch bytes
+// a problem would need when it is more than the scratch holds.
+hipError_t launch_scaled_mm_noalloc(const GemmProblem& p, hipStream_t st, int64_t* needed);
+int64_t scaled_mm_noalloc_scratch_bytes();
+
 // Dynamic per-token quantisation of x [M, K] into q / a_scales, then the
 // scaled product with p's B and b scales (p.a, p.lda, p.sa are ignored).
 // Problems with quant_scaled_mm_fused() run as one fused kernel.
