@@ -95,6 +95,8 @@ def lib():
         L.oracle_kv_dequant.argtypes = [P, I64, P, P, I]
         L.oracle_quant_per_token_azp.restype = None
         L.oracle_quant_per_token_azp.argtypes = [P, I, I64, I64, I64, P, I64, P, P]
+        L.oracle_quant_per_tensor_azp.restype = None
+        L.oracle_quant_per_tensor_azp.argtypes = [P, I, I64, I64, I64, P, I64, P, P, I]
         L.oracle_colsum.restype = None
         L.oracle_colsum.argtypes = [P, I64, I64, I64, P]
         L.oracle_scaled_mm_azp.restype = None
@@ -229,6 +231,20 @@ def quant_per_token_azp(x: np.ndarray, xtype: str | None = None):
     lib().oracle_quant_per_token_azp(_ptr(x), _xtype_of(x, xtype), M, K, K, _ptr(q), K, _ptr(s),
                                      _ptr(z))
     return q, s, z
+
+
+def quant_per_tensor_azp(x: np.ndarray, xtype: str | None = None, scale=None, azp=None,
+                         dynamic: bool = True):
+    """Asymmetric per-tensor int8 quantisation -> (codes uint8 [M, K], scale f32, zero point int32).
+    dynamic: the scale and zero point come from the whole tensor's range; else the given ones."""
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    q = np.empty((M, K), np.uint8)
+    s = np.array([1.0 if scale is None else scale], np.float32)
+    z = np.array([0 if azp is None else azp], np.int32)
+    lib().oracle_quant_per_tensor_azp(_ptr(x), _xtype_of(x, xtype), M, K, K, _ptr(q), K, _ptr(s),
+                                      _ptr(z), 1 if dynamic else 0)
+    return q, s[0], int(z[0])
 
 
 def colsum(b: np.ndarray) -> np.ndarray:

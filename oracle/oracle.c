@@ -309,6 +309,42 @@ void oracle_quant_per_token_azp(const void* x, int xtype, int64_t M, int64_t K, 
     }
 }
 
+/* The same scheme with one scale and zero point for the whole tensor.     */
+/* dynamic: lo and hi over every element (0 included), written to *scale   */
+/* and *azp; static (calibrated): *scale and *azp are read (NULL: 1.0, 0). */
+void oracle_quant_per_tensor_azp(const void* x, int xtype, int64_t M, int64_t K, int64_t ldx,
+                                 uint8_t* q, int64_t ldq, float* scale, int32_t* azp,
+                                 int dynamic) {
+    float s = 1.0f, zf = 0.0f;
+    if (dynamic) {
+        float lo = 0.0f, hi = 0.0f;
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t k = 0; k < K; ++k) {
+                float v = load_x(x, xtype, m * ldx + k);
+                if (v > hi) hi = v;
+                if (v < lo) lo = v;
+            }
+        const float d = hi - lo;
+        s = d == 0.0f ? 1.0f : d / 255.0f;
+        zf = rintf(-128.0f - lo / s);
+        if (zf < -128.0f) zf = -128.0f;
+        if (zf > 127.0f) zf = 127.0f;
+        *scale = s;
+        *azp = (int32_t)zf;
+    } else {
+        if (scale) s = *scale;
+        if (azp) zf = (float)*azp;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            float r = rintf(load_x(x, xtype, m * ldx + k) / s) + zf;
+            if (r < -128.0f) r = -128.0f;
+            if (r > 127.0f) r = 127.0f;
+            q[m * ldq + k] = (uint8_t)(int8_t)(int)r;
+        }
+}
+
 /* Sum of each int8 weight row's codes, colsum[n] = sum_k b[n, k]. */
 void oracle_colsum(const uint8_t* b, int64_t ldb, int64_t N, int64_t K, int32_t* out) {
     for (int64_t n = 0; n < N; ++n) {

@@ -179,3 +179,57 @@ def test_colsum_brute_force_tiny():
             c = int(b[n, k])
             total += c - 256 if c >= 128 else c
         assert cs[n] == total
+
+
+# ---------------------------------------------------------------- per tensor
+# One scale and zero point for the whole tensor ("[Kernel] Add w8a8 CUTLASS
+# kernels": zero points per tensor or per token): the per-token scheme over
+# all elements at once (dynamic), or with a calibrated scale and zero point
+# (static).
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_azp_per_tensor_dynamic_is_one_long_row(seed):
+    """The dynamic per-tensor result equals the per-token one of the tensor
+    laid out as a single row (itself pinned by the closed forms and ties above)."""
+    x = _rows(seed, M=6, K=96)
+    q, s, z = oracle.quant_per_tensor_azp(x, "f32")
+    q1, s1, z1 = oracle.quant_per_token_azp(x.reshape(1, -1), "f32")
+    assert s == s1[0] and z == z1[0]
+    assert np.array_equal(q.reshape(1, -1), q1)
+
+
+def test_azp_per_tensor_closed_forms():
+    x = _rows(3, M=5, K=64)
+    q, s, z = oracle.quant_per_tensor_azp(x, "f32")
+    lo, hi = min(0.0, float(x.min())), max(0.0, float(x.max()))
+    assert s == np.float32(np.float32(hi - lo) / np.float32(255.0))
+    qi = q.view(np.int8)
+    assert qi.reshape(-1)[int(np.argmin(x))] == -128
+    assert (qi[x == 0] == z).all()
+    deq = (qi.astype(np.float64) - z) * np.float64(s)
+    assert (np.abs(deq - x) <= 0.5 * np.float64(s) * (1 + 2.0 ** -12)).all()
+    zq, zs, zz = oracle.quant_per_tensor_azp(np.zeros((3, 32), np.float32), "f32")
+    assert zs == np.float32(1.0) and zz == -128 and (zq.view(np.int8) == -128).all()
+
+
+@pytest.mark.parametrize("scale,azp", [(0.05, 3), (1.0, -128), (0.37, 127), (2.0, 0)])
+def test_azp_per_tensor_static_brute_force(scale, azp):
+    """Static: q = clamp(round_half_even(fl32(x / s)) + z, -128, 127), element
+    by element with numpy's binary32 division and Python's round (ties to even)."""
+    x = _rows(4, M=6, K=48) * np.float32(3.0)
+    x[0, :8] = np.float32(scale) * np.array([0.5, 1.5, 2.5, -0.5, -1.5, 100.5, -300.0, 1e6], np.float32)
+    q, s, z = oracle.quant_per_tensor_azp(x, "f32", scale=scale, azp=azp, dynamic=False)
+    assert s == np.float32(scale) and z == azp
+    qi = q.view(np.int8)
+    for m in range(x.shape[0]):
+        for k in range(x.shape[1]):
+            t = float(np.float32(x[m, k]) / np.float32(scale))
+            want = min(127, max(-128, round(t) + azp))
+            assert qi[m, k] == want, (m, k, x[m, k], t)
+
+
+def test_azp_per_tensor_static_null_means_one_and_zero():
+    x = _rows(5, M=6, K=32)
+    q, s, z = oracle.quant_per_tensor_azp(x, "f32", dynamic=False)
+    q2, _, _ = oracle.quant_per_tensor_azp(x, "f32", scale=1.0, azp=0, dynamic=False)
+    assert s == np.float32(1.0) and z == 0 and np.array_equal(q, q2)
