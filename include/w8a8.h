@@ -236,6 +236,24 @@ w8a8_status w8a8_quant_per_token_azp(const void* x, w8a8_dtype xt, int64_t M, in
                                      hipStream_t stream);
 
 /*
+ * Asymmetric int8 activations per tensor [P1: zero points per tensor or per
+ * token for the asymmetric int8 case]: the scheme of
+ * w8a8_quant_per_token_azp with one scale and zero point for the whole
+ * tensor x [M, K].
+ * dynamic == 1: lo and hi over every element (0 included), s and z as
+ *   above, written to *scale and *azp (both required). Three kernels on
+ *   `stream`; until the last one ends, the last (at most 8 KB of) codes of q
+ *   hold intermediate values (partial ranges).
+ * dynamic == 0 (static, calibrated): s = *scale and z = *azp are read
+ *   (NULL: 1.0 and 0).
+ * q = clamp(rint(x / s) + z, -128, 127). Feeds w8a8_scaled_mm_azp with
+ * n_a = n_azp = 1. Same layout rules as w8a8_quant_per_token.
+ */
+w8a8_status w8a8_quant_per_tensor_azp(const void* x, w8a8_dtype xt, int64_t M, int64_t K,
+                                      int64_t ldx, void* q, int64_t ldq, float* scale,
+                                      int32_t* azp, int dynamic, hipStream_t stream);
+
+/*
  * colsum[n] = sum_k b[n, k] over int8 weight codes b [N, K] (row stride ldb
  * bytes; the K x N column-major B of the product), int32, device. Computed
  * once per weight. K and ldb multiples of 16, b 16-byte aligned.

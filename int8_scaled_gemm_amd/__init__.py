@@ -64,6 +64,7 @@ SIGNATURES = {
     "kv_fp8_scaled_quant": [_P, _I, _I64, _P, _P, _I, _P],
     "kv_fp8_scaled_dequant": [_P, _I64, _P, _P, _I, _P],
     "w8a8_quant_per_token_azp": [_P, _I, _I64, _I64, _I64, _P, _I64, _P, _P, _P],
+    "w8a8_quant_per_tensor_azp": [_P, _I, _I64, _I64, _I64, _P, _I64, _P, _P, _I, _P],
     "w8a8_colsum": [_P, _I64, _I64, _I64, _P, _P],
     "w8a8_scaled_mm_azp": [_P, _I, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64,
                            _P, _P, _I64, _P],
@@ -344,6 +345,31 @@ def w8a8_quant_per_token_azp(x: torch.Tensor, q: torch.Tensor | None = None,
     return q, scales, azp
 
 
+def w8a8_quant_per_tensor_azp(x: torch.Tensor, scale: torch.Tensor | None = None,
+                              azp: torch.Tensor | None = None, dynamic: bool = True,
+                              q: torch.Tensor | None = None):
+    """Asymmetric per-tensor int8 quantisation of x [M, K] -> (codes int8
+    [M, K], scale fp32 [1], zero point int32 [1]). dynamic: both from the
+    tensor's range (allocated when None); static: the given ones (None: 1.0, 0)."""
+    M, K, ldx = _rows(x, "x")
+    _want(x, "x", dtypes=_X_DTYPES)
+    _want(q, "q", shape=(M, K), dtypes=(torch.int8,))
+    _want(scale, "scale", numel=1, dtypes=_F32)
+    _want(azp, "azp", numel=1, dtypes=_I32)
+    _check_cuda(x, q, scale, azp)
+    _same_device(x, q, scale, azp)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if dynamic and scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    if dynamic and azp is None:
+        azp = torch.empty(1, dtype=torch.int32, device=x.device)
+    _, _, ldq = _rows(q, "q")
+    _call("w8a8_quant_per_tensor_azp", _ptr(x), _dtype(x.dtype), M, K, ldx, _ptr(q), ldq,
+          _ptr(scale), _ptr(azp), 1 if dynamic else 0, _stream(x))
+    return q, scale, azp
+
+
 def w8a8_colsum(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Per-row sums of int8 weight codes w [N, K] (int32 [N])."""
     if w.dtype != torch.int8:
@@ -620,7 +646,8 @@ __all__ = ["w8a8_quant_per_token", "w8a8_quant_per_tensor", "w8a8_scaled_mm",
            "w8a8_scaled_mm_kernel", "w8a8_scaled_mm_workspace_size", "w8a8_quant_scaled_mm", "w8a8_quant_scaled_mm_kernel",
            "kv_fp8_scaled_quant", "kv_fp8_scaled_dequant", "scaled_mm", "W8A8Error",
            "w8a8_expand_shard_scales", "w8a8_requant_shared_scale",
-           "w8a8_quant_per_token_azp", "w8a8_colsum", "w8a8_scaled_mm_azp",
+           "w8a8_quant_per_token_azp", "w8a8_quant_per_tensor_azp", "w8a8_colsum",
+           "w8a8_scaled_mm_azp",
            "kv_fp8_decode_attention", "kv_fp8_attention_workspace_size",
            "quant_per_token", "quant_per_tensor", "kv_quant", "kv_dequant",
            "load_library", "version", "LIB_PATH", "SIGNATURES"]

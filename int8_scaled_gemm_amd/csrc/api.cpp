@@ -322,6 +322,22 @@ w8a8_status w8a8_quant_per_token_azp(const void* x, w8a8_dtype xt, int64_t M, in
                     fn);
 }
 
+w8a8_status w8a8_quant_per_tensor_azp(const void* x, w8a8_dtype xt, int64_t M, int64_t K,
+                                      int64_t ldx, void* q, int64_t ldq, float* scale,
+                                      int32_t* azp, int dynamic, hipStream_t stream) {
+    const char* fn = "w8a8_quant_per_tensor_azp";
+    if (dynamic != 0 && dynamic != 1) return fail(W8A8_ERR_INVALID_ARG, "%s: dynamic must be 0 or 1", fn);
+    w8a8_status s = check_quant_io(fn, x, xt, M, K, ldx, q, W8A8_Q_INT8, ldq);
+    if (s != W8A8_OK) return s;
+    if (dynamic && (!scale || !azp)) return fail(W8A8_ERR_INVALID_ARG, "%s: dynamic scaling needs scale and azp buffers", fn);
+    if ((reinterpret_cast<uintptr_t>(scale) | reinterpret_cast<uintptr_t>(azp)) & 3u)
+        return fail(W8A8_ERR_ALIGNMENT, "%s: scale and azp must be 4-byte aligned", fn);
+    if (!dynamic && (M == 0 || K == 0)) return ok();
+    return from_hip(w8a8::launch_quant_per_tensor_azp(xt, x, M, K, ldx, static_cast<uint8_t*>(q), ldq,
+                                                      scale, azp, dynamic != 0, stream),
+                    fn);
+}
+
 w8a8_status w8a8_colsum(const void* b, int64_t ldb, int64_t N, int64_t K, int32_t* colsum,
                         hipStream_t stream) {
     const char* fn = "w8a8_colsum";

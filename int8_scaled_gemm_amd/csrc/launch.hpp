@@ -24,6 +24,11 @@ hipError_t launch_quant_per_token_azp(int xt, const void* x, int64_t M, int64_t 
                                       hipStream_t st);
 hipError_t launch_colsum(const uint8_t* b, int64_t ldb, int64_t N, int64_t K, int32_t* colsum,
                          hipStream_t st);
+// Asymmetric int8 per tensor: one scale and zero point, from the whole
+// tensor's range (dynamic: written to *scale and *azp) or given (static).
+hipError_t launch_quant_per_tensor_azp(int xt, const void* x, int64_t M, int64_t K, int64_t ldx,
+                                       uint8_t* q, int64_t ldq, float* scale, int32_t* azp,
+                                       bool dynamic, hipStream_t st);
 
 // Merged layers: the most shards one call takes (their row ends travel as
 // kernel arguments).

@@ -483,6 +483,196 @@ __global__ __launch_bounds__(kBlock) void quant_rows_azp_kernel(const void* __re
     }
 }
 
+// The asymmetric scheme's scale, its reciprocal and the zero point from the
+// range: lo = -nlo <= 0 <= hi.
+struct AzpParams {
+    float s, zf;
+    double r;
+};
+
+__device__ __forceinline__ AzpParams azp_params(float hi, float nlo) {
+    AzpParams a;
+    const float lo = -nlo;
+    const float d = hi - lo;
+    a.s = d == 0.0f ? 1.0f : d / 255.0f;
+    a.r = 1.0 / static_cast<double>(a.s);
+    a.zf = fminf(fmaxf(__builtin_rintf(-128.0f - div_rn(lo, a.r)), -128.0f), 127.0f);
+    return a;
+}
+
+__device__ __forceinline__ u32x2 quant8_azp(const float v[8], double r, float zf) {
+    uint32_t w[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float c = fminf(fmaxf(__builtin_rintf(div_rn(v[j], r)) + zf, -128.0f), 127.0f);
+        w[j >> 2] |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xFFu) << (8 * (j & 3));
+    }
+    return u32x2{w[0], w[1]};
+}
+
+// Asymmetric per tensor: the range pass, as absmax_kernel, with two partial
+// maxima per workgroup, max(x, 0) and max(-x, 0), stored as 8 bytes in the
+// tail of the code buffer.
+template <int XT>
+__global__ __launch_bounds__(kBlock) void range_kernel(const void* __restrict__ x, int64_t ldx,
+                                                       Units u, int64_t K, uint8_t* q, int64_t ldq,
+                                                       Tail tail) {
+    float hi = 0.0f, nlo = 0.0f;
+    for (uint32_t base = blockIdx.x * kAbsUnroll; base < u.total; base += gridDim.x * kAbsUnroll) {
+        float v[kAbsUnroll][8];
+        bool ok[kAbsUnroll];
+#pragma unroll
+        for (int j = 0; j < kAbsUnroll; ++j) {
+            int64_t row, k;
+            ok[j] = unit_coords(u, base + j, K, row, k);
+            if (ok[j]) load8<XT, false>(x, row * ldx + k, v[j]);  // cached: read again next
+        }
+#pragma unroll
+        for (int j = 0; j < kAbsUnroll; ++j)
+            if (ok[j])
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    hi = fmaxf(hi, v[j][e]);
+                    nlo = fmaxf(nlo, -v[j][e]);
+                }
+    }
+    hi = wave_max(hi);
+    nlo = wave_max(nlo);
+    __shared__ float part[2][kBlock / 64];
+    if ((threadIdx.x & 63) == 0) {
+        part[0][threadIdx.x >> 6] = hi;
+        part[1][threadIdx.x >> 6] = nlo;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; ++w) {
+            hi = fmaxf(hi, part[0][w]);
+            nlo = fmaxf(nlo, part[1][w]);
+        }
+        *reinterpret_cast<f32x2*>(code_at(q, ldq, K, tail.start + 8 * blockIdx.x)) = f32x2{hi, nlo};
+    }
+}
+
+// The range from the stored partials, in every thread of the workgroup.
+__device__ void reduce_range(uint8_t* q, int64_t ldq, int64_t K, const Tail& tail, float& hi,
+                             float& nlo) {
+    hi = nlo = 0.0f;
+    for (int i = threadIdx.x; i < tail.parts; i += kBlock) {
+        const f32x2 p = *reinterpret_cast<const f32x2*>(code_at(q, ldq, K, tail.start + 8 * i));
+        hi = fmaxf(hi, p[0]);
+        nlo = fmaxf(nlo, p[1]);
+    }
+    hi = wave_max(hi);
+    nlo = wave_max(nlo);
+    __shared__ float part[2][kBlock / 64];
+    if ((threadIdx.x & 63) == 0) {
+        part[0][threadIdx.x >> 6] = hi;
+        part[1][threadIdx.x >> 6] = nlo;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) {
+        hi = fmaxf(hi, part[0][w]);
+        nlo = fmaxf(nlo, part[1][w]);
+    }
+}
+
+// Quantise with one scale and zero point. DYNAMIC: from the partials in the
+// tail, which is left to finish_tail_azp_kernel; otherwise *scale and *azp
+// (NULL: 1.0 and 0).
+template <int XT, bool DYNAMIC>
+__global__ __launch_bounds__(kBlock) void quant_tensor_azp_kernel(const void* __restrict__ x,
+                                                                  int64_t ldx, uint8_t* q,
+                                                                  int64_t ldq,
+                                                                  const float* __restrict__ scale,
+                                                                  const int32_t* __restrict__ azp,
+                                                                  Units u, int64_t K, Tail tail) {
+    AzpParams a;
+    if constexpr (DYNAMIC) {
+        float hi, nlo;
+        reduce_range(q, ldq, K, tail, hi, nlo);
+        a = azp_params(hi, nlo);
+    } else {
+        a.s = scale ? *scale : 1.0f;
+        a.r = 1.0 / static_cast<double>(a.s);
+        a.zf = azp ? static_cast<float>(*azp) : 0.0f;
+    }
+    for (uint32_t base = blockIdx.x * kUnroll; base < u.total; base += gridDim.x * kUnroll) {
+        float v[kUnroll][8];
+        bool ok[kUnroll];
+        int64_t row[kUnroll], k[kUnroll];
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+            ok[j] = unit_coords(u, base + j, K, row[j], k[j]);
+            if (DYNAMIC && ok[j] && row[j] * K + k[j] >= tail.start) ok[j] = false;
+            if (ok[j]) load8<XT>(x, row[j] * ldx + k[j], v[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j)
+            if (ok[j]) *reinterpret_cast<u32x2*>(q + row[j] * ldq + k[j]) = quant8_azp(v[j], a.r, a.zf);
+    }
+}
+
+// One workgroup: scale and zero point from the partials, written out, then
+// the tail's codes over the partials once every thread has read them.
+template <int XT>
+__global__ __launch_bounds__(kBlock) void finish_tail_azp_kernel(const void* __restrict__ x,
+                                                                 int64_t ldx, uint8_t* q,
+                                                                 int64_t ldq, float* scale,
+                                                                 int32_t* azp, int64_t M,
+                                                                 int64_t K, Tail tail) {
+    float hi, nlo;
+    reduce_range(q, ldq, K, tail, hi, nlo);
+    const AzpParams a = azp_params(hi, nlo);
+    __syncthreads();  // every partial has been read
+    if (threadIdx.x == 0) {
+        *scale = a.s;
+        *azp = static_cast<int32_t>(a.zf);
+    }
+    for (int64_t e = tail.start + 8 * static_cast<int64_t>(threadIdx.x); e < M * K; e += 8 * kBlock) {
+        const int64_t row = e / K, k = e % K;  // 8 elements, never across a row (K % 16 == 0)
+        float v[8];
+        load8<XT>(x, row * ldx + k, v);
+        *reinterpret_cast<u32x2*>(q + row * ldq + k) = quant8_azp(v, a.r, a.zf);
+    }
+}
+
+// scale 1.0, zero point -128: the range [0, 0] of an empty tensor
+__global__ void fill_azp_empty_kernel(float* s, int32_t* z) {
+    *s = 1.0f;
+    *z = -128;
+}
+
+template <int XT>
+hipError_t per_tensor_azp_typed(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                                int64_t ldq, float* scale, int32_t* azp, bool dynamic,
+                                hipStream_t st) {
+    const Units u = make_units(M, K);
+    const int g = grid_for(u.total, kUnroll);
+    if (!dynamic) {
+        if (M * K == 0) return hipSuccess;
+        hipLaunchKernelGGL((quant_tensor_azp_kernel<XT, false>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq,
+                           static_cast<const float*>(scale), static_cast<const int32_t*>(azp), u, K, Tail{0, 0});
+        return hipGetLastError();
+    }
+    const int64_t total = M * K;
+    if (total == 0) {
+        hipLaunchKernelGGL(fill_azp_empty_kernel, dim3(1), dim3(1), 0, st, scale, azp);
+        return hipGetLastError();
+    }
+    Tail tail;
+    tail.parts = std::min(grid_for(u.total, kAbsUnroll), 1024);
+    const int64_t tail_len = (8 * static_cast<int64_t>(tail.parts) + 15) / 16 * 16;
+    tail.start = total <= 65536 ? 0 : total - tail_len;
+    hipLaunchKernelGGL((range_kernel<XT>), dim3(tail.parts), dim3(kBlock), 0, st, x, ldx, u, K, q, ldq, tail);
+    if (tail.start > 0)
+        hipLaunchKernelGGL((quant_tensor_azp_kernel<XT, true>), dim3(std::min(g, 2048)), dim3(kBlock), 0, st, x, ldx,
+                           q, ldq, static_cast<const float*>(scale), static_cast<const int32_t*>(azp), u, K, tail);
+    hipLaunchKernelGGL((finish_tail_azp_kernel<XT>), dim3(1), dim3(kBlock), 0, st, x, ldx, q, ldq, scale, azp, M, K, tail);
+    return hipGetLastError();
+}
+
 // Per-row sums of int8 weight codes: one wave per row.
 __global__ __launch_bounds__(kBlock) void colsum_kernel(const uint8_t* __restrict__ b, int64_t ldb,
                                                        int64_t N, int64_t K, int32_t* __restrict__ out) {
@@ -513,6 +703,16 @@ hipError_t launch_quant_per_token_azp(int xt, const void* x, int64_t M, int64_t 
         default: hipLaunchKernelGGL((quant_rows_azp_kernel<D_F32>), g, blk, 0, st, x, ldx, q, ldq, scales, azp, K); break;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_quant_per_tensor_azp(int xt, const void* x, int64_t M, int64_t K, int64_t ldx,
+                                       uint8_t* q, int64_t ldq, float* scale, int32_t* azp,
+                                       bool dynamic, hipStream_t st) {
+    switch (xt) {
+        case D_BF16: return per_tensor_azp_typed<D_BF16>(x, M, K, ldx, q, ldq, scale, azp, dynamic, st);
+        case D_FP16: return per_tensor_azp_typed<D_FP16>(x, M, K, ldx, q, ldq, scale, azp, dynamic, st);
+        default: return per_tensor_azp_typed<D_F32>(x, M, K, ldx, q, ldq, scale, azp, dynamic, st);
+    }
 }
 
 hipError_t launch_colsum(const uint8_t* b, int64_t ldb, int64_t N, int64_t K, int32_t* colsum,

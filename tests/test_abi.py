@@ -258,3 +258,16 @@ def test_azp_validation(lib):
     assert f(K=65552, lda=65552, ldb=65552) == UNSUP
     assert f(ldb=64) == LAYOUT
     assert f(M=0, out=None, a=None, b=None) == OK
+
+
+def test_per_tensor_azp_validation(lib):
+    """Asymmetric int8 per tensor: host-side checks."""
+    qt = lib.w8a8_quant_per_tensor_azp
+    assert qt(FAKE, 0, 4, 128, 128, FAKE, 128, FAKE, FAKE, 2, None) == INVALID    # dynamic 0 or 1
+    assert qt(FAKE, 0, 4, 128, 128, FAKE, 128, None, FAKE, 1, None) == INVALID    # dynamic: outputs
+    assert qt(FAKE, 0, 4, 128, 128, FAKE, 128, FAKE, None, 1, None) == INVALID
+    assert qt(FAKE, 5, 4, 128, 128, FAKE, 128, FAKE, FAKE, 1, None) == DTYPE
+    assert qt(FAKE, 0, 4, 100, 112, FAKE, 112, FAKE, FAKE, 1, None) == ALIGN
+    assert qt(FAKE, 0, 4, 128, 128, FAKE, 128, FAKE + 2, FAKE, 1, None) == ALIGN
+    assert qt(FAKE, 0, 4, 128, 64, FAKE, 128, FAKE, FAKE, 1, None) == LAYOUT      # ldx < K
+    assert qt(None, 0, 0, 128, 128, None, 128, None, None, 0, None) == OK          # static, empty

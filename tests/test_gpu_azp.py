@@ -73,10 +73,11 @@ SHAPES = [(1, 4096, 4096), (16, 28672, 1024), (64, 4096, 4096 + 16), (33, 1000, 
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_scaled_mm_azp_parity(M, N, K, per_token):
     x = _x(M, K, 3 * M + N)
-    a, sa, z = oracle.quant_per_token_azp(_host(x)[0], "bf16")
-    if not per_token:
-        z = z[:1]
-        sa = sa[:1]
+    if per_token:
+        a, sa, z = oracle.quant_per_token_azp(_host(x)[0], "bf16")
+    else:  # one scale and zero point for the tensor
+        a, s1, z1 = oracle.quant_per_tensor_azp(_host(x)[0], "bf16")
+        sa, z = np.array([s1], np.float32), np.array([z1], np.int32)
     w = workloads.weights(N, K, seed=N + K)
     b, sb = oracle.quant_per_token(w.view(torch.int16).numpy().view(np.uint16), "int8", xtype="bf16")
     ad, bd = codes_to_dev(a, "int8"), codes_to_dev(b, "int8")
@@ -106,3 +107,55 @@ def test_scaled_mm_azp_without_zero_points_is_the_symmetric_product():
     d2 = w8.w8a8_scaled_mm(ad, bd.t(), sa, sb, torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(d1.view(torch.int16), d2.view(torch.int16))
+
+
+# ---------------------------------------------------------------- per tensor
+@pytest.mark.parametrize("xtype", ["bf16", "fp16", "f32"])
+@pytest.mark.parametrize("M,K", [(1, 16), (5, 272), (300, 1040), (64, 28672), (2048, 4096)])
+def test_quant_per_tensor_azp_dynamic_parity(M, K, xtype):
+    """Scale, zero point and codes bit for bit; (300, 1040) and up go through
+    the three-kernel path whose partial ranges sit in the tail of the codes."""
+    x = _x(M, K, 7 * M + K, xtype)
+    xh, xt = _host(x)
+    q_ref, s_ref, z_ref = oracle.quant_per_tensor_azp(xh, xt)
+    q, s, z = w8.w8a8_quant_per_tensor_azp(x.to(DEV))
+    torch.cuda.synchronize()
+    assert f32_bits(s.cpu().numpy())[0] == f32_bits([s_ref])[0]
+    assert int(z.item()) == z_ref
+    assert np.array_equal(bits(q), q_ref)
+
+
+@pytest.mark.parametrize("scale,azp", [(0.05, 3), (0.37, 127), (2.0, -128)])
+def test_quant_per_tensor_azp_static_parity(scale, azp):
+    M, K = 300, 1040
+    x = _x(M, K, 11)
+    xh, xt = _host(x)
+    q_ref, _, _ = oracle.quant_per_tensor_azp(xh, xt, scale=scale, azp=azp, dynamic=False)
+    sd = torch.tensor([scale], dtype=torch.float32, device=DEV)
+    zd = torch.tensor([azp], dtype=torch.int32, device=DEV)
+    q, _, _ = w8.w8a8_quant_per_tensor_azp(x.to(DEV), sd, zd, dynamic=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(q), q_ref)
+    q0, _, _ = w8.w8a8_quant_per_tensor_azp(x.to(DEV), dynamic=False)   # NULL: 1.0 and 0
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(q0), oracle.quant_per_tensor_azp(xh, xt, dynamic=False)[0])
+
+
+def test_quant_per_tensor_azp_strided_zero_and_empty():
+    big = _x(400, 2048, 13)
+    x = big[:, 512:512 + 1040]                      # a strided view, 416000 elements
+    xh = np.ascontiguousarray(_host(big)[0][:, 512:512 + 1040])
+    q_ref, s_ref, z_ref = oracle.quant_per_tensor_azp(xh, "bf16")
+    qd = torch.zeros(400, 2048, dtype=torch.int8, device=DEV)
+    q, s, z = w8.w8a8_quant_per_tensor_azp(x.to(DEV), q=qd[:, 16:16 + 1040])
+    torch.cuda.synchronize()
+    assert f32_bits(s.cpu().numpy())[0] == f32_bits([s_ref])[0] and int(z.item()) == z_ref
+    assert np.array_equal(bits(q), q_ref)
+    assert (qd[:, :16] == 0).all() and (qd[:, 16 + 1040:] == 0).all()   # nothing outside the view
+    zero = torch.zeros(70, 1024, dtype=torch.bfloat16, device=DEV)
+    q, s, z = w8.w8a8_quant_per_tensor_azp(zero)
+    torch.cuda.synchronize()
+    assert float(s.item()) == 1.0 and int(z.item()) == -128 and (q == -128).all()
+    q, s, z = w8.w8a8_quant_per_tensor_azp(torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert float(s.item()) == 1.0 and int(z.item()) == -128
