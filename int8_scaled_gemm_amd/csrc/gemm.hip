@@ -272,14 +272,27 @@ __device__ __forceinline__ void store4(const GemmArgs& p, int m, int n, const Ac
     }
 }
 
+// Wait until at most `pending` (<= P) stages of L loads each are still in
+// flight; loads retire in issue order.
+template <int P, int L>
+__device__ __forceinline__ void wait_stages(int pending) {
+    if constexpr (P == 0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+        if (pending >= P) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(P * L) : "memory");
+        else wait_stages<P - 1, L>(pending);
+    }
+}
+
 // BM x BN block tile; WGM x WGN waves, each owning a (BM/WGM) x (BN/WGN)
-// wave tile of 32 x 32 MFMA tiles. K is walked in 128-byte stages through a
-// 2-stage LDS ring filled by direct loads, the loads of stage k+1 in flight
-// while stage k is consumed, one barrier per stage. Inside a stage the
-// fragments of the next 64-byte half are read from LDS while the MFMAs of
-// the current half run (two register sets, interleaved by the scheduler
-// hints below).
-template <int QT, int OT, int BM, int BN, int WGM, int WGN>
+// wave tile of 32 x 32 MFMA tiles. K is walked in 128-byte stages through an
+// ST-slot LDS ring filled by direct loads: while stage k is consumed the
+// loads of stages k+1 .. k+ST-1 are in flight, one barrier per stage (small
+// tiles do little work per stage, so they keep more stages in flight to
+// cover the memory latency). Inside a stage the fragments of the next
+// 64-byte half are read from LDS while the MFMAs of the current half run
+// (two register sets, interleaved by the scheduler hints below).
+template <int QT, int OT, int BM, int BN, int WGM, int WGN, int ST>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
     typedef typename Acc32Of<QT>::type Acc;
     constexpr int NW = WGM * WGN;
@@ -292,7 +305,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
     constexpr int kMfma = TM * TN * (QT == Q_FP8 ? 1 : 2), kReads = 2 * (TM + TN);
     constexpr int kReadsPerMfma = (kReads + kMfma - 1) / kMfma;
     static_assert(TM >= 1 && TN >= 1 && kLoads % NW == 0, "tile shape");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
+    static_assert(ST >= 2 && kLPW * (ST - 2) <= 63, "loads in flight");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * kStage];
 
     int tm, tn;
     if (!tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn)) return;
@@ -372,21 +386,28 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
         issue(0, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (KT > 1) issue(1, 1);
+#pragma unroll
+        for (int s = 1; s < ST; ++s)
+            if (s < KT) issue(s, s);
         read(xa, wa, 0, 0);
+        int cur = 0;
         for (int kt = 0; kt + 1 < KT; ++kt) {
-            const int cur = kt & 1;
+            const int nxt = cur + 1 == ST ? 0 : cur + 1;
             read(xb, wb, cur, 1);  // half 1 of stage kt, while half 0 runs
             mfmas(xa, wa);
             interleave();
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-            __syncthreads();  // stage kt+1 has landed; every wave is done reading stage kt
-            if (kt + 2 < KT) issue(kt + 2, cur);
-            read(xa, wa, cur ^ 1, 0);  // half 0 of stage kt+1, while half 1 of kt runs
+            // stage kt+1 has landed once at most the stages issued after it
+            // (kt+2 .. min(KT-1, kt+ST-1)) are pending
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            wait_stages<ST - 2, kLPW>(min(KT - 2 - kt, ST - 2));
+            __syncthreads();  // ... in every wave; every wave is done reading stage kt
+            if (kt + ST < KT) issue(kt + ST, cur);
+            read(xa, wa, nxt, 0);  // half 0 of stage kt+1, while half 1 of kt runs
             mfmas(xb, wb);
             interleave();
+            cur = nxt;
         }
-        read(xb, wb, (KT - 1) & 1, 1);
+        read(xb, wb, cur, 1);
         mfmas(xa, wa);
         interleave();
         mfmas(xb, wb);
@@ -402,63 +423,42 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
         // c ^ (r % (BN / 8)).
         constexpr int kChunks = BN / 8;
         constexpr int kRowsPerAccess = 64 / kChunks;
-        static_assert(BM * BN * 2 <= 2 * kStage, "the output tile fits the LDS ring");
+        static_assert(BM * BN * 2 <= ST * kStage, "the output tile fits the LDS ring");
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __syncthreads();  // every wave is done reading the ring
-        // The lane's scales, loaded once: its TM row scales and its TN x 16
-        // column scales (rows and columns past the matrix are clamped; they
-        // are never stored).
-        float sav[TM], sbv[TN][16];
+        // The lane's TM row scales (and zero points) are loaded once; its
+        // 16 column scales (and code sums) of each 32-column group j just
+        // before that group is written, so that few stay live at a time
+        // (rows and columns past the matrix are clamped; they are never
+        // stored).
+        float sav[TM];
+        int zv[TM];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) sav[i] = 1.0f;
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) sbv[j][e] = 1.0f;
-        if (p.sa) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                sav[i] = p.sa[p.sa_per_row ? min(m0 + wm * WM + i * 32 + (lane & 31), p.M - 1) : 0];
-        }
-        if (p.sb) {
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int col = wn * WN + j * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    sbv[j][e] = p.sb[p.sb_per_col ? min(n0 + col, p.N - 1) : 0];
-                }
-        }
-        // asymmetric int8: the lane's zero points and column code sums, also loaded once
-        int zv[TM], csv[TN][16];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) zv[i] = 0;
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) csv[j][e] = 0;
-        if constexpr (QT == Q_INT8) {
-            if (p.azp) {
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    zv[i] = p.azp[p.azp_per_row ? min(m0 + wm * WM + i * 32 + (lane & 31), p.M - 1) : 0];
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int col = wn * WN + j * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                        csv[j][e] = p.colsum[min(n0 + col, p.N - 1)];
-                    }
-            }
+        for (int i = 0; i < TM; ++i) {
+            const int m = min(m0 + wm * WM + i * 32 + (lane & 31), p.M - 1);
+            sav[i] = p.sa ? p.sa[p.sa_per_row ? m : 0] : 1.0f;
+            zv[i] = 0;
+            if constexpr (QT == Q_INT8)
+                if (p.azp) zv[i] = p.azp[p.azp_per_row ? m : 0];
         }
         // The tile into LDS; the zero-point term is compiled in only where used.
         auto write_tile = [&](auto with_azp) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = wm * WM + i * 32 + (lane & 31);
-                const float sa = sav[i];
+            for (int j = 0; j < TN; ++j) {
+                float sbv[16];
+                int csv[16];
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
+                for (int e = 0; e < 16; ++e) {
+                    const int col = wn * WN + j * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    const int n = min(n0 + col, p.N - 1);
+                    sbv[e] = p.sb ? p.sb[p.sb_per_col ? n : 0] : 1.0f;
+                    csv[e] = 0;
+                    if constexpr (decltype(with_azp)::value) csv[e] = p.colsum[n];
+                }
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const int row = wm * WM + i * 32 + (lane & 31);
+                    const float sa = sav[i];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int col = wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
@@ -466,8 +466,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             auto a = acc[i][j][4 * q + r];
-                            if constexpr (decltype(with_azp)::value) a -= zv[i] * csv[j][4 * q + r];
-                            const float d = static_cast<float>(a) * sa * sbv[j][4 * q + r];
+                            if constexpr (decltype(with_azp)::value) a -= zv[i] * csv[4 * q + r];
+                            const float d = static_cast<float>(a) * sa * sbv[4 * q + r];
                             h[r] = (OT == D_BF16) ? to_bf16_bits(d) : to_fp16_bits(d);
                         }
                         const int slot = (col >> 3) ^ (row % kChunks);
@@ -475,6 +475,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
                             u32x2{h[0] | (static_cast<uint32_t>(h[1]) << 16),
                                   h[2] | (static_cast<uint32_t>(h[3]) << 16)};
                     }
+                }
             }
         };
         if (QT == Q_INT8 && p.azp) write_tile(std::true_type{});
@@ -529,18 +530,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
 // Activation rows past M read as zeros; their results are never stored.
 // ---------------------------------------------------------------------------
 constexpr int kNonTemporal = 2;  // cache-policy operand of the buffer load: nt
-
-// Wait until at most `pending` (<= P) stages of L loads each are still in
-// flight; loads retire in issue order.
-template <int P, int L>
-__device__ __forceinline__ void wait_stages(int pending) {
-    if constexpr (P == 0) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else {
-        if (pending >= P) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(P * L) : "memory");
-        else wait_stages<P - 1, L>(pending);
-    }
-}
 
 template <int QT, int OT, int CB, int MT, int CH, int ST>
 __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
@@ -824,13 +813,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
     }
 }
 
-template <int QT, int OT, int BM, int BN, int WGM, int WGN>
+template <int QT, int OT, int BM, int BN, int WGM, int WGN, int ST>
 hipError_t run_tile(GemmArgs a, hipStream_t st) {
     a.tiles_m = (a.M + BM - 1) / BM;
     a.tiles_n = (a.N + BN - 1) / BN;
     const int total = a.tiles_m * a.tiles_n;
     const int grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((gemm_tile_kernel<QT, OT, BM, BN, WGM, WGN>), dim3(grid),
+    hipLaunchKernelGGL((gemm_tile_kernel<QT, OT, BM, BN, WGM, WGN, ST>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, a);
     return hipGetLastError();
 }
@@ -904,10 +893,10 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
         case kDecode16x64: return run_decode<QT, OT, 16, 4, 512, 2>(a, st);
         case kDecode16x16L: return run_decode<QT, OT, 16, 1, 2048, 2>(a, st);
         case kDecode16x64L: return run_decode<QT, OT, 16, 4, 1024, 2>(a, st);
-        case kTile256x256: return run_tile<QT, OT, 256, 256, 2, 4>(a, st);
-        case kTile256x128: return run_tile<QT, OT, 256, 128, 4, 2>(a, st);
-        case kTile128x128: return run_tile<QT, OT, 128, 128, 2, 2>(a, st);
-        default: return run_tile<QT, OT, 64, 64, 2, 2>(a, st);
+        case kTile256x256: return run_tile<QT, OT, 256, 256, 2, 4, 2>(a, st);
+        case kTile256x128: return run_tile<QT, OT, 256, 128, 4, 2, 3>(a, st);
+        case kTile128x128: return run_tile<QT, OT, 128, 128, 2, 2, 4>(a, st);
+        default: return run_tile<QT, OT, 64, 64, 2, 2, 4>(a, st);
     }
 }
 
