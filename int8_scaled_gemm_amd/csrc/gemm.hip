@@ -894,9 +894,9 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
         case kDecode16x16L: return run_decode<QT, OT, 16, 1, 2048, 2>(a, st);
         case kDecode16x64L: return run_decode<QT, OT, 16, 4, 1024, 2>(a, st);
         case kTile256x256: return run_tile<QT, OT, 256, 256, 2, 4, 2>(a, st);
-        case kTile256x128: return run_tile<QT, OT, 256, 128, 4, 2, 3>(a, st);
-        case kTile128x128: return run_tile<QT, OT, 128, 128, 2, 2, 4>(a, st);
-        default: return run_tile<QT, OT, 64, 64, 2, 2, 4>(a, st);
+        case kTile256x128: return run_tile<QT, OT, 256, 128, 4, 2, 2>(a, st);
+        case kTile128x128: return run_tile<QT, OT, 128, 128, 2, 2, 2>(a, st);
+        default: return run_tile<QT, OT, 64, 64, 2, 2, 2>(a, st);
     }
 }
 
