@@ -915,18 +915,24 @@ hipError_t dispatch_ot(int ot, const GemmArgs& a, hipStream_t st) {
 }  // namespace
 
 // Split-K for decode problems above 16 rows with a long K on weights too
-// narrow for 64-column blocks to occupy the GPU: 4 splits of the 64-column
-// kernel, so that each activation tile is read once per 64 columns instead
-// of once per 16. Shorter K does not repay the extra pass. Where 16-column
-// workgroups fill 129..256 CUs the long-stage 16-column kernel is as fast
-// without the extra pass (Llama-3-8B down, 64 x 4096 x 14336: 23.6 us
-// against 24.0 us split) and takes those problems.
+// narrow for 64-column blocks to occupy the GPU: the 64-column kernel with K
+// split so that each activation tile is read once per 64 columns instead of
+// once per 16. The split count fills one round of the kernel's workgroup
+// slots (two 64 KB workgroups per CU on 256 CUs), at most 4: measured on
+// MI355X at 64 rows, Llama-3-70B QKV (160 column blocks) 33.6 us with 4
+// splits (640 workgroups, a second partial round) against 27.0 us with 3,
+// and Llama-3-8B down 26.4 us on the long-stage 16-column kernel against
+// 24.0 us with 4 splits (24.4 us with 8). Shorter K does not repay the
+// extra pass (Llama-3-8B QKV and O at 64 rows: 14.2 -> 17.3 us, 11.6 ->
+// 14.7 us), nor do problems of at most 16 rows.
 SplitPlan plan_splitk(int64_t M, int64_t N, int64_t K) {
     SplitPlan d{1, 0, 0};
-    if (M <= 16 || M > 64 || K < 8192 || (N + 63) / 64 >= 256 || long_k_16(N, K)) return d;
+    const int64_t blocks = (N + 63) / 64;
+    if (M <= 16 || M > 64 || K < 8192 || blocks >= 256) return d;
+    constexpr int64_t kSlots = 512;   // resident 64-column workgroups
     constexpr int kStageBytes = 256;  // the 64-column kernel's K stage
     const int64_t stages = (K + kStageBytes - 1) / kStageBytes;
-    d.splits = 4;
+    d.splits = static_cast<int>(std::min<int64_t>(4, std::max<int64_t>(2, kSlots / blocks)));
     d.stages_per_split = static_cast<int>((stages + d.splits - 1) / d.splits);
     d.workspace_bytes = static_cast<int64_t>(d.splits) * M * N * 4;
     return d;

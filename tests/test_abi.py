@@ -187,10 +187,12 @@ def test_quant_scaled_mm_validation(lib):
 def test_split_k_workspace_plan(lib):
     """Which problems split K with a workspace, and how much they need."""
     size = lib.w8a8_scaled_mm_workspace_size
-    assert size(64, 8192, 14336) == 4 * 64 * 8192 * 4
+    assert size(64, 8192, 14336) == 4 * 64 * 8192 * 4     # 128 column blocks: 4 splits
     assert size(17, 8192, 8192) == 4 * 17 * 8192 * 4
-    assert size(40, 1000, 8192) == 4 * 40 * 1000 * 4      # few 16-column workgroups
-    assert size(64, 4096, 14336) == 0                      # Llama-3-8B down: the long-stage kernel
+    assert size(40, 1000, 8192) == 4 * 40 * 1000 * 4      # few column blocks: at most 4 splits
+    assert size(64, 10240, 8192) == 3 * 64 * 10240 * 4    # 160 column blocks: 3 splits fill 512
+    assert size(64, 16320, 8192) == 2 * 64 * 16320 * 4    # 255 column blocks: 2 splits
+    assert size(64, 4096, 14336) == 4 * 64 * 4096 * 4     # Llama-3-8B down
     assert size(16, 4096, 14336) == 0                      # M <= 16: no split
     assert size(64, 4096, 4096) == 0                       # short K
     assert size(64, 28672, 8192) == 0                      # wide N
@@ -199,7 +201,8 @@ def test_split_k_workspace_plan(lib):
     name = lambda M, N, K: lib.w8a8_scaled_mm_ws_kernel(M, N, K).decode()
     assert name(64, 8192, 14336) == "gemm_decode_kernel<64x64>+splitk_reduce_kernel"
     assert name(64, 4096, 4096) == lib.w8a8_scaled_mm_kernel(64, 4096, 4096).decode()
-    assert name(64, 4096, 14336) == "gemm_decode_kernel<16x64,1K>"
+    assert name(64, 4096, 14336) == "gemm_decode_kernel<64x64>+splitk_reduce_kernel"
+    assert lib.w8a8_scaled_mm_kernel(64, 4096, 14336).decode() == "gemm_decode_kernel<16x64,1K>"
     ws = lib.w8a8_scaled_mm_ws
     args = (FAKE, 0, 64, FAKE, 128, FAKE, 128, 1, 16, 64, 128, None, 1, None, 1)
     assert ws(*args, FAKE + 16, 1024, None) == ALIGN       # 256-byte aligned workspace

@@ -278,6 +278,7 @@ def test_decode_configs_are_the_ones_named():
 # long K on narrow weights (the Llama-3-8B down projection at 64 tokens,
 # ragged N and K, the widest N that still splits).
 SPLITK_SHAPES = [(64, 4608, 14336), (40, 1000, 8192 + 16), (17, 300, 16384), (64, 16320, 8192),
+                 (64, 10240, 8192), (64, 4096, 14336),
                  (33, 48, 9000 - 9000 % 16)]
 
 
