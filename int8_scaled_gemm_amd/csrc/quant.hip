@@ -109,9 +109,15 @@ __global__ __launch_bounds__(kBlock) void quant_rows_2pass_kernel(const void* __
 // ------------------------------------------------------------------------
 // Per-tensor passes over an [M, K] tensor with a row stride. Work is cut in
 // units of one row x 2048 elements (256 lanes x 8); each block takes kUnroll
-// units per step so that every lane keeps kUnroll 16-byte loads in flight.
+// units per step so that every lane keeps kUnroll 16-byte loads in flight
+// (2 rather than 4: twice the workgroups, measured 8192 x 4096 27.7 -> 24.0
+// us, 512 x 14336 7.5 -> 6.7 us on MI355X).
 // ------------------------------------------------------------------------
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 2;
+// The quantising pass of a dynamic per-tensor scale keeps 4 (fewer
+// workgroups, each reducing the partial maxima once: KV quant call 40.6 us
+// against 41.2 us with 2).
+constexpr int kUnrollDynamic = 4;
 constexpr int kUnitElems = kBlock * 8;
 
 struct Units {
@@ -199,7 +205,7 @@ __device__ float reduce_partials(uint8_t* q, int64_t ldq, int64_t K, const Tail&
 // Quantise with one scale for the whole tensor. DYNAMIC: the scale comes
 // from the partial maxima in the tail, and the tail is left to
 // finish_tail_kernel; otherwise *scale is the scale (NULL: 1.0).
-template <int XT, int QT, bool DYNAMIC>
+template <int XT, int QT, bool DYNAMIC, int U = DYNAMIC ? kUnrollDynamic : kUnroll>
 __global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const void* __restrict__ x,
                                                               int64_t ldx, uint8_t* q, int64_t ldq,
                                                               const float* __restrict__ scale,
@@ -208,18 +214,18 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const void* __rest
     if constexpr (DYNAMIC) s = scale_from_absmax<QT>(reduce_partials(q, ldq, K, tail));
     else s = scale ? *scale : 1.0f;
     const double r = 1.0 / static_cast<double>(s);
-    for (uint32_t base = blockIdx.x * kUnroll; base < u.total; base += gridDim.x * kUnroll) {
-        float v[kUnroll][8];
-        bool ok[kUnroll];
-        int64_t row[kUnroll], k[kUnroll];
+    for (uint32_t base = blockIdx.x * U; base < u.total; base += gridDim.x * U) {
+        float v[U][8];
+        bool ok[U];
+        int64_t row[U], k[U];
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
+        for (int j = 0; j < U; ++j) {
             ok[j] = unit_coords(u, base + j, K, row[j], k[j]);
             if (DYNAMIC && ok[j] && row[j] * K + k[j] >= tail.start) ok[j] = false;
             if (ok[j]) load8<XT>(x, row[j] * ldx + k[j], v[j]);
         }
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j)
+        for (int j = 0; j < U; ++j)
             if (ok[j]) *reinterpret_cast<u32x2*>(q + row[j] * ldq + k[j]) = quant8<QT>(v[j], r);
     }
 }
@@ -251,12 +257,14 @@ __global__ __launch_bounds__(kBlock) void finish_tail_kernel(const void* __restr
 // pieces 32 bytes apart, each instruction leaving every other piece to the
 // next); float32 output is two 16-byte stores per lane, cached.
 // ------------------------------------------------------------------------
+constexpr int kDequantUnroll = 8;
+
 template <int XT>
 __global__ __launch_bounds__(kBlock) void kv_dequant_kernel(const uint8_t* __restrict__ q,
                                                             int64_t n,
                                                             const float* __restrict__ scale,
                                                             void* __restrict__ x) {
-    constexpr int U = 2 * kUnroll;  // 8-byte loads in flight per lane
+    constexpr int U = kDequantUnroll;  // 8-byte loads in flight per lane
     const float s = scale ? *scale : 1.0f;
     const int64_t nvec = n / 8;
     for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * U + threadIdx.x;
@@ -320,12 +328,13 @@ Units make_units(int64_t M, int64_t K) {
 template <int XT, int QT>
 hipError_t per_token_typed(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                            int64_t ldq, float* scales, hipStream_t st) {
-    // Fit the row in registers when possible: one wave per row up to 8192
-    // elements, one 256-lane block per row up to 32768, else two passes.
-    // Few rows (decode batches): a whole block per row at every K, so that
-    // each lane's share of the row, and with it the serial load -> divide ->
-    // store chain that bounds these small launches, is four times shorter.
-    if (M <= 256 && K <= 32768) {
+    // The row in registers, a whole workgroup per row (256 lanes up to 8192
+    // elements, 1024 up to 32768), else two passes. Each lane's share of its
+    // row, and with it the serial load -> divide -> store chain, is short:
+    // measured on MI355X against one wave per row, 8192 x 4096 28.4 -> 24.0
+    // us, 4096 x 8192 34.8 -> 28.0 us, 4096 x 28672 117 -> 81 us, and 4.5-5.4
+    // -> 3.1-4.1 us for decode batches.
+    if (K <= 32768) {
         const int g = static_cast<int>(M);
         if (K <= 2048)
             hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 256, 1>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
@@ -337,22 +346,6 @@ hipError_t per_token_typed(const void* x, int64_t M, int64_t K, int64_t ldx, uin
             hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 1024, 2, 1024>), dim3(g), dim3(1024), 0, st, x, ldx, q, ldq, scales, M, K);
         else
             hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 1024, 4, 1024>), dim3(g), dim3(1024), 0, st, x, ldx, q, ldq, scales, M, K);
-    } else if (K <= 8192) {
-        const int g = static_cast<int>((M + 3) / 4);
-        if (K <= 1024)
-            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 64, 2>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
-        else if (K <= 2048)
-            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 64, 4>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
-        else if (K <= 4096)
-            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 64, 8>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
-        else
-            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 64, 16>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
-    } else if (K <= 32768) {
-        const int g = static_cast<int>(M);
-        if (K <= 16384)
-            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 256, 8>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
-        else
-            hipLaunchKernelGGL((quant_rows_kernel<XT, QT, 256, 16>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
     } else {
         hipLaunchKernelGGL((quant_rows_2pass_kernel<XT, QT>), dim3(static_cast<int>(M)), dim3(kBlock), 0, st, x, ldx, q, ldq, scales, M, K);
     }
@@ -379,7 +372,7 @@ hipError_t per_tensor_typed(const void* x, int64_t M, int64_t K, int64_t ldx, ui
         // at most 8 workgroups per CU: each reduces the partials once, then
         // strides over the units
         if (tail.start > 0)
-            hipLaunchKernelGGL((quant_tensor_kernel<XT, QT, true>), dim3(std::min(g, 2048)), dim3(kBlock), 0, st, x, ldx, q, ldq, static_cast<const float*>(scale), u, K, tail);
+            hipLaunchKernelGGL((quant_tensor_kernel<XT, QT, true>), dim3(std::min(grid_for(u.total, kUnrollDynamic), 2048)), dim3(kBlock), 0, st, x, ldx, q, ldq, static_cast<const float*>(scale), u, K, tail);
         hipLaunchKernelGGL((finish_tail_kernel<XT, QT>), dim3(1), dim3(kBlock), 0, st, x, ldx, q, ldq, scale, M, K, tail);
     } else {
         hipLaunchKernelGGL((quant_tensor_kernel<XT, QT, false>), dim3(g), dim3(kBlock), 0, st, x, ldx, q, ldq, static_cast<const float*>(scale), u, K, Tail{0, 0});
@@ -856,7 +849,7 @@ hipError_t launch_requant_shared_scale(const uint8_t* w, int64_t ldw, int qt, in
 hipError_t launch_kv_dequant(const uint8_t* q, int64_t n, const float* scale, void* x, int xt,
                              hipStream_t st) {
     if (n == 0) return hipSuccess;
-    const int g = grid_for(static_cast<uint64_t>(n / 16), static_cast<uint64_t>(kBlock) * kUnroll);
+    const int g = grid_for(static_cast<uint64_t>(n / 8), static_cast<uint64_t>(kBlock) * kDequantUnroll);
     switch (xt) {
         case D_BF16: hipLaunchKernelGGL((kv_dequant_kernel<D_BF16>), dim3(g), dim3(kBlock), 0, st, q, n, scale, x); break;
         case D_FP16: hipLaunchKernelGGL((kv_dequant_kernel<D_FP16>), dim3(g), dim3(kBlock), 0, st, q, n, scale, x); break;
