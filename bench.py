@@ -684,7 +684,7 @@ def measure(name, args, dev, stream, otype, detail=False):
         main_kind = {"kv": "kv_quant", "merge": "merge_requant", "attn": "attn"}.get(name, "gemm")
         dom = max((k for k in kernels if kinds[k] == main_kind),
                   key=lambda k: kernels[k]["avg_s"] * kernels[k]["launches"])
-        roof = roofline(dom, kernels[dom], spec, name)
+        roof = roofline(dom, kernels[dom], spec, name if otype == torch.bfloat16 else f"{name}_{OUT_NAMES[otype]}")
         # The clock the roofline kernel runs at: the matrix-core peak scales
         # with it (HBM bandwidth does not), so an MFMA-bound entry is also
         # given against the peak at the measured clock.
@@ -732,6 +732,7 @@ def kernel_table(kernels, spec):
 
 
 OUT_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+OUT_NAMES = {v: k for k, v in OUT_DTYPES.items()}
 
 
 def main():
