@@ -407,3 +407,40 @@ def decode_attention_fp8kv(q, k_codes, v_codes, seq_starts, k_scale=None, v_scal
             p /= p.sum()
             out[b, h] = p @ vf[t0:t1, g, :]
     return out
+
+
+def paged_rows(block_tables, seq_lens, block_size, num_blocks):
+    """Cache rows of each sequence in a paged layout: logical row t of
+    sequence b is physical row block_tables[b][t // block_size] * block_size
+    + t % block_size. Rows whose block entry lies outside 0 .. num_blocks-1
+    are absent (None)."""
+    rows = []
+    for b in range(len(seq_lens)):
+        rb = []
+        for t in range(int(seq_lens[b])):
+            blk = int(block_tables[b][t // block_size])
+            rb.append(blk * block_size + t % block_size if 0 <= blk < num_blocks else None)
+        rows.append(rb)
+    return rows
+
+
+def decode_attention_fp8kv_paged(q, k_codes, v_codes, block_tables, seq_lens, block_size,
+                                 k_scale=None, v_scale=None, sm_scale=None):
+    """decode_attention_fp8kv over a paged cache ("Enable scaled FP8 (e4m3fn)
+    KV cache on ROCm": the paged-attention kernel reads the fp8 cache through
+    its block table). The cache [num_blocks * block_size, Hkv, D] is cut into
+    blocks of block_size consecutive rows; sequence b's logical row t lives in
+    physical block block_tables[b][t // block_size]. Each sequence's rows are
+    gathered in logical order (absent rows dropped) and attended exactly as in
+    the contiguous layout."""
+    num_blocks = k_codes.shape[0] // block_size
+    rows = paged_rows(block_tables, seq_lens, block_size, num_blocks)
+    Hkv, D = k_codes.shape[1], k_codes.shape[2]
+    gathered = [[r for r in rb if r is not None] for rb in rows]
+    starts = np.zeros(len(rows) + 1, np.int64)
+    for b, rb in enumerate(gathered):
+        starts[b + 1] = starts[b] + len(rb)
+    idx = np.array([r for rb in gathered for r in rb], np.int64)
+    kc = k_codes[idx] if idx.size else np.zeros((0, Hkv, D), np.uint8)
+    vc = v_codes[idx] if idx.size else np.zeros((0, Hkv, D), np.uint8)
+    return decode_attention_fp8kv(q, kc, vc, starts, k_scale, v_scale, sm_scale)

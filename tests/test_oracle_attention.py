@@ -124,3 +124,94 @@ def test_order_of_rows_within_a_sequence_does_not_matter():
     a = oracle.decode_attention_fp8kv(q, k, v, [0, 30], 0.02, 0.1)
     b = oracle.decode_attention_fp8kv(q, k[perm], v[perm], [0, 30], 0.02, 0.1)
     np.testing.assert_allclose(a, b, rtol=1e-12)
+
+
+# ------------------------------------------------------------------ paged cache
+# The cache cut into blocks of block_size consecutive rows, each sequence's
+# logical rows found through its block table (the paged layout the
+# paged-attention kernel reads).
+
+def _paged_case(rng, bs=16, Hkv=2, D=128, lens=(37, 0, 16, 70), spare=5):
+    nblk = sum(-(-L // bs) for L in lens) + spare
+    k, v = _codes(rng, (nblk * bs, Hkv, D)), _codes(rng, (nblk * bs, Hkv, D))
+    perm = rng.permutation(nblk)
+    maxb = max(-(-L // bs) for L in lens)
+    tables = np.full((len(lens), maxb + 1), -1, np.int64)
+    used = 0
+    for b, L in enumerate(lens):
+        for j in range(-(-L // bs)):
+            tables[b, j] = perm[used]
+            used += 1
+    return k, v, tables, np.array(lens), bs
+
+
+def test_paged_matches_torch_sdpa_on_gathered_rows():
+    rng = np.random.default_rng(11)
+    k, v, tables, lens, bs = _paged_case(rng)
+    B, Hq, Hkv, D = len(lens), 4, 2, 128
+    qb, qt = _bf16(rng, (B, Hq, D))
+    got = oracle.decode_attention_fp8kv_paged(qb, k, v, tables, lens, bs, 0.02, 0.03, 0.09)
+    kd = _torch_dec(k) * float(np.float32(0.02))
+    vd = _torch_dec(v) * float(np.float32(0.03))
+    for b in range(B):
+        if lens[b] == 0:
+            assert (got[b] == 0).all()
+            continue
+        idx = torch.tensor([tables[b][t // bs] * bs + t % bs for t in range(lens[b])])
+        kk = kd[idx].permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+        vv = vd[idx].permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt[b][:, None, :], kk, vv, scale=float(np.float32(0.09)))[:, 0, :].numpy()
+        np.testing.assert_allclose(got[b], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_paged_in_order_blocks_equal_the_contiguous_layout():
+    """Tables that list consecutive blocks for sequences starting on block
+    boundaries give exactly the contiguous result over the same rows."""
+    rng = np.random.default_rng(12)
+    bs, lens = 8, [20, 8, 31]
+    starts = [0, 24, 32, 64]   # each sequence starts on a block boundary
+    k, v = _codes(rng, (64, 2, 128)), _codes(rng, (64, 2, 128))
+    tables = np.array([[0, 1, 2, -1], [3, -1, -1, -1], [4, 5, 6, 7]])
+    q = rng.standard_normal((3, 4, 128))
+    paged = oracle.decode_attention_fp8kv_paged(q, k, v, tables, lens, bs, 0.5, 0.25)
+    kc = np.concatenate([k[starts[b]:starts[b] + lens[b]] for b in range(3)])
+    vc = np.concatenate([v[starts[b]:starts[b] + lens[b]] for b in range(3)])
+    cont = oracle.decode_attention_fp8kv(q, kc, vc, np.cumsum([0] + lens), 0.5, 0.25)
+    np.testing.assert_array_equal(paged, cont)
+
+
+def test_paged_block_placement_does_not_matter():
+    """Moving the physical blocks (and the tables with them) leaves every
+    output unchanged; a block shared by two sequences is read by both."""
+    rng = np.random.default_rng(13)
+    k, v, tables, lens, bs = _paged_case(rng, lens=(40, 33, 16))
+    tables[2, 0] = tables[0, 0]          # the third sequence shares the first's first block
+    q = rng.standard_normal((3, 2, 128))
+    a = oracle.decode_attention_fp8kv_paged(q, k, v, tables, lens, bs)
+    nblk = k.shape[0] // bs
+    move = rng.permutation(nblk)         # physical block i goes to slot move[i]
+    k2 = np.empty_like(k); v2 = np.empty_like(v)
+    for i in range(nblk):
+        k2[move[i] * bs:(move[i] + 1) * bs] = k[i * bs:(i + 1) * bs]
+        v2[move[i] * bs:(move[i] + 1) * bs] = v[i * bs:(i + 1) * bs]
+    t2 = np.where(tables >= 0, move[np.clip(tables, 0, None)], -1)
+    b = oracle.decode_attention_fp8kv_paged(q, k2, v2, t2, lens, bs)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(a[2], oracle.decode_attention_fp8kv(
+        q[2:3], k[tables[0, 0] * bs:tables[0, 0] * bs + 16], v[tables[0, 0] * bs:tables[0, 0] * bs + 16],
+        [0, 16])[0])
+
+
+def test_paged_blocks_outside_the_cache_are_absent():
+    rng = np.random.default_rng(14)
+    k, v, tables, lens, bs = _paged_case(rng, lens=(48,))
+    q = rng.standard_normal((1, 2, 128))
+    nblk = k.shape[0] // bs
+    t_bad = tables.copy()
+    t_bad[0, 1] = nblk + 3               # the middle block points past the cache
+    got = oracle.decode_attention_fp8kv_paged(q, k, v, t_bad, lens, bs)
+    keep = [tables[0, 0], tables[0, 2]]  # the other two blocks, in order
+    kc = np.concatenate([k[i * bs:(i + 1) * bs] for i in keep])
+    vc = np.concatenate([v[i * bs:(i + 1) * bs] for i in keep])
+    np.testing.assert_array_equal(got, oracle.decode_attention_fp8kv(q, kc, vc, [0, 32]))
