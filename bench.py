@@ -270,7 +270,38 @@ def _attn_call(q, kc, vc, starts, max_len, ks, vs, out, ws):
     return w8.kv_fp8_decode_attention(q, kc, vc, starts, max_len, ks, vs, out=out, workspace=ws)
 
 
-def build_attn_workload(dev, layers=workloads.KV_LAYERS):
+def _paged_attn_call(q, kc, vc, tables, lens, max_len, ks, vs, out, ws):
+    return w8.kv_fp8_paged_decode_attention(q, kc, vc, tables, lens, max_len, ks, vs, out=out,
+                                            workspace=ws)
+
+
+PAGE_ROWS = 16  # rows per cache block of the paged layout
+
+
+def paged_layout(starts, block_size=PAGE_ROWS, seed=7):
+    """Block tables of the attention workload's sequences in a paged cache:
+    each sequence's rows cut into blocks of block_size rows (the last one
+    padded), the blocks placed in a seeded shuffled order. Returns the
+    tables [B, max blocks] (-1 past each sequence), the lengths, the block
+    count, and for every physical block the contiguous row its rows start at
+    (-1 for none)."""
+    lens = (starts[1:] - starts[:-1]).to(torch.int32)
+    nb = [-(-int(L) // block_size) for L in lens]
+    nblk = sum(nb)
+    perm = torch.randperm(nblk, generator=torch.Generator().manual_seed(seed))
+    tables = torch.full((len(nb), max(nb)), -1, dtype=torch.int32)
+    src = torch.full((nblk,), -1, dtype=torch.int64)
+    used = 0
+    for b, n in enumerate(nb):
+        for j in range(n):
+            blk = int(perm[used])
+            used += 1
+            tables[b, j] = blk
+            src[blk] = int(starts[b]) + j * block_size
+    return tables, lens, nblk, src
+
+
+def build_attn_workload(dev, layers=workloads.KV_LAYERS, paged=False):
     """Decode attention of one query token per sequence over each layer's
     fp8 KV cache: the layer's K and V [32768, 8, 128] quantised offline
     (kv_fp8_scaled_quant, not timed), 16 sequences of uneven length, 32
@@ -278,6 +309,21 @@ def build_attn_workload(dev, layers=workloads.KV_LAYERS):
     launches, keep = [], []
     hq, hkv, d = workloads.ATTN_HEADS
     starts = workloads.attention_seq_starts()
+    if paged:
+        tables, lens, nblk, src = paged_layout(starts)
+        tables_d, lens_d = tables.to(dev), lens.to(dev)
+        # physical row r of the paged cache holds contiguous row gather[r] (or zeros)
+        offs = torch.arange(PAGE_ROWS).repeat(nblk)
+        base = src.repeat_interleave(PAGE_ROWS)
+        gather = torch.where(base >= 0, base + offs, torch.full_like(base, -1))
+        seq_end = torch.zeros_like(gather)
+        for b in range(len(lens)):
+            for j in range(tables.shape[1]):
+                blk = int(tables[b, j])
+                if blk >= 0:
+                    seq_end[blk * PAGE_ROWS:(blk + 1) * PAGE_ROWS] = int(starts[b + 1])
+        gather = torch.where((gather >= 0) & (gather < seq_end), gather, torch.full_like(gather, -1)).to(dev)
+        keep += [tables_d, lens_d, gather]
     B = starts.numel() - 1
     max_len = int((starts[1:] - starts[:-1]).max())
     rows = workloads.KV_SHAPE[0]
@@ -291,13 +337,26 @@ def build_attn_workload(dev, layers=workloads.KV_LAYERS):
             x = workloads.kv_tensor(layer, which, device=dev)
             q8, sc = w8.kv_fp8_scaled_quant(x)
             del x
+            if paged:  # the same rows, blocks of 16 in shuffled places (padding rows zero)
+                flat = q8.view(torch.uint8).reshape(q8.shape[0], -1)
+                pg = torch.zeros((gather.numel(), flat.shape[1]), dtype=torch.uint8, device=dev)
+                ok = gather >= 0
+                pg[ok] = flat[gather[ok]]
+                q8 = pg.reshape(nblk, PAGE_ROWS, hkv, d)
+                del flat
             cache += [q8.view(torch.uint8), sc]
         kc, ks, vc, vs = cache
         q = workloads.attention_queries(B, hq, d, seed=200 + layer, device=dev)
         out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
         nbytes = 2 * rows * hkv * d + 2 * 2 * B * hq * d + 4 * (B + 1) + 8
-        launches.append(Launch("attn", _attn_call, (q, kc, vc, starts_d, max_len, ks, vs, out, ws),
-                               4 * rows * hq * d, nbytes, f"attention L{layer}", ATTN_KERNELS))
+        if paged:
+            nbytes += 4 * tables.numel()
+            launches.append(Launch("attn", _paged_attn_call,
+                                   (q, kc, vc, tables_d, lens_d, max_len, ks, vs, out, ws),
+                                   4 * rows * hq * d, nbytes, f"paged attention L{layer}", ATTN_KERNELS))
+        else:
+            launches.append(Launch("attn", _attn_call, (q, kc, vc, starts_d, max_len, ks, vs, out, ws),
+                                   4 * rows * hq * d, nbytes, f"attention L{layer}", ATTN_KERNELS))
         keep += [kc, ks, vc, vs, q, out]
     return launches, keep
 
@@ -331,6 +390,9 @@ WORKLOADS = {
                       "token for 16 sequences of uneven length (32768 cache rows), 32 query heads "
                       "over 8 KV heads, head dim 128, K and V dequantised with their per-tensor "
                       "scales as they are read, bf16 out"),
+    "attn_paged": dict(desc="decode attention over the scaled fp8 KV cache in a paged layout: the attn "
+                            "workload's 32 layers with each sequence's rows in blocks of 16 placed in a "
+                            "shuffled order and found through per-sequence block tables"),
     "merge": dict(desc="merged-layer weight scales: per-shard scales of the merged QKV and "
                        "gate_up weights (Llama-3-8B fp8, Llama-3-70B int8) expanded to "
                        "per-channel scales, and the codes rescaled to one shared scale"),
@@ -529,10 +591,15 @@ def cpu_baseline(spec, launches_meta, budget_s: float):
                 "kind": "oracle",
                 "sample": f"expansion + requantisation of {done} of the step's "
                           f"{len(workloads.MERGED_LAYERS)} merged weights ({dt:.1f} s)"}
-    if spec is WORKLOADS["attn"]:   # the oracle's attention over whole layers
+    if spec is WORKLOADS["attn"] or spec is WORKLOADS["attn_paged"]:   # attention over whole layers
+        paged = spec is WORKLOADS["attn_paged"]
         hq, hkv, d = workloads.ATTN_HEADS
-        starts = workloads.attention_seq_starts().numpy()
+        st = workloads.attention_seq_starts()
+        starts = st.numpy()
         B = starts.size - 1
+        if paged:
+            tables, lens, nblk, src = paged_layout(st)
+            tables, lens = tables.numpy(), lens.numpy()
         dt, nbytes, done = 0.0, 0, 0
         for layer in range(4):   # drawing and quantising a layer's cache costs more than its attention
             codes = []
@@ -541,8 +608,21 @@ def cpu_baseline(spec, launches_meta, budget_s: float):
                 c, sc = oracle.kv_quant(xh, xtype="bf16")
                 codes += [c.reshape(workloads.KV_SHAPE), sc]
             qh = workloads.as_u16(workloads.attention_queries(B, hq, d, seed=200 + layer))
+            if paged:   # the same rows in the paged placement (not timed)
+                pk = np.zeros((nblk * PAGE_ROWS, hkv, d), np.uint8)
+                pv = np.zeros((nblk * PAGE_ROWS, hkv, d), np.uint8)
+                for b in range(B):
+                    for j in range(-(-int(lens[b]) // PAGE_ROWS)):
+                        r0 = int(starts[b]) + j * PAGE_ROWS
+                        n = min(PAGE_ROWS, int(starts[b + 1]) - r0)
+                        blk = int(tables[b, j])
+                        pk[blk * PAGE_ROWS:blk * PAGE_ROWS + n] = codes[0][r0:r0 + n]
+                        pv[blk * PAGE_ROWS:blk * PAGE_ROWS + n] = codes[2][r0:r0 + n]
             t0 = time.perf_counter()
-            oracle.decode_attention_fp8kv(qh, codes[0], codes[2], starts, codes[1], codes[3])
+            if paged:
+                oracle.decode_attention_fp8kv_paged(qh, pk, pv, tables, lens, PAGE_ROWS, codes[1], codes[3])
+            else:
+                oracle.decode_attention_fp8kv(qh, codes[0], codes[2], starts, codes[1], codes[3])
             dt += time.perf_counter() - t0
             nbytes += 2 * codes[0].size + 4 * B * hq * d
             done += 1
@@ -620,6 +700,8 @@ def build(name, spec, dev, otype):
         return build_kv_workload(dev)
     if name == "attn":
         return build_attn_workload(dev)
+    if name == "attn_paged":
+        return build_attn_workload(dev, paged=True)
     if name == "merge":
         return build_merge_workload(dev)
     return build_gemm_workload(spec["layers"], spec["Ms"], spec["qtype"], spec["act"], dev, otype)
@@ -681,7 +763,8 @@ def measure(name, args, dev, stream, otype, detail=False):
         # batches are latency-bound (a few KB each) and are listed with their
         # latency only.
         kinds = {L.kernel: L.kind for L in launches}
-        main_kind = {"kv": "kv_quant", "merge": "merge_requant", "attn": "attn"}.get(name, "gemm")
+        main_kind = {"kv": "kv_quant", "merge": "merge_requant", "attn": "attn",
+                     "attn_paged": "attn"}.get(name, "gemm")
         dom = max((k for k in kernels if kinds[k] == main_kind),
                   key=lambda k: kernels[k]["avg_s"] * kernels[k]["launches"])
         roof = roofline(dom, kernels[dom], spec, name if otype == torch.bfloat16 else f"{name}_{OUT_NAMES[otype]}")
@@ -786,7 +869,7 @@ def main():
         value = r["nbytes"] / (step_ms / 1e3) / 1e9
         metric, unit = "scaled fp8 KV cache quant+dequant GB/s (algorithmic bytes)", "GB/s"
         dtype = "fp8e4m3"
-    elif args.workload == "attn":
+    elif args.workload in ("attn", "attn_paged"):
         value = r["nbytes"] / (step_ms / 1e3) / 1e9
         metric, unit = "fp8 KV cache decode attention GB/s (algorithmic bytes)", "GB/s"
         dtype = "fp8e4m3 cache, f32 arithmetic"
@@ -807,10 +890,10 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic (seeded; Llama-3 layer shapes, bf16 N(0,1) activations with 1% "
-                "outlier channels x20, N(0,0.02) weights)" if args.workload not in ("kv", "merge", "attn") else
+                "outlier channels x20, N(0,0.02) weights)" if args.workload not in ("kv", "merge", "attn", "attn_paged") else
                 "synthetic (seeded; N(0,1) K/V with 0.1% outliers x10)" if args.workload == "kv" else
                 "synthetic (seeded; N(0,1) K/V with 0.1% outliers x10 quantised to e4m3fn, "
-                "N(0,1) bf16 queries, sequence lengths from seeded weights)" if args.workload == "attn" else
+                "N(0,1) bf16 queries, sequence lengths from seeded weights)" if args.workload in ("attn", "attn_paged") else
                 "synthetic (seeded; uniformly random valid codes, shard scales U(2e-4, 4e-3))",
         "config": {"workload": desc, "mode": "hip-graph replay, inputs resident in HBM",
                    "step_bytes": r["nbytes"], "step_flops": r["flops"],

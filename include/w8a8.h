@@ -345,6 +345,33 @@ w8a8_status kv_fp8_decode_attention(void* out, const void* q, int64_t B, int64_t
                                     void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Decode attention over a paged e4m3fn KV cache [P3: the paged-attention
+ * kernel reads the fp8 cache through its block table and dequantises it
+ * with the KV scale]. The same operation and arguments as
+ * kv_fp8_decode_attention, with the cache cut into blocks of block_size
+ * consecutive rows and each sequence's rows found through its block table:
+ *   k_cache, v_cache: device e4m3fn codes [num_blocks * block_size, Hkv, D].
+ *   block_tables: device int32 [B, table_stride]; logical row t of sequence b
+ *     is cache row block_tables[b * table_stride + t / block_size] *
+ *     block_size + t % block_size. Entries outside 0 .. num_blocks-1 make
+ *     their rows absent (never read, no weight).
+ *   seq_lens: device int32 [B], rows per sequence (at most max_seq_len; rows
+ *     past it are not read). table_stride * block_size >= max_seq_len, so a
+ *     sequence's rows never index past its table row.
+ *   block_size: a power of two, 1 .. 1024 (else W8A8_ERR_UNSUPPORTED).
+ * Blocks may be shared between sequences (a common prefix). The workspace
+ * is kv_fp8_attention_workspace_size(B, Hq, Hkv, max_seq_len) bytes.
+ */
+w8a8_status kv_fp8_paged_decode_attention(void* out, const void* q, int64_t B, int64_t Hq,
+                                          int64_t Hkv, int64_t D, const uint8_t* k_cache,
+                                          const uint8_t* v_cache, int64_t num_blocks,
+                                          int64_t block_size, const int32_t* block_tables,
+                                          int64_t table_stride, const int32_t* seq_lens,
+                                          int64_t max_seq_len, const float* k_scale,
+                                          const float* v_scale, float sm_scale, void* workspace,
+                                          int64_t workspace_bytes, hipStream_t stream);
+
+/*
  * Name of the kernel configuration w8a8_scaled_mm runs for an M x N x K
  * problem, such as "gemm_decode_kernel<16x16>" or
  * "gemm_tile_kernel<256x256>" (a static string; "" for negative sizes), so

@@ -72,6 +72,8 @@ SIGNATURES = {
     "w8a8_requant_shared_scale": [_P, _I64, _I, _I64, _P, _I64, _P, _P, _I64, _P, _P],
     "kv_fp8_decode_attention": [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _P,
                                 ctypes.c_float, _P, _I64, _P],
+    "kv_fp8_paged_decode_attention": [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _I64, _I64, _P, _I64,
+                                      _P, _I64, _P, _P, ctypes.c_float, _P, _I64, _P],
 }
 
 
@@ -318,6 +320,57 @@ def kv_fp8_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
           _ptr(v_cache), rows, _ptr(seq_starts), max_seq_len, _ptr(k_scale), _ptr(v_scale),
           float(sm_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
           _stream(q))
+    return out
+
+
+def kv_fp8_paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                  block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                                  max_seq_len: int, k_scale: torch.Tensor | None = None,
+                                  v_scale: torch.Tensor | None = None, sm_scale: float = 0.0,
+                                  out: torch.Tensor | None = None,
+                                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention over a paged e4m3fn KV cache: q [B, Hq, D] bf16,
+    caches [num_blocks, block_size, Hkv, D] e4m3fn, block_tables [B, n] int32
+    (logical row t of sequence b lives in block block_tables[b, t // block_size]),
+    seq_lens [B] int32 -> out [B, Hq, D] bf16."""
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"kv_fp8_paged_decode_attention: {name} must be a contiguous "
+                             f"[num_blocks, block_size, Hkv, D] tensor")
+    if q.dim() != 3 or not q.is_contiguous() or q.dtype != torch.bfloat16:
+        raise ValueError("kv_fp8_paged_decode_attention: q must be a contiguous bfloat16 [B, Hq, D] tensor")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("kv_fp8_paged_decode_attention: k_cache and v_cache shapes differ")
+    B, Hq, D = q.shape
+    nblk, bs, Hkv, Dk = k_cache.shape
+    if Dk != D:
+        raise ValueError("kv_fp8_paged_decode_attention: head dimension mismatch")
+    if block_tables.dim() != 2 or block_tables.size(0) != B or block_tables.dtype != torch.int32:
+        raise ValueError("block_tables must be an int32 [B, n] tensor")
+    if block_tables.size(1) > 1 and block_tables.stride(1) != 1:
+        raise ValueError("block_tables must have unit stride along its last dimension")
+    _want(k_cache, "k_cache", dtypes=(torch.float8_e4m3fn, torch.uint8))
+    _want(v_cache, "v_cache", dtypes=(torch.float8_e4m3fn, torch.uint8))
+    _want(seq_lens, "seq_lens", numel=B, dtypes=_I32, contiguous=True)
+    _want(k_scale, "k_scale", numel=1, dtypes=_F32)
+    _want(v_scale, "v_scale", numel=1, dtypes=_F32)
+    _want(out, "out", shape=(B, Hq, D), dtypes=(torch.bfloat16,), contiguous=True)
+    _want(workspace, "workspace", contiguous=True)
+    _check_cuda(q, k_cache, v_cache, block_tables, seq_lens, k_scale, v_scale, out, workspace)
+    _same_device(q, k_cache, v_cache, block_tables, seq_lens, k_scale, v_scale, out, workspace)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    need = kv_fp8_attention_workspace_size(B, Hq, Hkv, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                         f"the call needs {need}")
+    stride = block_tables.stride(0) if B > 1 else block_tables.size(1)
+    _call("kv_fp8_paged_decode_attention", _ptr(out), _ptr(q), B, Hq, Hkv, D, _ptr(k_cache),
+          _ptr(v_cache), nblk, bs, _ptr(block_tables), stride, _ptr(seq_lens), max_seq_len,
+          _ptr(k_scale), _ptr(v_scale), float(sm_scale), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(q))
     return out
 
 
@@ -648,6 +701,7 @@ __all__ = ["w8a8_quant_per_token", "w8a8_quant_per_tensor", "w8a8_scaled_mm",
            "w8a8_expand_shard_scales", "w8a8_requant_shared_scale",
            "w8a8_quant_per_token_azp", "w8a8_quant_per_tensor_azp", "w8a8_colsum",
            "w8a8_scaled_mm_azp",
-           "kv_fp8_decode_attention", "kv_fp8_attention_workspace_size",
+           "kv_fp8_decode_attention", "kv_fp8_paged_decode_attention",
+           "kv_fp8_attention_workspace_size",
            "quant_per_token", "quant_per_tensor", "kv_quant", "kv_dequant",
            "load_library", "version", "LIB_PATH", "SIGNATURES"]

@@ -445,12 +445,15 @@ int64_t kv_fp8_attention_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int6
     return B * Hq * splits * (128 + 2) * 4;
 }
 
-w8a8_status kv_fp8_decode_attention(void* out, const void* q, int64_t B, int64_t Hq, int64_t Hkv,
-                                    int64_t D, const uint8_t* k_cache, const uint8_t* v_cache,
-                                    int64_t rows, const int32_t* seq_starts, int64_t max_seq_len,
-                                    const float* k_scale, const float* v_scale, float sm_scale,
-                                    void* workspace, int64_t workspace_bytes, hipStream_t stream) {
-    const char* fn = "kv_fp8_decode_attention";
+namespace {
+
+// The checks and arguments shared by the contiguous and the paged attention
+// calls (everything but the row layout).
+w8a8_status attention_common(const char* fn, void* out, const void* q, int64_t B, int64_t Hq,
+                             int64_t Hkv, int64_t D, const uint8_t* k_cache,
+                             const uint8_t* v_cache, int64_t rows, int64_t max_seq_len,
+                             const float* k_scale, const float* v_scale, float sm_scale,
+                             void* workspace, int64_t workspace_bytes, w8a8::AttnArgs& a) {
     if (B < 0 || Hq < 0 || Hkv < 0 || D < 0 || rows < 0 || max_seq_len < 0)
         return fail(W8A8_ERR_SHAPE, "%s: negative size", fn);
     if (B == 0 || Hq == 0) return ok();
@@ -461,23 +464,21 @@ w8a8_status kv_fp8_decode_attention(void* out, const void* q, int64_t B, int64_t
         return fail(W8A8_ERR_UNSUPPORTED, "%s: %lld query heads per KV head (1, 2, 4 or 8)", fn, (long long)G);
     if (B > 65535 || Hkv > 65535 || Hq > 65535 || max_seq_len > kMaxDim || rows > kMaxDim)
         return fail(W8A8_ERR_UNSUPPORTED, "%s: sizes beyond the launch limits", fn);
-    if (!out || !q || !seq_starts || !workspace) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL out, q, seq_starts or workspace", fn);
+    if (!out || !q || !workspace) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL out, q or workspace", fn);
     if (rows > 0 && (!k_cache || !v_cache)) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL cache", fn);
     if (!aligned16(out) || !aligned16(q) || (k_cache && !aligned16(k_cache)) || (v_cache && !aligned16(v_cache)) ||
         !aligned16(workspace))
         return fail(W8A8_ERR_ALIGNMENT, "%s: out, q, caches and workspace must be 16-byte aligned", fn);
-    if ((reinterpret_cast<uintptr_t>(seq_starts) | reinterpret_cast<uintptr_t>(k_scale) |
-         reinterpret_cast<uintptr_t>(v_scale)) & 3u)
-        return fail(W8A8_ERR_ALIGNMENT, "%s: seq_starts and scales must be 4-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3u)
+        return fail(W8A8_ERR_ALIGNMENT, "%s: scales must be 4-byte aligned", fn);
     if (workspace_bytes < kv_fp8_attention_workspace_size(B, Hq, Hkv, max_seq_len))
         return fail(W8A8_ERR_INVALID_ARG, "%s: workspace of %lld bytes, %lld needed", fn, (long long)workspace_bytes,
                     (long long)kv_fp8_attention_workspace_size(B, Hq, Hkv, max_seq_len));
-    w8a8::AttnArgs a;
     a.out = static_cast<uint16_t*>(out);
     a.q = static_cast<const uint16_t*>(q);
     a.k = k_cache;
     a.v = v_cache;
-    a.starts = seq_starts;
+    a.starts = nullptr;
     a.k_scale = k_scale;
     a.v_scale = v_scale;
     a.sm_scale = sm_scale != 0.0f ? sm_scale : 0.08838834764831845f;  // 1/sqrt(128)
@@ -488,6 +489,56 @@ w8a8_status kv_fp8_decode_attention(void* out, const void* q, int64_t B, int64_t
     a.splits = w8a8::attention_splits(B, Hkv, max_seq_len);
     a.chunk = w8a8::attention_chunk(max_seq_len, a.splits);
     a.part = static_cast<float*>(workspace);
+    return W8A8_OK;
+}
+
+}  // namespace
+
+w8a8_status kv_fp8_decode_attention(void* out, const void* q, int64_t B, int64_t Hq, int64_t Hkv,
+                                    int64_t D, const uint8_t* k_cache, const uint8_t* v_cache,
+                                    int64_t rows, const int32_t* seq_starts, int64_t max_seq_len,
+                                    const float* k_scale, const float* v_scale, float sm_scale,
+                                    void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    const char* fn = "kv_fp8_decode_attention";
+    w8a8::AttnArgs a;
+    const w8a8_status s = attention_common(fn, out, q, B, Hq, Hkv, D, k_cache, v_cache, rows, max_seq_len,
+                                           k_scale, v_scale, sm_scale, workspace, workspace_bytes, a);
+    if (s != W8A8_OK || B == 0 || Hq == 0) return s;
+    if (!seq_starts) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL seq_starts", fn);
+    if (reinterpret_cast<uintptr_t>(seq_starts) & 3u) return fail(W8A8_ERR_ALIGNMENT, "%s: seq_starts must be 4-byte aligned", fn);
+    a.starts = seq_starts;
+    return from_hip(w8a8::launch_attention(a, stream), fn);
+}
+
+w8a8_status kv_fp8_paged_decode_attention(void* out, const void* q, int64_t B, int64_t Hq,
+                                          int64_t Hkv, int64_t D, const uint8_t* k_cache,
+                                          const uint8_t* v_cache, int64_t num_blocks,
+                                          int64_t block_size, const int32_t* block_tables,
+                                          int64_t table_stride, const int32_t* seq_lens,
+                                          int64_t max_seq_len, const float* k_scale,
+                                          const float* v_scale, float sm_scale, void* workspace,
+                                          int64_t workspace_bytes, hipStream_t stream) {
+    const char* fn = "kv_fp8_paged_decode_attention";
+    if (num_blocks < 0 || table_stride < 0) return fail(W8A8_ERR_SHAPE, "%s: negative size", fn);
+    if (block_size < 1 || block_size > 1024 || (block_size & (block_size - 1)))
+        return fail(W8A8_ERR_UNSUPPORTED, "%s: block size %lld (a power of two, 1 .. 1024)", fn, (long long)block_size);
+    if (num_blocks > kMaxDim / block_size) return fail(W8A8_ERR_UNSUPPORTED, "%s: cache beyond the launch limits", fn);
+    w8a8::AttnArgs a;
+    const w8a8_status s = attention_common(fn, out, q, B, Hq, Hkv, D, k_cache, v_cache, num_blocks * block_size,
+                                           max_seq_len, k_scale, v_scale, sm_scale, workspace, workspace_bytes, a);
+    if (s != W8A8_OK || B == 0 || Hq == 0) return s;
+    if (!block_tables || !seq_lens) return fail(W8A8_ERR_INVALID_ARG, "%s: NULL block_tables or seq_lens", fn);
+    if ((reinterpret_cast<uintptr_t>(block_tables) | reinterpret_cast<uintptr_t>(seq_lens)) & 3u)
+        return fail(W8A8_ERR_ALIGNMENT, "%s: block_tables and seq_lens must be 4-byte aligned", fn);
+    if (table_stride * block_size < max_seq_len)
+        return fail(W8A8_ERR_SHAPE, "%s: %lld table entries of %lld rows cannot cover max_seq_len %lld", fn,
+                    (long long)table_stride, (long long)block_size, (long long)max_seq_len);
+    if (table_stride > kMaxDim / B) return fail(W8A8_ERR_UNSUPPORTED, "%s: block table beyond the launch limits", fn);
+    a.tables = block_tables;
+    a.lens = seq_lens;
+    a.table_stride = table_stride;
+    a.bshift = __builtin_ctzll(static_cast<unsigned long long>(block_size));
+    a.nblocks = num_blocks;
     return from_hip(w8a8::launch_attention(a, stream), fn);
 }
 

@@ -47,7 +47,7 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-template <int G>
+template <int G, bool PAGED>
 __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
     constexpr int NT = G * 64;
     constexpr int PER = kChunks / NT;  // pieces per thread per block
@@ -61,8 +61,23 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = g * G + w;
-    const int first = p.starts[b];
-    const int len = max(p.starts[b + 1] - first, 0);
+    const int first = PAGED ? 0 : p.starts[b];
+    const int len = max(PAGED ? p.lens[b] : p.starts[b + 1] - first, 0);
+    // Cache row of the sequence's logical row t (t < len), or -1 when it is
+    // absent: outside the cache, or (paged) a block entry outside the cache
+    // or past the table's row.
+    auto cache_row = [&](int t) -> int64_t {
+        if constexpr (PAGED) {
+            const int64_t j = t >> p.bshift;
+            if (j >= p.table_stride) return -1;
+            const int blk = p.tables[static_cast<int64_t>(b) * p.table_stride + j];
+            if (blk < 0 || blk >= p.nblocks) return -1;
+            return (static_cast<int64_t>(blk) << p.bshift) + (t & ((1 << p.bshift) - 1));
+        } else {
+            const int64_t row = static_cast<int64_t>(first) + t;
+            return row >= 0 && row < p.rows ? row : -1;
+        }
+    };
     const int r0 = s * p.chunk, r1 = min(len, r0 + p.chunk);
     float* dst = p.part + ((static_cast<int64_t>(b) * p.Hq + h) * p.splits + s) * (kD + 2);
     if (r0 >= r1) {  // past the end of the sequence: no weight
@@ -93,9 +108,9 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
             const int i = threadIdx.x + NT * j;
             const int half = i / (kChunks / 2), k = i % (kChunks / 2);
             const int t = base + k / 8;
-            const int64_t row = static_cast<int64_t>(first) + t;
+            const int64_t row = t < r1 ? cache_row(t) : -1;
             v[j] = u32x4{0, 0, 0, 0};
-            if (t < r1 && row >= 0 && row < p.rows)
+            if (row >= 0)
                 v[j] = *reinterpret_cast<const u32x4*>((half ? p.v : p.k) + row * rstride +
                                                        static_cast<int64_t>(g) * kD + 16 * (k % 8));
         }
@@ -156,8 +171,7 @@ __global__ __launch_bounds__(G * 64) void attn_split_kernel(AttnArgs p) {
         }
         __syncthreads();
         const float sc = ss[w][lane] * qscale;  // score of row base + lane for head h
-        const int64_t row = static_cast<int64_t>(first) + base + lane;
-        const bool valid = base + lane < r1 && row >= 0 && row < p.rows;  // absent rows: no weight
+        const bool valid = base + lane < r1 && cache_row(base + lane) >= 0;  // absent rows: no weight
         const float mn = fmaxf(m, wave_max(valid ? sc : -INFINITY));
         // A block with no row inside the cache leaves mn = m = -inf: nothing
         // to add (and -inf - -inf must not reach the exponential).
@@ -252,12 +266,19 @@ int attention_chunk(int64_t max_rows, int splits) {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
     const dim3 grid(a.splits, a.Hkv, a.B);
-    switch (a.Hq / a.Hkv) {
-        case 1: hipLaunchKernelGGL((attn_split_kernel<1>), grid, dim3(64), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((attn_split_kernel<2>), grid, dim3(128), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((attn_split_kernel<4>), grid, dim3(256), 0, st, a); break;
-        default: hipLaunchKernelGGL((attn_split_kernel<8>), grid, dim3(512), 0, st, a); break;
+#define W8A8_ATTN(PG)                                                                                 \
+    switch (a.Hq / a.Hkv) {                                                                           \
+        case 1: hipLaunchKernelGGL((attn_split_kernel<1, PG>), grid, dim3(64), 0, st, a); break;     \
+        case 2: hipLaunchKernelGGL((attn_split_kernel<2, PG>), grid, dim3(128), 0, st, a); break;    \
+        case 4: hipLaunchKernelGGL((attn_split_kernel<4, PG>), grid, dim3(256), 0, st, a); break;    \
+        default: hipLaunchKernelGGL((attn_split_kernel<8, PG>), grid, dim3(512), 0, st, a); break;   \
     }
+    if (a.tables) {
+        W8A8_ATTN(true)
+    } else {
+        W8A8_ATTN(false)
+    }
+#undef W8A8_ATTN
     hipLaunchKernelGGL(attn_combine_kernel, dim3(a.Hq, a.B), dim3(kD), 0, st, a);
     return hipGetLastError();
 }

@@ -106,6 +106,15 @@ struct AttnArgs {
     int64_t rows;            // cache rows (reads past them are skipped)
     int splits, chunk;       // row splits per sequence, rows per split (multiple of 64)
     float* part;             // [B, Hq, splits, 130] partial sums, maxima and weights
+    // Paged layout (tables != NULL): sequence b has lens[b] rows; its logical
+    // row t is cache row tables[b * table_stride + t / 2^bshift] * 2^bshift +
+    // t % 2^bshift (blocks of 2^bshift rows); entries outside 0 .. nblocks-1
+    // and rows past table_stride blocks are absent. starts is unused.
+    const int32_t* tables = nullptr;
+    const int32_t* lens = nullptr;
+    int64_t table_stride = 0;
+    int bshift = 0;
+    int64_t nblocks = 0;
 };
 int attention_splits(int64_t B, int64_t Hkv, int64_t max_rows);
 int attention_chunk(int64_t max_rows, int splits);

@@ -274,3 +274,24 @@ def test_per_tensor_azp_validation(lib):
     assert qt(FAKE, 0, 4, 128, 128, FAKE, 128, FAKE + 2, FAKE, 1, None) == ALIGN
     assert qt(FAKE, 0, 4, 128, 64, FAKE, 128, FAKE, FAKE, 1, None) == LAYOUT      # ldx < K
     assert qt(None, 0, 0, 128, 128, None, 128, None, None, 0, None) == OK          # static, empty
+
+
+def test_paged_attention_validation(lib):
+    """Paged attention: host-side checks of the block layout."""
+    f = lib.kv_fp8_paged_decode_attention
+
+    def call(B=2, Hq=8, Hkv=2, D=128, nblk=4, bs=16, tables=FAKE, stride=4, lens=FAKE, max_len=64,
+             ws=FAKE, ws_bytes=1 << 20):
+        return f(FAKE, FAKE, B, Hq, Hkv, D, FAKE, FAKE, nblk, bs, tables, stride, lens, max_len,
+                 None, None, 0.0, ws, ws_bytes, None)
+    assert call(bs=12) == UNSUP                  # not a power of two
+    assert call(bs=2048) == UNSUP
+    assert call(bs=0) == UNSUP
+    assert call(stride=3) == SHAPE               # 3 blocks of 16 rows cannot cover 64
+    assert call(nblk=-1) == SHAPE
+    assert call(tables=None) == INVALID
+    assert call(lens=None) == INVALID
+    assert call(tables=FAKE + 2) == ALIGN
+    assert call(D=64) == UNSUP
+    assert call(ws_bytes=16) == INVALID           # workspace too small
+    assert call(B=0) == OK

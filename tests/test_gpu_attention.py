@@ -125,3 +125,110 @@ def test_attention_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+
+
+# ------------------------------------------------------------------ paged cache
+def _paged_layout(lens, bs, seed, spare=3, hkv=2):
+    """Blocks of bs rows in a shuffled placement; returns caches [nblk, bs,
+    hkv, 128] codes, their scales and the block tables (-1 past each length)."""
+    rng = np.random.default_rng(seed)
+    nblk = sum(-(-L // bs) for L in lens) + spare
+    kc, ks = _kv(nblk * bs, hkv, seed, "k")
+    vc, vs = _kv(nblk * bs, hkv, seed, "v")
+    perm = rng.permutation(nblk)
+    width = max(1, max(-(-L // bs) for L in lens))
+    tables = np.full((len(lens), width), -1, np.int32)
+    used = 0
+    for b, L in enumerate(lens):
+        for j in range(-(-L // bs)):
+            tables[b, j] = perm[used]
+            used += 1
+    return kc, ks, vc, vs, tables
+
+
+def _run_paged(lens, hq, hkv, bs, seed, tables=None, max_len=None, sm=0.0):
+    kc, ks, vc, vs, t = _paged_layout(lens, bs, seed, hkv=hkv)
+    tables = t if tables is None else tables(t)
+    max_len = max(max(lens), 1) if max_len is None else max_len
+    B = len(lens)
+    q = workloads.attention_queries(B, hq, 128, seed=seed)
+    nblk = kc.shape[0] // bs
+    out = w8.kv_fp8_paged_decode_attention(
+        q.to(DEV), torch.from_numpy(kc.reshape(nblk, bs, hkv, 128)).to(DEV),
+        torch.from_numpy(vc.reshape(nblk, bs, hkv, 128)).to(DEV),
+        torch.from_numpy(np.ascontiguousarray(tables)).to(DEV),
+        torch.tensor(lens, dtype=torch.int32, device=DEV), max_len,
+        torch.tensor([ks], device=DEV), torch.tensor([vs], device=DEV), sm_scale=sm)
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention_fp8kv_paged(q.view(torch.int16).numpy().view(np.uint16), kc, vc,
+                                              tables, lens, bs, ks, vs, sm if sm else None)
+    return bits(out), ref, vc, vs
+
+
+@pytest.mark.parametrize("bs", [1, 16, 64])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_paged_attention_matches_oracle(G, bs):
+    print(f"paged attention G={G} block {bs}", flush=True)
+    lens = [0, 1, 70, 1300, 257]
+    got, ref, vc, vs = _run_paged(lens, G * 2, 2, bs, seed=20 + G + bs)
+    _check(got, ref, vc, vs, None, G)
+    assert not got[0].any()
+
+
+def test_paged_attention_shared_and_absent_blocks():
+    """A block shared by two sequences (a common prefix) and table entries
+    pointing outside the cache (those rows absent), with an explicit scale."""
+    lens = [200, 96, 160]
+
+    def edit(t):
+        t = t.copy()
+        t[1, 0] = t[0, 0]        # sequence 1 starts with sequence 0's first block
+        t[2, 3] = 10 ** 6        # past the cache
+        t[2, 5] = -7
+        return t
+    got, ref, vc, vs = _run_paged(lens, 8, 2, 16, seed=31, tables=edit, sm=0.06)
+    _check(got, ref, vc, vs, None, 4)
+
+
+def test_paged_attention_equals_contiguous_kernel_on_the_bench_layer():
+    """One Llama-3-8B layer (32768 rows, 16 sequences, 32 over 8 heads) in
+    16-row blocks placed in shuffled order: the paged kernel reads the same
+    rows in the same logical order as the contiguous one, so the outputs are
+    bit-identical; both meet the oracle bar."""
+    hq, hkv, d = workloads.ATTN_HEADS
+    starts = workloads.attention_seq_starts().numpy()
+    lens = np.diff(starts).astype(np.int32)
+    max_len = int(lens.max())
+    rows = int(starts[-1])
+    bs = 16
+    kc, ks = _kv(rows, hkv, 0, "k")
+    vc, vs = _kv(rows, hkv, 0, "v")
+    q = workloads.attention_queries(len(lens), hq, d, seed=0)
+    # sequence b's rows in blocks of 16 (the last one padded), blocks shuffled
+    nb = [-(-int(L) // bs) for L in lens]
+    nblk = sum(nb)
+    perm = np.random.default_rng(7).permutation(nblk)
+    kp = np.zeros((nblk * bs, hkv, d), np.uint8)
+    vp = np.zeros((nblk * bs, hkv, d), np.uint8)
+    tables = np.full((len(lens), max(nb)), -1, np.int32)
+    used = 0
+    for b, L in enumerate(lens):
+        for j in range(nb[b]):
+            r0 = starts[b] + j * bs
+            r1 = min(r0 + bs, starts[b + 1])
+            blk = perm[used]
+            used += 1
+            kp[blk * bs:blk * bs + (r1 - r0)] = kc[r0:r1]
+            vp[blk * bs:blk * bs + (r1 - r0)] = vc[r0:r1]
+            tables[b, j] = blk
+    sc = (torch.tensor([ks], device=DEV), torch.tensor([vs], device=DEV))
+    cont = w8.kv_fp8_decode_attention(q.to(DEV), torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV),
+                                      torch.from_numpy(starts.astype(np.int32)).to(DEV), max_len, *sc)
+    paged = w8.kv_fp8_paged_decode_attention(
+        q.to(DEV), torch.from_numpy(kp.reshape(nblk, bs, hkv, d)).to(DEV),
+        torch.from_numpy(vp.reshape(nblk, bs, hkv, d)).to(DEV), torch.from_numpy(tables).to(DEV),
+        torch.from_numpy(lens).to(DEV), max_len, *sc)
+    torch.cuda.synchronize()
+    assert torch.equal(paged.view(torch.int16), cont.view(torch.int16))
+    ref = oracle.decode_attention_fp8kv(q.view(torch.int16).numpy().view(np.uint16), kc, vc, starts, ks, vs)
+    _check(bits(paged), ref, vc, vs, starts, hq // hkv)
