@@ -48,6 +48,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import re
 import os
 import sys
 import threading
@@ -510,16 +511,24 @@ def clock_under_load(g, stream, replay_s, seconds=2.5, settle_s=0.3, period_s=0.
                       "launches began replaying back to back, over %.1f s" % (settle_s, seconds)}
 
 
-def source_digest():
-    """sha256 over the library's kernel sources: a PMC traffic record taken
-    from other sources no longer describes the kernels."""
+def source_digest(kernel):
+    """sha256 over the sources that define `kernel` ("a+b" for a call of
+    several kernels): the host code and shared headers, and each source file
+    that defines one of its kernels. A PMC traffic record taken from other
+    sources no longer describes the kernel."""
     import hashlib
-    h = hashlib.sha256()
     csrc = os.path.join(ROOT, "int8_scaled_gemm_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+    names = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp", ".cpp")))
+    texts = {}
+    for f in names:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            texts[f] = fh.read()
+    parts = [k.split("<")[0].encode() for k in kernel.split("+")]
+    used = [f for f in names if not f.endswith(".hip")
+            or any(re.search(rb"void\s+" + re.escape(k) + rb"\s*\(", texts[f]) for k in parts)]
+    h = hashlib.sha256()
+    for f in used:
+        h.update(f.encode() + b"\0" + texts[f])
     return h.hexdigest()
 
 
@@ -533,7 +542,7 @@ def recorded_traffic(kernel, workload):
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    digest = source_digest()
+    digest = source_digest(kernel)
     for e in rec.get("entries", []):
         if e.get("kernel") == kernel and e.get("workload") == workload \
                 and e.get("source_sha256") == digest:
