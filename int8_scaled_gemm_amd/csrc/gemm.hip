@@ -161,6 +161,29 @@ __device__ void raw_buffer_load_lds(i32x4 rsrc, lds_u32p lds, int size, int voff
 
 constexpr int kOutOfRange = 0x7FFFFFF0;
 
+// The same load written as inline asm, for the ring loops that wait for
+// their stages themselves: the compiler does not see these loads, so it
+// neither waits for all of them before each barrier (its workgroup fence
+// otherwise covers every direct-to-LDS load in flight, which keeps only one
+// stage in flight whatever the ring depth) nor before each LDS read. Every
+// wait for them is an explicit s_waitcnt vmcnt (wait_stages); loads retire
+// in issue order. No register result.
+template <bool NT>
+__device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, const void* lds, int voffset) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u32p)(const_cast<void*>(lds)))));
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                     :
+                     : "v"(voffset), "s"(rsrc), "s"(m0)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"(voffset), "s"(rsrc), "s"(m0)
+                     : "memory", "m0");
+}
+
 __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t nbytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     i32x4 r;
@@ -344,8 +367,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
             const bool is_a = i < BM / 8;
             const bool ok = base_off[j] != kOutOfRange && kt * kBK + kin[j] < p.K;
             const int off = ok ? base_off[j] + kt * kBK : kOutOfRange;
-            raw_buffer_load_lds(is_a ? ra : rb, (lds_u32p)(st + (is_a ? 0 : BM * kBK) + (is_a ? i : i - BM / 8) * 1024),
-                                16, off, 0, 0, 0);
+            buffer_load_lds16<false>(is_a ? ra : rb, st + (is_a ? 0 : BM * kBK) + (is_a ? i : i - BM / 8) * 1024,
+                                     off);
         }
     };
 
@@ -585,8 +608,10 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
             const int k = k0 + 16 * c;
             const bool ok = r < (is_w ? wrows : p.M) && k < kend;
             const int off = ok ? r * (is_w ? ldb : lda) + k : kOutOfRange;
-            raw_buffer_load_lds(is_w ? rb : ra, (lds_u32p)(base + (is_w ? 0 : CB * CH) + t * 1024),
-                                16, off, 0, 0, is_w ? kNonTemporal : 0);
+            if (is_w)
+                buffer_load_lds16<true>(rb, base + t * 1024, off);
+            else
+                buffer_load_lds16<false>(ra, base + CB * CH + t * 1024, off);
         }
     };
 
@@ -841,15 +866,21 @@ hipError_t run_decode(const GemmArgs& a, hipStream_t st) {
 // scaled_mm_kernel_name, so that profiles can be matched to launches).
 enum Config {
     kDecode64x16,    // gemm_decode_kernel, 64 columns, M <= 16 (stage 512 B, 2 stages)
+    kDecode64x16R,   // the same, 4 stages of 256 B
     kDecode64x64,    // gemm_decode_kernel, 64 columns, M <= 64 (stage 256 B, 2 stages)
     kDecode16x16,    // gemm_decode_kernel, 16 columns, M <= 16 (stage 1 KB, 2 stages)
+    kDecode16x16R,   // the same, 4 stages of 512 B
     kDecode16x64,    // gemm_decode_kernel, 16 columns, M <= 64 (stage 512 B, 2 stages)
-    kDecode16x16L,   // gemm_decode_kernel, 16 columns, M <= 16, long K (stage 2 KB, 2 stages)
+    kDecode16x64R,   // the same, 3 stages
+    kDecode16x16L,   // gemm_decode_kernel, 16 columns, M <= 16, long K (4 stages of 1 KB)
     kDecode16x64L,   // gemm_decode_kernel, 16 columns, M <= 64, long K (stage 1 KB, 2 stages)
-    kTile256x256,    // gemm_tile_kernel 256 x 256, 8 waves
-    kTile256x128,    // gemm_tile_kernel 256 x 128, 8 waves
-    kTile128x128,    // gemm_tile_kernel 128 x 128, 4 waves
-    kTile64x64,      // gemm_tile_kernel 64 x 64, 4 waves
+    kTile256x256,    // gemm_tile_kernel 256 x 256, 8 waves, 2 stages
+    kTile256x128,    // gemm_tile_kernel 256 x 128, 8 waves, 3 stages
+    kTile128x128,    // gemm_tile_kernel 128 x 128, 4 waves, 2 stages
+    kTile128x128R,   // the same, 3 stages
+    kTile64x64,      // gemm_tile_kernel 64 x 64, 4 waves, 2 stages
+    kTile64x64R3,    // the same, 3 stages
+    kTile64x64R4,    // the same, 4 stages
 };
 
 // 16-column workgroups on a long K that fill at most one per CU: a stage
@@ -862,14 +893,30 @@ bool long_k_16(int64_t N, int64_t K) {
     return K >= 8192 && groups > 128 && groups <= 256;
 }
 
+// Ring depth: the direct loads of later stages stay in flight across the
+// stage barriers, so a deeper ring keeps more bytes in flight per
+// workgroup, at the cost of LDS and so of resident workgroups. Measured on
+// MI355X (A/B, same process): deeper pays where the grid still fits one
+// round of the deeper ring's resident workgroups, and loses where it then
+// needs two (decode: 1 x 4096 x 4096 7.1 -> 6.0 us, 16 x 4096 x 14336 16.1
+// -> 13.3, 64 x 4096 x 4096 11.6 -> 9.7, 1 x 28672 x 4096 21.3 -> 20.1, but
+// 64 x 6144 x 4096 14.0 -> 17.0 and 1 x 57344 x 8192 72 -> 97; tiles:
+// 512 x 4096 x 4096 26.3 -> 20.3, 512 x 4096 x 14336 81.9 -> 63.6,
+// 1024 x 4096 x 4096 33.1 -> 25.5, 2048 x 4096 x 4096 43.7 -> 37.7, but
+// 512 x 10240 x 8192 int8 on 128 x 128 tiles 73 -> 84).
 Config select_config(int64_t M, int64_t N, int64_t K) {
     if (M <= 64) {
         // Measured on MI355X at the Llama-3 decode shapes: 64-column blocks
         // stream fastest once they still give every CU a block (N >= 16384);
         // narrower weights need 16-column blocks to reach every CU.
-        if ((N + 63) / 64 >= 256) return M <= 16 ? kDecode64x16 : kDecode64x64;
+        const int64_t blocks64 = (N + 63) / 64, groups16 = (N + 15) / 16;
+        if (blocks64 >= 256) {
+            if (M > 16) return kDecode64x64;
+            return blocks64 <= 512 ? kDecode64x16R : kDecode64x16;
+        }
         if (long_k_16(N, K)) return M <= 16 ? kDecode16x16L : kDecode16x64L;
-        return M <= 16 ? kDecode16x16 : kDecode16x64;
+        if (M <= 16) return groups16 <= 384 ? kDecode16x16R : kDecode16x16;
+        return groups16 <= 256 ? kDecode16x64R : kDecode16x64;
     }
     // The largest tile that still gives every CU a block, else the smallest;
     // 256 x 256 already from 192 tiles (three quarters of the CUs), where
@@ -879,8 +926,9 @@ Config select_config(int64_t M, int64_t N, int64_t K) {
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (tiles(256, 256) >= 192) return kTile256x256;
     if (tiles(256, 128) >= 256) return kTile256x128;
-    if (tiles(128, 128) >= 256) return kTile128x128;
-    return kTile64x64;
+    if (tiles(128, 128) >= 256) return tiles(128, 128) <= 256 ? kTile128x128R : kTile128x128;
+    const int64_t t64 = tiles(64, 64);
+    return t64 <= 512 ? kTile64x64R4 : t64 <= 768 ? kTile64x64R3 : kTile64x64;
 }
 
 template <int QT, int OT>
@@ -888,14 +936,20 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
     if (a.splits > 1) return run_decode<QT, OT, 64, 4, 256, 2>(a, st);
     switch (select_config(a.M, a.N, a.K)) {
         case kDecode64x16: return run_decode<QT, OT, 64, 1, 512, 2>(a, st);
+        case kDecode64x16R: return run_decode<QT, OT, 64, 1, 256, 4>(a, st);
         case kDecode64x64: return run_decode<QT, OT, 64, 4, 256, 2>(a, st);
         case kDecode16x16: return run_decode<QT, OT, 16, 1, 1024, 2>(a, st);
+        case kDecode16x16R: return run_decode<QT, OT, 16, 1, 512, 4>(a, st);
         case kDecode16x64: return run_decode<QT, OT, 16, 4, 512, 2>(a, st);
-        case kDecode16x16L: return run_decode<QT, OT, 16, 1, 2048, 2>(a, st);
+        case kDecode16x64R: return run_decode<QT, OT, 16, 4, 512, 3>(a, st);
+        case kDecode16x16L: return run_decode<QT, OT, 16, 1, 1024, 4>(a, st);
         case kDecode16x64L: return run_decode<QT, OT, 16, 4, 1024, 2>(a, st);
         case kTile256x256: return run_tile<QT, OT, 256, 256, 2, 4, 2>(a, st);
-        case kTile256x128: return run_tile<QT, OT, 256, 128, 4, 2, 2>(a, st);
+        case kTile256x128: return run_tile<QT, OT, 256, 128, 4, 2, 3>(a, st);
         case kTile128x128: return run_tile<QT, OT, 128, 128, 2, 2, 2>(a, st);
+        case kTile128x128R: return run_tile<QT, OT, 128, 128, 2, 2, 3>(a, st);
+        case kTile64x64R3: return run_tile<QT, OT, 64, 64, 2, 2, 3>(a, st);
+        case kTile64x64R4: return run_tile<QT, OT, 64, 64, 2, 2, 4>(a, st);
         default: return run_tile<QT, OT, 64, 64, 2, 2, 2>(a, st);
     }
 }
@@ -1122,14 +1176,20 @@ const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K, bool workspac
     if (workspace && plan_splitk(M, N, K).splits > 1) return "gemm_decode_kernel<64x64>+splitk_reduce_kernel";
     switch (select_config(M, N, K)) {
         case kDecode64x16: return "gemm_decode_kernel<64x16>";
+        case kDecode64x16R: return "gemm_decode_kernel<64x16,4x256>";
         case kDecode64x64: return "gemm_decode_kernel<64x64>";
         case kDecode16x16: return "gemm_decode_kernel<16x16>";
+        case kDecode16x16R: return "gemm_decode_kernel<16x16,4x512>";
         case kDecode16x64: return "gemm_decode_kernel<16x64>";
-        case kDecode16x16L: return "gemm_decode_kernel<16x16,2K>";
+        case kDecode16x64R: return "gemm_decode_kernel<16x64,3x512>";
+        case kDecode16x16L: return "gemm_decode_kernel<16x16,4x1K>";
         case kDecode16x64L: return "gemm_decode_kernel<16x64,1K>";
         case kTile256x256: return "gemm_tile_kernel<256x256>";
         case kTile256x128: return "gemm_tile_kernel<256x128>";
         case kTile128x128: return "gemm_tile_kernel<128x128>";
+        case kTile128x128R: return "gemm_tile_kernel<128x128,3x128>";
+        case kTile64x64R3: return "gemm_tile_kernel<64x64,3x128>";
+        case kTile64x64R4: return "gemm_tile_kernel<64x64,4x128>";
         default: return "gemm_tile_kernel<64x64>";
     }
 }

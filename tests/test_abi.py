@@ -148,20 +148,28 @@ def test_binding_layout_errors_are_python_errors():
 def test_kernel_configuration_names(lib):
     """Host-only query of the kernel configuration a GEMM problem runs with."""
     name = lambda M, N, K: lib.w8a8_scaled_mm_kernel(M, N, K).decode()
-    assert name(1, 4096, 4096) == "gemm_decode_kernel<16x16>"
-    assert name(64, 6144, 4096) == "gemm_decode_kernel<16x64>"
-    assert name(1, 28672, 4096) == "gemm_decode_kernel<64x16>"
+    # deeper rings where the grid fits one round of their resident workgroups
+    assert name(1, 4096, 4096) == "gemm_decode_kernel<16x16,4x512>"      # 256 groups
+    assert name(1, 6144, 4096) == "gemm_decode_kernel<16x16,4x512>"      # 384
+    assert name(1, 8192, 4096) == "gemm_decode_kernel<16x16>"            # 512
+    assert name(64, 4096, 4096) == "gemm_decode_kernel<16x64,3x512>"     # 256
+    assert name(64, 6144, 4096) == "gemm_decode_kernel<16x64>"           # 384
+    assert name(1, 28672, 4096) == "gemm_decode_kernel<64x16,4x256>"     # 448 blocks
+    assert name(1, 57344, 8192) == "gemm_decode_kernel<64x16>"           # 896
     assert name(17, 28672, 4096) == "gemm_decode_kernel<64x64>"
-    assert name(16, 4096, 14336) == "gemm_decode_kernel<16x16,2K>"
-    assert name(16, 6144, 14336) == "gemm_decode_kernel<16x16>"  # more workgroups than CUs
+    assert name(16, 4096, 14336) == "gemm_decode_kernel<16x16,4x1K>"
+    assert name(16, 6144, 14336) == "gemm_decode_kernel<16x16,4x512>"  # more workgroups than CUs
     assert name(8192, 28672, 4096) == "gemm_tile_kernel<256x256>"
     assert name(2048, 4096, 4096) == "gemm_tile_kernel<256x128>"
-    assert name(512, 4096, 4096) == "gemm_tile_kernel<64x64>"
+    assert name(512, 4096, 4096) == "gemm_tile_kernel<64x64,4x128>"      # 512 tiles
+    assert name(512, 6144, 4096) == "gemm_tile_kernel<64x64,3x128>"      # 768
+    assert name(512, 7168, 4096) == "gemm_tile_kernel<64x64>"            # 896
     # 256 x 256 from 192 tiles: one round of large tiles beats two of 256 x 128
     assert name(2048, 6144, 4096) == "gemm_tile_kernel<256x256>"   # 8 x 24 = 192 tiles
     assert name(512, 28672, 4096) == "gemm_tile_kernel<256x256>"   # 2 x 112 = 224 tiles
     assert name(2048, 5888, 4096) == "gemm_tile_kernel<256x128>"   # 8 x 23 = 184 tiles
-    assert name(1024, 4096, 4096) == "gemm_tile_kernel<128x128>"
+    assert name(1024, 4096, 4096) == "gemm_tile_kernel<128x128,3x128>"   # 256 tiles
+    assert name(1024 + 128, 4096, 4096) == "gemm_tile_kernel<128x128>"   # 288
     assert name(-1, 4, 4) == ""
 
 

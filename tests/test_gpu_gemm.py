@@ -57,9 +57,19 @@ def test_scaled_mm_parity(qtype, M, N, K):
 
 
 # Shapes that select each block tile of the tiled kernel (256x256, 256x128,
-# 128x128, 64x128), with ragged M, N and K tails; checked on sampled rows.
+# 128x128 with 2 and 3 ring stages, 64x64 with 4, 3 and 2), with ragged M, N
+# and K tails; checked on sampled rows.
 TILE_SHAPES = [(4096 + 37, 4096 + 48, 384 + 16), (2048, 4096 + 16, 272), (1024 + 5, 4096, 144),
-               (200, 300, 1040)]
+               (200, 300, 1040), (1024 - 3, 4096, 144), (512, 5120 + 16, 400), (512 + 3, 6144 + 16, 272)]
+
+
+def test_tile_configs_are_the_ones_named():
+    """The shapes above cover every tile configuration."""
+    names = {w8.w8a8_scaled_mm_kernel(M, N, K) for M, N, K in TILE_SHAPES}
+    assert names == {"gemm_tile_kernel<256x256>", "gemm_tile_kernel<256x128>",
+                     "gemm_tile_kernel<128x128>", "gemm_tile_kernel<128x128,3x128>",
+                     "gemm_tile_kernel<64x64,4x128>", "gemm_tile_kernel<64x64,3x128>",
+                     "gemm_tile_kernel<64x64>"}, names
 
 
 @pytest.mark.parametrize("otype", ["bf16", "fp16"])
@@ -251,7 +261,9 @@ DECODE_SHAPES = [(1, 4096, 4096), (5, 6144 + 16, 4096 + 16), (16, 4096, 14336), 
                  (16, 16384, 2064), (17, 16384, 2048), (64, 16400, 272), (40, 20000, 512),
                  (3, 16336, 16), (64, 28672, 4096),
                  # long K on 129..256 sixteen-column workgroups: the long-stage variants
-                 (64, 4096, 14336), (40, 3000 + 8, 8192 + 16)]
+                 (64, 4096, 14336), (40, 3000 + 8, 8192 + 16),
+                 # grids past one round of the deeper rings: the 2-stage variants
+                 (1, 32768 + 16, 272), (48, 6144 + 16, 1040)]
 
 
 @pytest.mark.parametrize("qtype", ["fp8", "int8"])
@@ -269,9 +281,11 @@ def test_decode_configs_parity(qtype, M, N, K):
 def test_decode_configs_are_the_ones_named():
     """The shapes above cover every decode configuration."""
     names = {w8.w8a8_scaled_mm_kernel(M, N, K) for M, N, K in DECODE_SHAPES}
-    assert names == {"gemm_decode_kernel<16x16>", "gemm_decode_kernel<16x64>",
-                     "gemm_decode_kernel<64x16>", "gemm_decode_kernel<64x64>",
-                     "gemm_decode_kernel<16x16,2K>", "gemm_decode_kernel<16x64,1K>"}, names
+    assert names == {"gemm_decode_kernel<16x16>", "gemm_decode_kernel<16x16,4x512>",
+                     "gemm_decode_kernel<16x64>", "gemm_decode_kernel<16x64,3x512>",
+                     "gemm_decode_kernel<64x16>", "gemm_decode_kernel<64x16,4x256>",
+                     "gemm_decode_kernel<64x64>", "gemm_decode_kernel<16x16,4x1K>",
+                     "gemm_decode_kernel<16x64,1K>"}, names
 
 
 # Split-K through a caller workspace: decode problems above 16 rows with a
