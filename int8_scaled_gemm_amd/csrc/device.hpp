@@ -40,28 +40,43 @@ template <typename T>
 __device__ __forceinline__ T load16(const T* p, bool nt) {
     return nt ? __builtin_nontemporal_load(p) : *p;
 }
+// The same in two halves: the raw 16 (float32: 32) bytes, then their
+// widening, so that several loads can be in flight before the first use.
 template <int XT, bool NT = true>
-__device__ __forceinline__ void load8(const void* base, int64_t idx, float v[8]) {
+__device__ __forceinline__ void load8_raw(const void* base, int64_t idx, u32x4 r[2]) {
+    if constexpr (XT == D_F32) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + idx);
+        r[0] = load16(p, NT);
+        r[1] = load16(p + 1, NT);
+    } else {
+        r[0] = load16(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + idx), NT);
+    }
+}
+template <int XT>
+__device__ __forceinline__ void widen8(const u32x4 r[2], float v[8]) {
     if constexpr (XT == D_BF16) {
-        u32x4 r = load16(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + idx), NT);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(r[i] << 16);
-            v[2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
+            v[2 * i] = __uint_as_float(r[0][i] << 16);
+            v[2 * i + 1] = __uint_as_float(r[0][i] & 0xFFFF0000u);
         }
     } else if constexpr (XT == D_FP16) {
-        h16x8 h = load16(reinterpret_cast<const h16x8*>(static_cast<const uint16_t*>(base) + idx), NT);
+        const h16x8 h = __builtin_bit_cast(h16x8, r[0]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = static_cast<float>(h[i]);
     } else {
-        const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
-        f32x4 lo = load16(p, NT), hi = load16(p + 1, NT);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            v[i] = lo[i];
-            v[4 + i] = hi[i];
+            v[i] = __uint_as_float(r[0][i]);
+            v[4 + i] = __uint_as_float(r[1][i]);
         }
     }
+}
+template <int XT, bool NT = true>
+__device__ __forceinline__ void load8(const void* base, int64_t idx, float v[8]) {
+    u32x4 r[2];
+    load8_raw<XT, NT>(base, idx, r);
+    widen8<XT>(r, v);
 }
 
 // ----------------------------------------------------------- quantisation

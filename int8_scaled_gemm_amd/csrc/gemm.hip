@@ -697,12 +697,15 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
 // correctly rounded division, so codes and scale are bit-identical to
 // w8a8_quant_per_token. The codes stay in LDS; workgroup 0 also writes them
 // and the scale to memory at the end. The weight rows stream through a
-// 2-slot LDS ring in chunks of 16 rows x 2 KB, two chunks in flight. The row
-// x is requested before the weights: loads retire in issue order, so the
-// quantisation then waits only for x. Weight chunk c of row r sits at slot
-// c ^ (r % 16).
+// 4-slot LDS ring in chunks of 16 rows x 1 KB, three chunks in flight. The
+// row x is requested before the weights: loads retire in issue order, so the
+// quantisation then waits only for x (the first chunks are compiler-visible
+// loads, which it counts; the later ones are the inline-asm loads with
+// explicit waits, and the barriers carry no fence, so that no wait drains
+// the ring). Weight chunk c of row r sits at slot c ^ (r % 16).
 // ---------------------------------------------------------------------------
-constexpr int kDynqChunk = 2048;       // K bytes of weight per chunk
+constexpr int kDynqChunk = 1024;       // K bytes of weight per chunk
+constexpr int kDynqSlots = 4;          // chunks in the LDS ring
 constexpr int kDynqMaxK = 15360;       // longest row quantised in LDS (two workgroups per CU)
 
 template <int XT, int QT, int OT>
@@ -714,7 +717,8 @@ __global__ __launch_bounds__(256) void gemm_dynq_kernel(GemmArgs p, const void* 
     constexpr int WL = 16 * CH / 4096;  // weight loads per wave per chunk
     constexpr int SW = CH / kBK / 4;    // slices per wave per chunk
     constexpr int kGroups = (kDynqMaxK + 2047) / 2048;  // 8-element groups of x per thread
-    __shared__ __attribute__((aligned(1024))) uint8_t wbuf[2][16 * CH];
+    constexpr int NB = kDynqSlots;
+    __shared__ __attribute__((aligned(1024))) uint8_t wbuf[NB][16 * CH];
     __shared__ __attribute__((aligned(16))) uint8_t arow[kDynqMaxK];
     __shared__ float part[4];
 
@@ -730,7 +734,7 @@ __global__ __launch_bounds__(256) void gemm_dynq_kernel(GemmArgs p, const void* 
     // chunk order rotated per workgroup, as in the decode kernel
     const int rot = (ldb % 4096 == 0 && nch > 0) ? blockIdx.x % nch : 0;
     auto chunk_k = [&](int ci) { return (ci + rot < nch ? ci + rot : ci + rot - nch) * CH; };
-    auto chunk = [&](int ci, int buf) {
+    auto chunk = [&](int ci, int buf, bool visible) {
         const int kc = chunk_k(ci);
 #pragma unroll
         for (int j = 0; j < WL; ++j) {
@@ -739,31 +743,47 @@ __global__ __launch_bounds__(256) void gemm_dynq_kernel(GemmArgs p, const void* 
             const int r = o / CH, c = ((o % CH) >> 4) ^ (r & 15);
             const int k = kc + 16 * c;
             const int off = (r < wrows && k < K) ? r * ldb + k : kOutOfRange;
-            raw_buffer_load_lds(rb, (lds_u32p)(wbuf[buf] + t * 1024), 16, off, 0, 0, kNonTemporal);
+            if (visible)
+                raw_buffer_load_lds(rb, (lds_u32p)(wbuf[buf] + t * 1024), 16, off, 0, 0, kNonTemporal);
+            else
+                buffer_load_lds16<true>(rb, wbuf[buf] + t * 1024, off);
         }
     };
+    // A barrier without the workgroup fence of __syncthreads (which would
+    // wait for every direct load in flight): LDS stores are waited for here,
+    // the ring's loads by their explicit waits.
+    auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
-    // x first, then the first two weight chunks.
-    float v[kGroups][8];
+    // x first, then the first weight chunks.
+    // All of the thread's loads of x are issued, unconditionally and
+    // before the first is used, so that the compiler's wait for them counts
+    // the weight loads issued after them (groups past K load the row's first
+    // 8 elements, one cache line, and are not used).
+    u32x4 raw[kGroups][2];
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) {
         const int k = 8 * threadIdx.x + 2048 * j;
-        if (k < K) load8<XT>(x, k, v[j]);
+        load8_raw<XT>(x, k < K ? k : 0, raw[j]);
     }
     asm volatile("" ::: "memory");
-    if (nch > 0) chunk(0, 0);
-    if (nch > 1) chunk(1, 1);
+#pragma unroll
+    for (int ci = 0; ci < NB - 1; ++ci)
+        if (ci < nch) chunk(ci, ci, true);
 
     // The row's maximum |x|, its scale and its codes (into LDS).
+    float v[kGroups][8];
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kGroups; ++j)
+    for (int j = 0; j < kGroups; ++j) {
+        if (2048 * j >= K) break;
+        widen8<XT>(raw[j], v[j]);
         if (8 * static_cast<int>(threadIdx.x) + 2048 * j < K)
 #pragma unroll
             for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
+    }
     amax = wave_max(amax);
     if (lane == 0) part[wave] = amax;
-    __syncthreads();
+    barrier();
     amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
     const float s = scale_from_absmax<QT>(amax);
     const double rcp = 1.0 / static_cast<double>(s);
@@ -777,12 +797,11 @@ __global__ __launch_bounds__(256) void gemm_dynq_kernel(GemmArgs p, const void* 
     const u32x4 z = {0, 0, 0, 0};
     Acc acc = Acc{0, 0, 0, 0};
     for (int ci = 0; ci < nch; ++ci) {
-        // chunk ci has landed once at most the next chunk's loads are pending
-        if (ci + 1 < nch) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WL) : "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();  // every wave's share of chunk ci (and the codes) is in LDS
+        // chunk ci has landed once at most the chunks issued after it are pending
+        wait_stages<NB - 2, WL>(min(nch - 1 - ci, NB - 2));
+        barrier();  // every wave's share of chunk ci (and the codes) is in LDS; slot (ci - 1) % NB is free
         const int kc = chunk_k(ci);
-        const uint8_t* wrow = wbuf[ci & 1] + r16 * CH;
+        const uint8_t* wrow = wbuf[ci % NB] + r16 * CH;
 #pragma unroll
         for (int sv = 0; sv < SW; ++sv) {
             const int u = 4 * sv + wave;
@@ -797,12 +816,12 @@ __global__ __launch_bounds__(256) void gemm_dynq_kernel(GemmArgs p, const void* 
                                   hi ? *reinterpret_cast<const u32x4*>(arow + k + 16) : z);
             mma<QT>(acc, af, wf);
         }
-        __syncthreads();  // every wave is done with slot ci & 1
-        if (ci + 2 < nch) chunk(ci + 2, ci & 1);
+        if (ci + NB - 1 < nch) chunk(ci + NB - 1, (ci + NB - 1) % NB, false);
     }
 
     // Add the four waves' sums in a fixed order; row 0 of column l % 16 is
     // element 0 of lanes 0..15.
+    __syncthreads();  // every wave is done with the ring
     Acc* red = reinterpret_cast<Acc*>(wbuf[0]);
     red[wave * 64 + lane] = acc;
     __syncthreads();
