@@ -651,13 +651,51 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
 
     // In a 16 x 16 tile lane l holds rows 4 (l / 16) + r, r < 4, of column l % 16.
     // Each result goes out scaled (no split) or as a plain partial sum of this
-    // workgroup's K range (split K).
+    // workgroup's K range (split K). The scales (and zero-point operands) of
+    // a tile's four outputs are all loaded before the first store, at
+    // clamped indices: loads under each store's own bounds check were waited
+    // for one at a time.
     typedef typename std::conditional<QT == Q_FP8, float, int32_t>::type Part;
     Part* part = static_cast<Part*>(p.part) + static_cast<int64_t>(sp) * p.M * p.N;
-    auto put = [&](int m, int n, auto v) {
-        if (m < p.M && n < p.N) {
-            if (S > 1) part[static_cast<int64_t>(m) * p.N + n] = static_cast<Part>(v);
-            else store_out<OT>(p, m, n, v);
+    auto put4 = [&](int i, int n, const Acc& v) {
+        const int m0 = 16 * i + 4 * g;
+        if (S > 1) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (m0 + r < p.M && n < p.N) part[static_cast<int64_t>(m0 + r) * p.N + n] = static_cast<Part>(v[r]);
+            return;
+        }
+        const int nc = min(n, p.N - 1);
+        const float sb = p.sb ? p.sb[p.sb_per_col ? nc : 0] : 1.0f;
+        float sa[4];
+        int32_t z[4] = {0, 0, 0, 0};
+        int32_t cs = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int mc = min(m0 + r, p.M - 1);
+            sa[r] = p.sa ? p.sa[p.sa_per_row ? mc : 0] : 1.0f;
+            if constexpr (QT == Q_INT8)
+                if (p.azp) z[r] = p.azp[p.azp_per_row ? mc : 0];
+        }
+        if constexpr (QT == Q_INT8)
+            if (p.azp) cs = p.colsum[nc];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = m0 + r;
+            if (m < p.M && n < p.N) {
+                auto acc_r = v[r];
+                if constexpr (QT == Q_INT8)
+                    if (p.azp) acc_r -= z[r] * cs;
+                const int64_t o = static_cast<int64_t>(m) * p.ldo + n;
+                if constexpr (OT == D_I32) {
+                    static_cast<int32_t*>(p.out)[o] = static_cast<int32_t>(acc_r);
+                } else {
+                    const float d = static_cast<float>(acc_r) * sa[r] * sb;
+                    if constexpr (OT == D_BF16) static_cast<uint16_t*>(p.out)[o] = to_bf16_bits(d);
+                    else if constexpr (OT == D_FP16) static_cast<uint16_t*>(p.out)[o] = to_fp16_bits(d);
+                    else static_cast<float*>(p.out)[o] = d;
+                }
+            }
         }
     };
     if constexpr (WPG == 1) {
@@ -665,8 +703,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             if (i >= mt) break;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) put(16 * i + 4 * g + r, n, acc[i][r]);
+            put4(i, n, acc[i]);
         }
     } else {
         // The WPG waves of a column group hold sums over disjoint K slices:
@@ -682,8 +719,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
             Acc sum = red[(first * MT + i) * 64 + lane];
 #pragma unroll
             for (int w = 1; w < WPG; ++w) sum += red[((first + w) * MT + i) * 64 + lane];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) put(16 * i + 4 * g + r, n, sum[r]);
+            put4(i, n, sum);
         }
     }
 }
@@ -840,20 +876,54 @@ __global__ __launch_bounds__(256) void gemm_dynq_kernel(GemmArgs p, const void* 
 }
 
 // Split-K epilogue: D = scales * (sum of the splits' partial sums, added in
-// split order), 4 elements per thread.
+// split order), 4 elements per thread. Every load (partial sums at clamped
+// indices, scales, zero-point operands) is issued before the first is used.
+constexpr int kMaxSplitsK = 4;  // plan_splitk splits K at most 4 ways
+
 template <int QT, int OT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
     typedef typename std::conditional<QT == Q_FP8, float, int32_t>::type Part;
     const Part* part = static_cast<const Part*>(p.part);
     const int64_t plane = static_cast<int64_t>(p.M) * p.N;
     const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (e0 >= plane) return;
+    Part v[kMaxSplitsK][4];
+    float sa[4], sb[4];
+    int32_t z[4] = {0, 0, 0, 0}, cs[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int64_t e = min(e0 + r, plane - 1);
+        const int m = static_cast<int>(e / p.N), n = static_cast<int>(e % p.N);
+#pragma unroll
+        for (int q = 0; q < kMaxSplitsK; ++q) v[q][r] = part[min(q, p.splits - 1) * plane + e];
+        sa[r] = p.sa ? p.sa[p.sa_per_row ? m : 0] : 1.0f;
+        sb[r] = p.sb ? p.sb[p.sb_per_col ? n : 0] : 1.0f;
+        if constexpr (QT == Q_INT8) {
+            if (p.azp) {
+                z[r] = p.azp[p.azp_per_row ? m : 0];
+                cs[r] = p.colsum[n];
+            }
+        }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int64_t e = e0 + r;
         if (e >= plane) break;
-        Part sum = part[e];
-        for (int q = 1; q < p.splits; ++q) sum += part[q * plane + e];
-        store_out<OT>(p, static_cast<int>(e / p.N), static_cast<int>(e % p.N), sum);
+        Part sum = v[0][r];
+#pragma unroll
+        for (int q = 1; q < kMaxSplitsK; ++q)
+            if (q < p.splits) sum += v[q][r];
+        if constexpr (QT == Q_INT8)
+            if (p.azp) sum -= z[r] * cs[r];
+        const int64_t o = (e / p.N) * p.ldo + e % p.N;
+        if constexpr (OT == D_I32) {
+            static_cast<int32_t*>(p.out)[o] = static_cast<int32_t>(sum);
+        } else {
+            const float d = static_cast<float>(sum) * sa[r] * sb[r];
+            if constexpr (OT == D_BF16) static_cast<uint16_t*>(p.out)[o] = to_bf16_bits(d);
+            else if constexpr (OT == D_FP16) static_cast<uint16_t*>(p.out)[o] = to_fp16_bits(d);
+            else static_cast<float*>(p.out)[o] = d;
+        }
     }
 }
 
@@ -1005,7 +1075,7 @@ SplitPlan plan_splitk(int64_t M, int64_t N, int64_t K) {
     constexpr int64_t kSlots = 512;   // resident 64-column workgroups
     constexpr int kStageBytes = 256;  // the 64-column kernel's K stage
     const int64_t stages = (K + kStageBytes - 1) / kStageBytes;
-    d.splits = static_cast<int>(std::min<int64_t>(4, std::max<int64_t>(2, kSlots / blocks)));
+    d.splits = static_cast<int>(std::min<int64_t>(kMaxSplitsK, std::max<int64_t>(2, kSlots / blocks)));
     d.stages_per_split = static_cast<int>((stages + d.splits - 1) / d.splits);
     d.workspace_bytes = static_cast<int64_t>(d.splits) * M * N * 4;
     return d;
@@ -1129,8 +1199,10 @@ hipError_t launch_scaled_mm_noalloc(const GemmProblem& p, hipStream_t st, int64_
 // quantizer launch on weights up to 16384 rows; on wider ones (gate_up,
 // 28672) the per-workgroup quantisation over N / 16 workgroups costs more
 // than the launch, and the 64-column decode kernel is faster.
+// (K == 0 takes the two-call path: the fused kernel reads x[0 .. 7] whatever
+// the row's length.)
 bool quant_scaled_mm_fused(int64_t M, int64_t N, int64_t K) {
-    return M == 1 && K <= kDynqMaxK && (N + 63) / 64 < 256;
+    return M == 1 && K > 0 && K <= kDynqMaxK && (N + 63) / 64 < 256;
 }
 
 hipError_t launch_quant_scaled_mm(const GemmProblem& p, int xt, const void* x, int64_t ldx,

@@ -38,14 +38,26 @@ __global__ __launch_bounds__(BS) void quant_rows_kernel(const void* __restrict__
     const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
     const bool active = row < M;
 
+    // Every load is issued before the first is used (a conditional load
+    // that is widened at once would be waited for before the next is
+    // issued); lanes past the row load the tensor's first element group
+    // instead and count zeros. K == 0 (a call that only writes scales of 1)
+    // reads nothing.
+    u32x4 raw[VPT][2] = {};
+    if (K > 0) {
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int64_t k = static_cast<int64_t>(t + i * TPR) * 8;
+            load8_raw<XT>(x, active && k < K ? row * ldx + k : 0, raw[i]);
+        }
+    }
     float v[VPT][8];
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
         const int64_t k = static_cast<int64_t>(t + i * TPR) * 8;
-        if (active && k < K) {
-            load8<XT>(x, row * ldx + k, v[i]);
-        } else {
+        widen8<XT>(raw[i], v[i]);
+        if (!(active && k < K)) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
         }
@@ -157,6 +169,20 @@ __device__ __forceinline__ uint8_t* code_at(uint8_t* q, int64_t ldq, int64_t K, 
     return q + (e / K) * ldq + (e % K);
 }
 
+// The 8 elements at x + off[j] for each of U units, every load issued before
+// the first is widened (a conditional load widened at once is waited for
+// before the next one is issued). A unit that is not ok loads the tensor's
+// first 8 elements instead, and its values are not to be used.
+template <int XT, bool NT, int U>
+__device__ __forceinline__ void load_units(const void* x, const int64_t (&off)[U], const bool (&ok)[U],
+                                           float (&v)[U][8]) {
+    u32x4 raw[U][2];
+#pragma unroll
+    for (int j = 0; j < U; ++j) load8_raw<XT, NT>(x, ok[j] ? off[j] : 0, raw[j]);
+#pragma unroll
+    for (int j = 0; j < U; ++j) widen8<XT>(raw[j], v[j]);
+}
+
 template <int XT>
 __global__ __launch_bounds__(kBlock) void absmax_kernel(const void* __restrict__ x, int64_t ldx,
                                                         Units u, int64_t K, uint8_t* q,
@@ -165,12 +191,14 @@ __global__ __launch_bounds__(kBlock) void absmax_kernel(const void* __restrict__
     for (uint32_t base = blockIdx.x * kAbsUnroll; base < u.total; base += gridDim.x * kAbsUnroll) {
         float v[kAbsUnroll][8];
         bool ok[kAbsUnroll];
+        int64_t off[kAbsUnroll];
 #pragma unroll
         for (int j = 0; j < kAbsUnroll; ++j) {
             int64_t row, k;
             ok[j] = unit_coords(u, base + j, K, row, k);
-            if (ok[j]) load8<XT, false>(x, row * ldx + k, v[j]);  // cached: read again next
+            off[j] = row * ldx + k;
         }
+        load_units<XT, false>(x, off, ok, v);  // cached: read again next
 #pragma unroll
         for (int j = 0; j < kAbsUnroll; ++j)
             if (ok[j])
@@ -217,13 +245,14 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_kernel(const void* __rest
     for (uint32_t base = blockIdx.x * U; base < u.total; base += gridDim.x * U) {
         float v[U][8];
         bool ok[U];
-        int64_t row[U], k[U];
+        int64_t row[U], k[U], off[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             ok[j] = unit_coords(u, base + j, K, row[j], k[j]);
             if (DYNAMIC && ok[j] && row[j] * K + k[j] >= tail.start) ok[j] = false;
-            if (ok[j]) load8<XT>(x, row[j] * ldx + k[j], v[j]);
+            off[j] = row[j] * ldx + k[j];
         }
+        load_units<XT, true>(x, off, ok, v);
 #pragma unroll
         for (int j = 0; j < U; ++j)
             if (ok[j]) *reinterpret_cast<u32x2*>(q + row[j] * ldq + k[j]) = quant8<QT>(v[j], r);
@@ -514,12 +543,14 @@ __global__ __launch_bounds__(kBlock) void range_kernel(const void* __restrict__ 
     for (uint32_t base = blockIdx.x * kAbsUnroll; base < u.total; base += gridDim.x * kAbsUnroll) {
         float v[kAbsUnroll][8];
         bool ok[kAbsUnroll];
+        int64_t off[kAbsUnroll];
 #pragma unroll
         for (int j = 0; j < kAbsUnroll; ++j) {
             int64_t row, k;
             ok[j] = unit_coords(u, base + j, K, row, k);
-            if (ok[j]) load8<XT, false>(x, row * ldx + k, v[j]);  // cached: read again next
+            off[j] = row * ldx + k;
         }
+        load_units<XT, false>(x, off, ok, v);  // cached: read again next
 #pragma unroll
         for (int j = 0; j < kAbsUnroll; ++j)
             if (ok[j])
@@ -594,13 +625,14 @@ __global__ __launch_bounds__(kBlock) void quant_tensor_azp_kernel(const void* __
     for (uint32_t base = blockIdx.x * kUnroll; base < u.total; base += gridDim.x * kUnroll) {
         float v[kUnroll][8];
         bool ok[kUnroll];
-        int64_t row[kUnroll], k[kUnroll];
+        int64_t row[kUnroll], k[kUnroll], off[kUnroll];
 #pragma unroll
         for (int j = 0; j < kUnroll; ++j) {
             ok[j] = unit_coords(u, base + j, K, row[j], k[j]);
             if (DYNAMIC && ok[j] && row[j] * K + k[j] >= tail.start) ok[j] = false;
-            if (ok[j]) load8<XT>(x, row[j] * ldx + k[j], v[j]);
+            off[j] = row[j] * ldx + k[j];
         }
+        load_units<XT, true>(x, off, ok, v);
 #pragma unroll
         for (int j = 0; j < kUnroll; ++j)
             if (ok[j]) *reinterpret_cast<u32x2*>(q + row[j] * ldq + k[j]) = quant8_azp(v[j], a.r, a.zf);

@@ -109,6 +109,22 @@ def test_quant_scaled_mm_zero_row_and_saturation():
     assert np.array_equal(f32_bits(sa.cpu().numpy()), f32_bits(sa_ref))
 
 
+def test_quant_scaled_mm_empty_row():
+    """K == 0 at one token (the fused kernel's shape, which would read the
+    row's first elements): nothing is read, the scale is 1.0 and the output
+    zero. The host-side choice is the two-call path."""
+    assert w8.w8a8_quant_scaled_mm_kernel(1, 64, 0) == "quant_rows_kernel+scaled_mm"
+    x = torch.empty(1, 0, dtype=torch.bfloat16, device=DEV)
+    bd = torch.empty(64, 0, dtype=torch.float8_e4m3fn, device=DEV).t()
+    q = torch.empty(1, 0, dtype=torch.float8_e4m3fn, device=DEV)
+    sa = torch.full((1,), 7.0, dtype=torch.float32, device=DEV)
+    out = torch.full((1, 64), 5.0, dtype=torch.bfloat16, device=DEV)
+    w8.w8a8_quant_scaled_mm(x, bd, None, "fp8", out=out, q=q, a_scales=sa)
+    torch.cuda.synchronize()
+    assert float(sa[0]) == 1.0
+    assert (out.float() == 0).all()
+
+
 def test_quant_scaled_mm_graph_replay():
     """The fused call captures into a HIP graph; every replay matches eager."""
     M, N, K = 1, 4096, 4096
