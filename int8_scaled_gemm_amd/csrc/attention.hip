@@ -231,13 +231,19 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs p) {
             }
             return;
         }
+        // The rows of the lane's four K and four V pieces first (a paged row
+        // reads its block entry from LDS; read between the loads, whose asm
+        // orders memory, each would be waited for in turn).
+        int64_t row[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) row[j] = cache_row(k, (64 * j + lane) / 8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int i = 64 * (j & 3) + lane;
             const int t = i / 8, sl = i % 8;
             const int c = sl ^ (j < 4 ? (t & 7) : vswz(t));
-            const int64_t row = cache_row(k, t);
-            const uint8_t* src = row >= 0 ? (j < 4 ? p.k : p.v) + row * rstride + goff + 16 * c : kZeroPiece;
+            const uint8_t* src =
+                row[j & 3] >= 0 ? (j < 4 ? p.k : p.v) + row[j & 3] * rstride + goff + 16 * c : kZeroPiece;
             load_lds16(src, lds_addr(&ring[slot][(j < 4 ? 0 : kStep * kD) + 16 * 64 * (j & 3)]));
         }
     };
