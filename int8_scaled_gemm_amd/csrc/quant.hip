@@ -298,16 +298,21 @@ __global__ __launch_bounds__(kBlock) void kv_dequant_kernel(const uint8_t* __res
     const int64_t nvec = n / 8;
     for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock * U + threadIdx.x;
          base < nvec; base += static_cast<int64_t>(gridDim.x) * kBlock * U) {
+        // Every load is issued before the first is used, and every store
+        // after the last conversion: a load under its bounds check was
+        // waited for before the next was issued, and a load after a store
+        // made the compiler wait for the store as well. Pieces past the
+        // tensor load its first 8 codes and are not stored.
         u32x2 c[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             const int64_t i = base + j * kBlock;
-            if (i < nvec) c[j] = reinterpret_cast<const u32x2*>(q)[i];
+            c[j] = reinterpret_cast<const u32x2*>(q)[i < nvec ? i : 0];
         }
+        typedef typename std::conditional<XT == D_F32, f32x4, u32x4>::type Out;
+        Out o[U][XT == D_F32 ? 2 : 1];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            const int64_t i = base + j * kBlock;
-            if (i >= nvec) continue;
             float f[8];
 #pragma unroll
             for (int w = 0; w < 2; ++w) {
@@ -317,11 +322,9 @@ __global__ __launch_bounds__(kBlock) void kv_dequant_kernel(const uint8_t* __res
                 f[4 * w + 3] = __builtin_amdgcn_cvt_f32_fp8(c[j][w], 3) * s;
             }
             if constexpr (XT == D_F32) {
-                f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(x) + i * 8);
-                o[0] = f32x4{f[0], f[1], f[2], f[3]};
-                o[1] = f32x4{f[4], f[5], f[6], f[7]};
+                o[j][0] = f32x4{f[0], f[1], f[2], f[3]};
+                o[j][1] = f32x4{f[4], f[5], f[6], f[7]};
             } else {
-                u32x4 o;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     uint32_t lo, hi;
@@ -332,9 +335,20 @@ __global__ __launch_bounds__(kBlock) void kv_dequant_kernel(const uint8_t* __res
                         lo = to_fp16_bits(f[2 * w]);
                         hi = to_fp16_bits(f[2 * w + 1]);
                     }
-                    o[w] = lo | (hi << 16);
+                    o[j][0][w] = lo | (hi << 16);
                 }
-                __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(x) + i * 8));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int64_t i = base + j * kBlock;
+            if (i >= nvec) continue;
+            if constexpr (XT == D_F32) {
+                f32x4* out = reinterpret_cast<f32x4*>(static_cast<float*>(x) + i * 8);
+                out[0] = o[j][0];
+                out[1] = o[j][1];
+            } else {
+                __builtin_nontemporal_store(o[j][0], reinterpret_cast<u32x4*>(static_cast<uint16_t*>(x) + i * 8));
             }
         }
     }
