@@ -216,11 +216,21 @@ __global__ __launch_bounds__(kBlock) void absmax_kernel(const void* __restrict__
     }
 }
 
-// Maximum of the stored partials, in every thread of the workgroup.
+// Maximum of the stored partials (at most 1024, at least 1), in every
+// thread of the workgroup; a thread's loads are all issued before the first
+// is used (past the count they re-read partial 0).
 __device__ float reduce_partials(uint8_t* q, int64_t ldq, int64_t K, const Tail& tail) {
+    constexpr int kPer = 1024 / kBlock;
+    float pv[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = threadIdx.x + j * kBlock;
+        pv[j] = *reinterpret_cast<const float*>(code_at(q, ldq, K, tail.start + 4 * (i < tail.parts ? i : 0)));
+    }
     float amax = 0.0f;
-    for (int i = threadIdx.x; i < tail.parts; i += kBlock)
-        amax = fmaxf(amax, *reinterpret_cast<const float*>(code_at(q, ldq, K, tail.start + 4 * i)));
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+        if (static_cast<int>(threadIdx.x) + j * kBlock < tail.parts) amax = fmaxf(amax, pv[j]);
     amax = wave_max(amax);
     __shared__ float part[kBlock / 64];
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
@@ -266,12 +276,29 @@ __global__ __launch_bounds__(kBlock) void finish_tail_kernel(const void* __restr
                                                              int64_t ldx, uint8_t* q, int64_t ldq,
                                                              float* scale, int64_t M, int64_t K,
                                                              Tail tail) {
+    // The thread's first two 8-element groups of the tail are requested
+    // together with the partial maxima (a tail past a large tensor has at
+    // most 4096 elements: two groups per thread); groups past the tensor
+    // load its first group and are not used.
+    const int64_t total = M * K;
+    const int64_t e0 = tail.start + 8 * static_cast<int64_t>(threadIdx.x), e1 = e0 + 8 * kBlock;
+    auto xoff = [&](int64_t e) { return e < total ? (e / K) * ldx + e % K : 0; };  // never across a row (K % 16 == 0)
+    u32x4 ra[2][2];
+    load8_raw<XT>(x, xoff(e0), ra[0]);
+    load8_raw<XT>(x, xoff(e1), ra[1]);
     const float s = scale_from_absmax<QT>(reduce_partials(q, ldq, K, tail));
     __syncthreads();  // every partial has been read
     if (threadIdx.x == 0) *scale = s;
     const double r = 1.0 / static_cast<double>(s);
-    for (int64_t e = tail.start + 8 * static_cast<int64_t>(threadIdx.x); e < M * K; e += 8 * kBlock) {
-        const int64_t row = e / K, k = e % K;  // 8 elements, never across a row (K % 16 == 0)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t e = j ? e1 : e0;
+        float v[8];
+        widen8<XT>(ra[j], v);
+        if (e < total) *reinterpret_cast<u32x2*>(q + (e / K) * ldq + e % K) = quant8<QT>(v, r);
+    }
+    for (int64_t e = e1 + 8 * kBlock; e < total; e += 8 * kBlock) {  // small tensors: the whole tensor is the tail
+        const int64_t row = e / K, k = e % K;
         float v[8];
         load8<XT>(x, row * ldx + k, v);
         *reinterpret_cast<u32x2*>(q + row * ldq + k) = quant8<QT>(v, r);
