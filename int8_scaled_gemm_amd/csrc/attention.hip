@@ -17,9 +17,9 @@
 //    codes, converted exactly to fp16 and read transposed from LDS, make the
 //    output sums on fp16 MFMAs. Writes (o, m, l) per head and split.
 //  - attn_combine_kernel: per (sequence, head), the splits' partial sums
-//    rescaled to the common maximum (kept as a running maximum in one pass
-//    over the splits), divided by the total weight, times v_scale, rounded
-//    to bf16.
+//    rescaled to the common maximum (32 splits at a time, all their loads in
+//    flight together, with a running maximum across batches), divided by the
+//    total weight, times v_scale, rounded to bf16.
 #include <math.h>
 
 #include <algorithm>
@@ -36,6 +36,7 @@ constexpr int kStep = 32;      // cache rows per wave step
 constexpr int kMaxSplits = 1024;  // row splits per sequence at most
 constexpr int kStages = 2;        // steps in a wave's LDS ring
 constexpr int64_t kMinWaves = 1024;  // waves the split rule aims for at least
+constexpr int kCombineBatch = 32;    // splits whose partial sums the combine requests together
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -367,25 +368,41 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs p) {
 }
 
 __global__ __launch_bounds__(kD) void attn_combine_kernel(AttnArgs p) {
-    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x, lane = threadIdx.x & (kCombineBatch - 1);
     const float* part = p.part + (static_cast<int64_t>(b) * p.Hq + h) * p.splits * (kD + 2);
-    // Only the splits that start inside the sequence were written. One pass
-    // with a running maximum: the sums so far and each split's are rescaled
-    // to the larger of the two maxima as they are added; a split with no
-    // weight (every row absent) adds nothing.
+    // Only the splits that start inside the sequence were written. They are
+    // taken kCombineBatch at a time, every load of a batch issued before the
+    // first is used (past the last split a batch re-reads it, unused): lane j
+    // (mod 32) holds split j's maximum and weight, and every thread its
+    // dim of each split's sums. The batch's largest maximum over the splits
+    // with weight, each split's sums scaled to the larger of it and the
+    // running maximum, added to the running sums rescaled likewise. A split
+    // with no weight (every row absent) adds nothing.
     const int len = max(p.tables ? p.lens[b] : p.starts[b + 1] - p.starts[b], 0);
     const int live = min(p.splits, (len + p.chunk - 1) / p.chunk);
     float mx = -INFINITY, tot = 0.0f, acc = 0.0f;
-#pragma unroll 8
-    for (int s = 0; s < live; ++s) {
-        const float* ps = part + s * (kD + 2);
-        const float ms = ps[kD], ls = ps[kD + 1], v = ps[d];
-        const bool w = ls > 0.0f;
-        const float mn = w ? fmaxf(mx, ms) : mx;
-        const float a = w ? __expf(mx - mn) : 1.0f;  // 0 while nothing is summed
-        const float f = w ? __expf(ms - mn) : 0.0f;
-        tot = w ? fmaf(ls, f, tot * a) : tot;
-        acc = w ? fmaf(v, f, acc * a) : acc;
+    for (int s0 = 0; s0 < live; s0 += kCombineBatch) {
+        const float* pl = part + min(s0 + lane, live - 1) * (kD + 2);
+        const float mj = pl[kD], lj = pl[kD + 1];
+        float v[kCombineBatch];
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j) v[j] = part[min(s0 + j, live - 1) * (kD + 2) + d];
+        const bool wj = s0 + lane < live && lj > 0.0f;
+        float mb = wj ? mj : -INFINITY;
+#pragma unroll
+        for (int m = kCombineBatch / 2; m >= 1; m >>= 1) mb = fmaxf(mb, __shfl_xor(mb, m, 64));
+        const float mn = fmaxf(mx, mb);  // -inf while no split so far has weight
+        const float a = mn == -INFINITY ? 1.0f : __expf(mx - mn);  // 0 while nothing is summed
+        const float fj = wj ? __expf(mj - mn) : 0.0f;
+        float tb = lj * fj;
+#pragma unroll
+        for (int m = kCombineBatch / 2; m >= 1; m >>= 1) tb += __shfl_xor(tb, m, 64);
+        float ab = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j)
+            ab = fmaf(v[j], __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fj), j)), ab);
+        tot = fmaf(tot, a, tb);
+        acc = fmaf(acc, a, ab);
         mx = mn;
     }
     const float vs = p.v_scale ? *p.v_scale : 1.0f;

@@ -76,6 +76,14 @@ def test_attention_explicit_softmax_scale_and_one_split():
     _check(got, ref, vc, vs, starts, 4)
 
 
+def test_attention_more_splits_than_one_combine_batch():
+    """A 6000-row sequence over 2 KV heads: 94 splits of 64 rows, which the
+    combine takes 32 at a time (three batches, the last one short)."""
+    starts = [0, 6000, 6100]
+    got, ref, vc, vs = _run(starts, 8, 2, 6000, seed=41)
+    _check(got, ref, vc, vs, starts, 4)
+
+
 def test_attention_rows_outside_the_cache_are_not_read():
     # the last sequence claims rows past the end of the cache: only the
     # cache's rows take part (the oracle sees the same truncated sequence)
@@ -187,6 +195,20 @@ def test_paged_attention_shared_and_absent_blocks():
         t[2, 5] = -7
         return t
     got, ref, vc, vs = _run_paged(lens, 8, 2, 16, seed=31, tables=edit, sm=0.06)
+    _check(got, ref, vc, vs, None, 4)
+
+
+def test_paged_attention_absent_prefix_spans_a_combine_batch():
+    """The first 130 blocks of a 3000-row sequence absent (table entries -1):
+    the splits of the combine's whole first batch have no weight, and the
+    result is the attention over the rows from 2080 on."""
+    lens = [3000, 40]
+
+    def edit(t):
+        t = t.copy()
+        t[0, :130] = -1
+        return t
+    got, ref, vc, vs = _run_paged(lens, 8, 2, 16, seed=43, tables=edit)
     _check(got, ref, vc, vs, None, 4)
 
 
