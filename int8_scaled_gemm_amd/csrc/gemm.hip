@@ -330,6 +330,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
     static_assert(TM >= 1 && TN >= 1 && kLoads % NW == 0, "tile shape");
     static_assert(ST >= 2 && kLPW * (ST - 2) <= 63, "loads in flight");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * kStage];
+    __shared__ float scl[BM + BN];  // the tile's row scales, then its column scales
+    static_assert(NW * 64 >= BM + BN, "one thread per row and column scale");
 
     int tm, tn;
     if (!tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn)) return;
@@ -404,6 +406,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
         }
     };
 
+    // The 2-byte-output epilogue's scales, one per thread (rows past the
+    // matrix clamped), loaded now and kept in a register through the main
+    // loop, so that the epilogue does not start with a memory round trip
+    // (measured on MI355X: 8192 x 28672 x 4096 763 -> 754 us, 2048 x 6144 x
+    // 4096 53.2 -> 51.7 us).
+    float scale_pre = 1.0f;
+    if constexpr (OT == D_BF16 || OT == D_FP16) {
+        const int t = threadIdx.x;
+        if (t < BM) {
+            const int m = min(m0 + t, p.M - 1);
+            scale_pre = p.sa ? p.sa[p.sa_per_row ? m : 0] : 1.0f;
+        } else if (t < BM + BN) {
+            const int n = min(n0 + t - BM, p.N - 1);
+            scale_pre = p.sb ? p.sb[p.sb_per_col ? n : 0] : 1.0f;
+        }
+    }
     const int KT = (p.K + kBK - 1) / kBK;
     if (KT > 0) {
         issue(0, 0);
@@ -447,19 +465,21 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
         constexpr int kChunks = BN / 8;
         constexpr int kRowsPerAccess = 64 / kChunks;
         static_assert(BM * BN * 2 <= ST * kStage, "the output tile fits the LDS ring");
+        if (threadIdx.x < BM + BN) scl[threadIdx.x] = scale_pre;
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __syncthreads();  // every wave is done reading the ring
-        // The lane's TM row scales (and zero points) are loaded once; its
-        // 16 column scales (and code sums) of each 32-column group j just
+        __syncthreads();  // every wave is done reading the ring; scl is written
+        // The lane's TM row scales (and zero points) are read once; its 16
+        // column scales (and code sums) of each 32-column group j just
         // before that group is written, so that few stay live at a time
         // (rows and columns past the matrix are clamped; they are never
-        // stored).
+        // stored). The scales come from scl, the zero points and code sums
+        // from memory.
         float sav[TM];
         int zv[TM];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int m = min(m0 + wm * WM + i * 32 + (lane & 31), p.M - 1);
-            sav[i] = p.sa ? p.sa[p.sa_per_row ? m : 0] : 1.0f;
+            sav[i] = scl[wm * WM + i * 32 + (lane & 31)];
             zv[i] = 0;
             if constexpr (QT == Q_INT8)
                 if (p.azp) zv[i] = p.azp[p.azp_per_row ? m : 0];
@@ -474,7 +494,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
                 for (int e = 0; e < 16; ++e) {
                     const int col = wn * WN + j * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                     const int n = min(n0 + col, p.N - 1);
-                    sbv[e] = p.sb ? p.sb[p.sb_per_col ? n : 0] : 1.0f;
+                    sbv[e] = scl[BM + col];
                     csv[e] = 0;
                     if constexpr (decltype(with_azp)::value) csv[e] = p.colsum[n];
                 }
