@@ -331,6 +331,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
     static_assert(ST >= 2 && kLPW * (ST - 2) <= 63, "loads in flight");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[ST * kStage];
     __shared__ float scl[BM + BN];  // the tile's row scales, then its column scales
+    __shared__ int32_t zcs[QT == Q_INT8 ? BM + BN : 1];  // its zero points, then its code sums
     static_assert(NW * 64 >= BM + BN, "one thread per row and column scale");
 
     int tm, tn;
@@ -406,20 +407,25 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
         }
     };
 
-    // The 2-byte-output epilogue's scales, one per thread (rows past the
-    // matrix clamped), loaded now and kept in a register through the main
+    // The 2-byte-output epilogue's scales (and for asymmetric int8 the zero
+    // points and code sums), one per thread (rows and columns past the
+    // matrix clamped), loaded now and kept in registers through the main
     // loop, so that the epilogue does not start with a memory round trip
     // (measured on MI355X: 8192 x 28672 x 4096 763 -> 754 us, 2048 x 6144 x
     // 4096 53.2 -> 51.7 us).
     float scale_pre = 1.0f;
+    int32_t zcs_pre = 0;
     if constexpr (OT == D_BF16 || OT == D_FP16) {
         const int t = threadIdx.x;
+        const bool azp = QT == Q_INT8 && p.azp;
         if (t < BM) {
             const int m = min(m0 + t, p.M - 1);
             scale_pre = p.sa ? p.sa[p.sa_per_row ? m : 0] : 1.0f;
+            if (azp) zcs_pre = p.azp[p.azp_per_row ? m : 0];
         } else if (t < BM + BN) {
             const int n = min(n0 + t - BM, p.N - 1);
             scale_pre = p.sb ? p.sb[p.sb_per_col ? n : 0] : 1.0f;
+            if (azp) zcs_pre = p.colsum[n];
         }
     }
     const int KT = (p.K + kBK - 1) / kBK;
@@ -465,24 +471,23 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
         constexpr int kChunks = BN / 8;
         constexpr int kRowsPerAccess = 64 / kChunks;
         static_assert(BM * BN * 2 <= ST * kStage, "the output tile fits the LDS ring");
-        if (threadIdx.x < BM + BN) scl[threadIdx.x] = scale_pre;
+        if (threadIdx.x < BM + BN) {
+            scl[threadIdx.x] = scale_pre;
+            if constexpr (QT == Q_INT8) zcs[threadIdx.x] = zcs_pre;
+        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __syncthreads();  // every wave is done reading the ring; scl is written
         // The lane's TM row scales (and zero points) are read once; its 16
         // column scales (and code sums) of each 32-column group j just
-        // before that group is written, so that few stay live at a time
-        // (rows and columns past the matrix are clamped; they are never
-        // stored). The scales come from scl, the zero points and code sums
-        // from memory.
+        // before that group is written, so that few stay live at a time.
         float sav[TM];
         int zv[TM];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int m = min(m0 + wm * WM + i * 32 + (lane & 31), p.M - 1);
             sav[i] = scl[wm * WM + i * 32 + (lane & 31)];
             zv[i] = 0;
             if constexpr (QT == Q_INT8)
-                if (p.azp) zv[i] = p.azp[p.azp_per_row ? m : 0];
+                if (p.azp) zv[i] = zcs[wm * WM + i * 32 + (lane & 31)];
         }
         // The tile into LDS; the zero-point term is compiled in only where used.
         auto write_tile = [&](auto with_azp) {
@@ -493,10 +498,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_tile_kernel(GemmArgs p) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int col = wn * WN + j * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    const int n = min(n0 + col, p.N - 1);
                     sbv[e] = scl[BM + col];
                     csv[e] = 0;
-                    if constexpr (decltype(with_azp)::value) csv[e] = p.colsum[n];
+                    if constexpr (decltype(with_azp)::value) csv[e] = zcs[BM + col];
                 }
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
