@@ -991,8 +991,7 @@ enum Config {
     kTile256x128,    // gemm_tile_kernel 256 x 128, 8 waves, 3 stages
     kTile128x128,    // gemm_tile_kernel 128 x 128, 4 waves, 2 stages
     kTile128x128R,   // the same, 3 stages
-    kTile64x64,      // gemm_tile_kernel 64 x 64, 4 waves, 2 stages
-    kTile64x64R3,    // the same, 3 stages
+    kTile64x64R3,    // gemm_tile_kernel 64 x 64, 4 waves, 3 stages
     kTile64x64R4,    // the same, 4 stages
 };
 
@@ -1032,16 +1031,18 @@ Config select_config(int64_t M, int64_t N, int64_t K) {
         return groups16 <= 256 ? kDecode16x64R : kDecode16x64;
     }
     // The largest tile that still gives every CU a block, else the smallest;
-    // 256 x 256 already from 192 tiles (three quarters of the CUs), where
-    // one round of the large tile beats two of the half-size one (measured
-    // on MI355X: 2048 x 6144 x 4096 52 us against 64, 512 x 28672 x 4096 58
-    // against 70).
+    // 256 x 256 and 128 x 128 already from 192 tiles (three quarters of the
+    // CUs), where one round of the large tile beats two of the half-size one
+    // (measured on MI355X: 2048 x 6144 x 4096 52 us against 64, 512 x 28672
+    // x 4096 58 against 70, 512 x 6144 x 4096 on 128 x 128 tiles 23.2 against
+    // 28.2 on 64 x 64; at 128 tiles 64 x 64 still wins: 512 x 4096 x 4096
+    // 19.8 against 22.0). Below 192 tiles of 128 x 128 there are at most 768
+    // of 64 x 64.
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (tiles(256, 256) >= 192) return kTile256x256;
     if (tiles(256, 128) >= 256) return kTile256x128;
-    if (tiles(128, 128) >= 256) return tiles(128, 128) <= 256 ? kTile128x128R : kTile128x128;
-    const int64_t t64 = tiles(64, 64);
-    return t64 <= 512 ? kTile64x64R4 : t64 <= 768 ? kTile64x64R3 : kTile64x64;
+    if (tiles(128, 128) >= 192) return tiles(128, 128) <= 256 ? kTile128x128R : kTile128x128;
+    return tiles(64, 64) <= 512 ? kTile64x64R4 : kTile64x64R3;
 }
 
 template <int QT, int OT>
@@ -1063,8 +1064,8 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
         case kTile128x128R: return run_tile<QT, OT, 128, 128, 2, 2, 3>(a, st);
         case kTile64x64R3: return run_tile<QT, OT, 64, 64, 2, 2, 3>(a, st);
         case kTile64x64R4: return run_tile<QT, OT, 64, 64, 2, 2, 4>(a, st);
-        default: return run_tile<QT, OT, 64, 64, 2, 2, 2>(a, st);
     }
+    return hipErrorInvalidValue;  // not reached: select_config returns one of the above
 }
 
 template <int QT>
@@ -1305,8 +1306,8 @@ const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K, bool workspac
         case kTile128x128R: return "gemm_tile_kernel<128x128,3x128>";
         case kTile64x64R3: return "gemm_tile_kernel<64x64,3x128>";
         case kTile64x64R4: return "gemm_tile_kernel<64x64,4x128>";
-        default: return "gemm_tile_kernel<64x64>";
     }
+    return "";  // not reached
 }
 
 }  // namespace w8a8

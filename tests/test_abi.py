@@ -162,8 +162,9 @@ def test_kernel_configuration_names(lib):
     assert name(8192, 28672, 4096) == "gemm_tile_kernel<256x256>"
     assert name(2048, 4096, 4096) == "gemm_tile_kernel<256x128>"
     assert name(512, 4096, 4096) == "gemm_tile_kernel<64x64,4x128>"      # 512 tiles
-    assert name(512, 6144, 4096) == "gemm_tile_kernel<64x64,3x128>"      # 768
-    assert name(512, 7168, 4096) == "gemm_tile_kernel<64x64>"            # 896
+    assert name(512, 5120, 4096) == "gemm_tile_kernel<64x64,3x128>"      # 640 (160 of 128 x 128)
+    assert name(512, 6144, 4096) == "gemm_tile_kernel<128x128,3x128>"    # 192 of 128 x 128
+    assert name(512, 7168, 4096) == "gemm_tile_kernel<128x128,3x128>"    # 224
     # 256 x 256 from 192 tiles: one round of large tiles beats two of 256 x 128
     assert name(2048, 6144, 4096) == "gemm_tile_kernel<256x256>"   # 8 x 24 = 192 tiles
     assert name(512, 28672, 4096) == "gemm_tile_kernel<256x256>"   # 2 x 112 = 224 tiles

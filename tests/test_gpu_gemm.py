@@ -68,8 +68,7 @@ def test_tile_configs_are_the_ones_named():
     names = {w8.w8a8_scaled_mm_kernel(M, N, K) for M, N, K in TILE_SHAPES}
     assert names == {"gemm_tile_kernel<256x256>", "gemm_tile_kernel<256x128>",
                      "gemm_tile_kernel<128x128>", "gemm_tile_kernel<128x128,3x128>",
-                     "gemm_tile_kernel<64x64,4x128>", "gemm_tile_kernel<64x64,3x128>",
-                     "gemm_tile_kernel<64x64>"}, names
+                     "gemm_tile_kernel<64x64,4x128>", "gemm_tile_kernel<64x64,3x128>"}, names
 
 
 @pytest.mark.parametrize("otype", ["bf16", "fp16"])
