@@ -104,7 +104,7 @@ struct AttnArgs {
     float sm_scale;
     int B, Hq, Hkv;
     int64_t rows;            // cache rows (reads past them are skipped)
-    int splits, chunk;       // row splits per sequence, rows per split (multiple of 64)
+    int splits, chunk;       // row splits per sequence, rows per split (multiple of 32)
     float* part;             // [B, Hq, splits, 130] partial sums, maxima and weights
     // Paged layout (tables != NULL): sequence b has lens[b] rows; its logical
     // row t is cache row tables[b * table_stride + t / 2^bshift] * 2^bshift +
