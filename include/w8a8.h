@@ -23,8 +23,10 @@
  *  - All data pointers are DEVICE pointers on the current HIP device; scale
  *    arrays are device float32 arrays. The caller owns and allocates every
  *    buffer. The library never allocates, frees or synchronises, and keeps no
- *    global state, so each call can be captured into a HIP graph. Work is
- *    enqueued on `stream` (0 = the null stream) and runs asynchronously.
+ *    global state (besides the static device array that w8a8_scaled_mm_noalloc
+ *    uses instead of a workspace), so each call can be captured into a HIP
+ *    graph. Work is enqueued on `stream` (0 = the null stream) and runs
+ *    asynchronously.
  *  - Inputs are validated on the host from the arguments alone (device data
  *    is never read). A bad argument returns an error status and never aborts
  *    the process; w8a8_last_error() then holds a message (per thread).
@@ -138,8 +140,9 @@ int64_t w8a8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*
  * w8a8_scaled_mm with an optional caller workspace [P1: the same operation].
- * When workspace_bytes >= w8a8_scaled_mm_workspace_size(M, N, K) > 0, four
- * workgroups share each 64-column tile along K, write their partial sums to
+ * When workspace_bytes >= w8a8_scaled_mm_workspace_size(M, N, K) > 0, two to
+ * four workgroups (as many as fill one round of the GPU's workgroup slots)
+ * share each 64-column tile along K, write their partial sums to
  * the workspace, and a second kernel adds them in a fixed split order and
  * applies the scales: results are deterministic, and equal to
  * w8a8_scaled_mm's up to the fp8 summation order (bit-identical for int8).
