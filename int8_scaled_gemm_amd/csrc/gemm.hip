@@ -13,12 +13,17 @@
 //    operands staged in LDS by direct global -> LDS loads.
 //  - gemm_decode_kernel (M <= 64, bound by the weight stream): 16 x 16 MFMAs
 //    (v_mfma_f32_16x16x128_f8f6f4, v_mfma_i32_16x16x64_i8) on a block of
-//    16 or 64 output columns, weights streamed once through an LDS ring.
+//    16 or 64 output columns, weights streamed once through an LDS ring;
+//    with a caller workspace and a long K, split along K, the partial sums
+//    added by splitk_reduce_kernel.
+//  - gemm_dynq_kernel (M == 1): the per-token quantisation of the one row
+//    and the product in one kernel.
 // Each MFMA lane holds a run of contiguous K bytes of one row of each
 // operand; the order of K inside a fragment differs from memory order, but A
 // and B always share it, so the sum is the same.
 // The epilogue is fused: scales applied in fp32 and the result rounded to
-// nearest even into bf16/fp16 in registers, then stored once.
+// nearest even into bf16/fp16 in registers, then stored once (the tile
+// kernel through LDS, as whole rows).
 
 #include <atomic>
 #include <mutex>
