@@ -21,7 +21,7 @@ import torch
 import int8_scaled_gemm_amd as w8
 import oracle
 import workloads
-from tests.gpu_util import DEV, TORCH_OF, assert_close_fraction, bits, check_scaled_mm_rows, f32_bits
+from tests.gpu_util import DEV, TORCH_OF, assert_close_fraction, bits, check_scaled_mm_rows, f32_bits, ulp
 
 pytestmark = pytest.mark.gpu
 
@@ -109,6 +109,42 @@ def test_fp8_prefill_full(M, name, N, K, otype):
 def test_int8_70b_full(M, name, N, K):
     print(f"int8 70B M={M} {name} {N}x{K}", flush=True)
     _check_layer(M, N, K, "int8", "per_token", seed=13 * M + N % 83)
+
+
+@pytest.mark.parametrize("name,N,K", workloads.LLAMA3_70B_LAYERS)
+@pytest.mark.parametrize("M", workloads.INT8_70B_M)
+def test_int8_azp_70b_full(M, name, N, K):
+    """The int8_azp workload's route at its sizes: per-token asymmetric
+    activations (scale and zero point per row), per-channel int8 weights and
+    their code sums, the product with the zero-point term in the epilogue.
+    Sampled rows of every step against the oracle: codes, scales, zero points
+    and code sums bit for bit, the int32 sums exactly, the bf16 output within
+    one ulp of the exact value and equal to its rounding almost everywhere."""
+    print(f"int8 azp 70B M={M} {name} {N}x{K}", flush=True)
+    seed = 17 * M + N % 89
+    w, wq, ws, wq_h, ws_h = _weights_checked(N, K, "int8", seed)
+    del w
+    cs = w8.w8a8_colsum(wq)
+    x = workloads.activations(M, K, seed=seed + 500, device=DEV)
+    q, sa, z = w8.w8a8_quant_per_token_azp(x)
+    out = w8.w8a8_scaled_mm_azp(q, wq.t(), sa, z, cs, ws, torch.bfloat16)
+    acc = w8.w8a8_scaled_mm_azp(q, wq.t(), None, z, cs, None, torch.int32)
+    torch.cuda.synchronize()
+    wrows = _sample_rows(N, seed + 2, 8)
+    assert np.array_equal(cs.cpu().numpy()[wrows], oracle.colsum(wq_h[wrows]))
+    rows = _sample_rows(M, seed + 1, 16 if M > 64 else M)
+    ri = torch.tensor(rows, device=DEV)
+    q_ref, s_ref, z_ref = oracle.quant_per_token_azp(_u16(x[ri]), "bf16")
+    q_h = bits(q[ri])
+    sa_h, z_h = sa[ri].cpu().numpy(), z[ri].cpu().numpy()
+    assert np.array_equal(q_h, q_ref)
+    assert np.array_equal(f32_bits(sa_h), f32_bits(s_ref)) and np.array_equal(z_h, z_ref)
+    assert np.array_equal(acc[ri].cpu().numpy(), oracle.scaled_mm_azp(q_h, wq_h, None, z_h, None, "i32"))
+    ref = oracle.scaled_mm_azp(q_h, wq_h, sa_h, z_h, ws_h, "f64")
+    got = out[ri].float().cpu().numpy().astype(np.float64)
+    assert (np.abs(got - ref) <= ulp(ref, "bf16")).all()
+    exact = np.mean(bits(out[ri]) == oracle.scaled_mm_azp(q_h, wq_h, sa_h, z_h, ws_h, "bf16"))
+    assert exact > 0.99, exact
 
 
 def test_kv_cache_layer_full_sampled():
