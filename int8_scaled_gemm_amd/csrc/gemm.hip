@@ -997,7 +997,8 @@ enum Config {
     kTile256x256,    // gemm_tile_kernel 256 x 256, 8 waves, 2 stages
     kTile256x128,    // gemm_tile_kernel 256 x 128, 8 waves, 3 stages
     kTile128x128,    // gemm_tile_kernel 128 x 128, 4 waves, 2 stages
-    kTile128x128R,   // the same, 3 stages
+    kTile128x128R,   // gemm_tile_kernel 128 x 128, 8 waves, 3 stages (4 waves: 5% slower)
+    kTile128x64,     // gemm_tile_kernel 128 x 64, 8 waves, 4 stages
     kTile64x64R3,    // gemm_tile_kernel 64 x 64, 4 waves, 3 stages
     kTile64x64R4,    // the same, 4 stages
 };
@@ -1043,12 +1044,19 @@ Config select_config(int64_t M, int64_t N, int64_t K) {
     // (measured on MI355X: 2048 x 6144 x 4096 52 us against 64, 512 x 28672
     // x 4096 58 against 70, 512 x 6144 x 4096 on 128 x 128 tiles 23.2 against
     // 28.2 on 64 x 64; at 128 tiles 64 x 64 still wins: 512 x 4096 x 4096
-    // 19.8 against 22.0). Below 192 tiles of 128 x 128 there are at most 768
-    // of 64 x 64.
+    // 19.8 against 22.0). Between them, 128 x 64 tiles (eight 32 x 32 waves,
+    // a 96 KB ring: one workgroup per CU) where 192 to 256 of them fill one
+    // round: 512 x 4096 x 4096 20.2 -> 17.1 us, 512 x 4096 x 14336 63.0 ->
+    // 51.1, 300 x 4096 x 4096 18.5 -> 15.4, 128 x 16384 x 4096 27.2 -> 21.4
+    // against 64 x 64; past one round they lose (512 x 5120 x 4096, 320
+    // tiles: 27.1 -> 30.5), and so they do below 192 (400 x 2048 x 8192, 128
+    // tiles: 23.4 -> 27.7). Below 192 tiles of 128 x 128 there are at most
+    // 768 of 64 x 64.
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (tiles(256, 256) >= 192) return kTile256x256;
     if (tiles(256, 128) >= 256) return kTile256x128;
     if (tiles(128, 128) >= 192) return tiles(128, 128) <= 256 ? kTile128x128R : kTile128x128;
+    if (tiles(128, 64) >= 192 && tiles(128, 64) <= 256) return kTile128x64;
     return tiles(64, 64) <= 512 ? kTile64x64R4 : kTile64x64R3;
 }
 
@@ -1068,7 +1076,8 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
         case kTile256x256: return run_tile<QT, OT, 256, 256, 2, 4, 2>(a, st);
         case kTile256x128: return run_tile<QT, OT, 256, 128, 4, 2, 3>(a, st);
         case kTile128x128: return run_tile<QT, OT, 128, 128, 2, 2, 2>(a, st);
-        case kTile128x128R: return run_tile<QT, OT, 128, 128, 2, 2, 3>(a, st);
+        case kTile128x128R: return run_tile<QT, OT, 128, 128, 2, 4, 3>(a, st);
+        case kTile128x64: return run_tile<QT, OT, 128, 64, 4, 2, 4>(a, st);
         case kTile64x64R3: return run_tile<QT, OT, 64, 64, 2, 2, 3>(a, st);
         case kTile64x64R4: return run_tile<QT, OT, 64, 64, 2, 2, 4>(a, st);
     }
@@ -1311,6 +1320,7 @@ const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K, bool workspac
         case kTile256x128: return "gemm_tile_kernel<256x128>";
         case kTile128x128: return "gemm_tile_kernel<128x128>";
         case kTile128x128R: return "gemm_tile_kernel<128x128,3x128>";
+        case kTile128x64: return "gemm_tile_kernel<128x64,4x128>";
         case kTile64x64R3: return "gemm_tile_kernel<64x64,3x128>";
         case kTile64x64R4: return "gemm_tile_kernel<64x64,4x128>";
     }

@@ -161,8 +161,12 @@ def test_kernel_configuration_names(lib):
     assert name(16, 6144, 14336) == "gemm_decode_kernel<16x16,4x512>"  # more workgroups than CUs
     assert name(8192, 28672, 4096) == "gemm_tile_kernel<256x256>"
     assert name(2048, 4096, 4096) == "gemm_tile_kernel<256x128>"
-    assert name(512, 4096, 4096) == "gemm_tile_kernel<64x64,4x128>"      # 512 tiles
-    assert name(512, 5120, 4096) == "gemm_tile_kernel<64x64,3x128>"      # 640 (160 of 128 x 128)
+    # 128 x 64 where 192 to 256 of them fill one round, else 64 x 64
+    assert name(512, 4096, 4096) == "gemm_tile_kernel<128x64,4x128>"     # 256 tiles
+    assert name(300, 4096, 4096) == "gemm_tile_kernel<128x64,4x128>"     # 192
+    assert name(128, 16384, 4096) == "gemm_tile_kernel<128x64,4x128>"    # 256
+    assert name(400, 2048, 8192) == "gemm_tile_kernel<64x64,4x128>"      # 128 of 128 x 64; 224
+    assert name(512, 5120, 4096) == "gemm_tile_kernel<64x64,3x128>"      # 320 of 128 x 64; 640
     assert name(512, 6144, 4096) == "gemm_tile_kernel<128x128,3x128>"    # 192 of 128 x 128
     assert name(512, 7168, 4096) == "gemm_tile_kernel<128x128,3x128>"    # 224
     # 256 x 256 from 192 tiles: one round of large tiles beats two of 256 x 128

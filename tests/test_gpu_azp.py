@@ -66,7 +66,8 @@ def test_colsum_strided():
 
 
 SHAPES = [(1, 4096, 4096), (16, 28672, 1024), (64, 4096, 4096 + 16), (33, 1000, 1040),
-          (64, 28672, 512), (300, 520, 272), (1024, 768, 2048), (65, 130, 128)]
+          (64, 28672, 512), (300, 520, 272), (1024, 768, 2048), (65, 130, 128),
+          (400 + 7, 3072 + 16, 1040), (1024 - 3, 4096, 144)]
 
 
 @pytest.mark.parametrize("per_token", [True, False])
