@@ -89,6 +89,22 @@ def test_tile_configs_sampled_rows(qtype, M, N, K, otype):
     assert_close_fraction(info, qtype, otype)
 
 
+@pytest.mark.parametrize("qtype,otype", [("fp8", "f32"), ("int8", "f32"), ("int8", "i32")])
+@pytest.mark.parametrize("M,N,K", TILE_SHAPES)
+def test_tile_configs_wide_outputs_sampled_rows(qtype, otype, M, N, K):
+    """The 4-byte outputs (float32, and int8's raw int32 accumulator) on
+    every block tile: their epilogue stores the fragments directly instead of
+    restaging the tile through LDS."""
+    a, sa, b, sb = _quantized(M, N, K, qtype, seed=M + 3 * N + K)
+    if otype == "i32":
+        sa = sb = None
+    got = _run(a, b, qtype, sa, sb, otype)
+    rng = np.random.default_rng(M + 1)
+    rows = [0, 1, 31, 32, 127, 128, M - 1, M - 2] + list(rng.integers(0, M, 24))
+    rows = [r for r in rows if r < M]
+    check_scaled_mm_rows(got, rows, a, b, qtype, sa, sb, otype)
+
+
 @pytest.mark.parametrize("qtype", ["fp8", "int8"])
 @pytest.mark.parametrize("otype", ["bf16", "fp16", "f32"])
 @pytest.mark.parametrize("gran", ["tensor-tensor", "token-tensor", "tensor-channel", "none"])
@@ -159,12 +175,14 @@ def test_tiny_int8_case_end_to_end():
 
 
 @pytest.mark.parametrize("col0", [24, 23])
-@pytest.mark.parametrize("M", [7, 150])
-def test_submatrices_and_output_padding(M, col0):
+@pytest.mark.parametrize("M,N", [(7, 96), (150, 96), (300, 4096 + 32), (3000, 4096)])
+def test_submatrices_and_output_padding(M, N, col0):
     """A and B as column windows of wider matrices (leading dimensions larger
     than K), output into a window of a wider buffer: padding untouched. An
-    odd first column leaves the output only 2-byte aligned (element stores)."""
-    N, K = 96, 256
+    odd first column leaves the output only 2-byte aligned (element stores).
+    The shapes reach the decode kernel and the 64x64, 128x64 and 256x256
+    tiles."""
+    K = 256
     qtype = "fp8"
     abig = workloads.random_codes((M, K + 64), qtype, seed=5).numpy()
     bbig = workloads.random_codes((N + 8, K + 32), qtype, seed=6).numpy()
