@@ -66,7 +66,13 @@ typedef enum w8a8_status {
 /* 8-bit code type of quantised operands. */
 typedef enum w8a8_qtype {
     W8A8_Q_INT8 = 0,        /* symmetric int8, codes -127..127 */
-    W8A8_Q_FP8_E4M3FN = 1   /* OCP fp8 E4M3 */
+    W8A8_Q_FP8_E4M3FN = 1,  /* OCP fp8 E4M3 */
+    /* Range markers, never valid arguments: they give the type the range of
+     * a 32-bit int, so that any int a caller passes is a value of the type
+     * and is rejected by the validation (W8A8_ERR_DTYPE). Without them a
+     * C++ compiler may take the type to hold only 0 and 1. */
+    W8A8_QTYPE_RANGE_MIN = -2147483647 - 1,
+    W8A8_QTYPE_RANGE_MAX = 2147483647
 } w8a8_qtype;
 
 /* Element type of high-precision tensors (inputs of quantizers, outputs). */
@@ -74,7 +80,10 @@ typedef enum w8a8_dtype {
     W8A8_BF16 = 0,
     W8A8_FP16 = 1,
     W8A8_F32 = 2,   /* float32 */
-    W8A8_I32 = 3    /* int32: raw int8 accumulator output of w8a8_scaled_mm only */
+    W8A8_I32 = 3,   /* int32: raw int8 accumulator output of w8a8_scaled_mm only */
+    /* Range markers, never valid arguments (as for w8a8_qtype). */
+    W8A8_DTYPE_RANGE_MIN = -2147483647 - 1,
+    W8A8_DTYPE_RANGE_MAX = 2147483647
 } w8a8_dtype;
 
 /*

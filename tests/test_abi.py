@@ -74,6 +74,10 @@ def test_scaled_mm_validation(lib):
     assert mm(lib, out=FAKE + 1) == ALIGN              # bf16 out must be 2-byte aligned
     assert mm(lib, qt=7) == DTYPE
     assert mm(lib, ot=9) == DTYPE
+    # any int is rejected, negative and extreme ones too (the enums span int)
+    for bad in (-1, 2, -2147483648, 2147483647):
+        assert mm(lib, qt=bad) == DTYPE, bad
+        assert mm(lib, ot=bad if bad != 2 else 4) == DTYPE, bad
     assert mm(lib, ot=3, qt=1) == DTYPE                 # raw int32 only for int8
     assert mm(lib, ot=3, qt=0, sa=FAKE) == INVALID      # raw accumulator takes no scales
     assert mm(lib, sa=FAKE, n_a=5) == SHAPE             # neither 1 nor M
@@ -187,6 +191,8 @@ def test_quant_scaled_mm_validation(lib):
     assert f(sa=None) == INVALID           # the per-token scales are an output
     assert f(ldb=64) == LAYOUT             # B not column-major
     assert f(xt=9) == DTYPE
+    assert f(xt=-1) == DTYPE
+    assert f(qt=-2147483648) == DTYPE
     assert f(ldx=100) == LAYOUT
     assert f(sb=FAKE, n_b=7) == SHAPE
     assert f(x=None) == INVALID
