@@ -154,6 +154,30 @@ def test_fp8_uniform_random_codes():
     check_scaled_mm(_run(a1, b, "fp8", sa[:7], sb, "f32"), a1, b, "fp8", sa[:7], sb, "f32")
 
 
+@pytest.mark.parametrize("M", [5, 100])
+def test_fp8_codes_read_as_ocp_e4m3(M):
+    """The matrix cores read the codes as OCP E4M3 (the e4m3fn of "Enable
+    scaled FP8 (e4m3fn) KV cache on ROCm"), not as the FNUZ variant: against
+    a weight code of 1.0 (0x38), 0x7E gives 448 (FNUZ: 224), 0x7F gives NaN
+    (FNUZ: 240), a row of 0x80 gives 0 (FNUZ: NaN), 0x01 and 0x08 give 2^-9
+    and 2^-6. M = 5 runs the decode kernel, M = 100 a tile kernel."""
+    N, K = 64, 128
+    a = np.zeros((M, K), np.uint8)
+    a[0, 0] = 0x7E
+    a[1, :] = 0x80
+    a[2, 0] = 0x7F
+    a[3, 0] = 0x01
+    a[4, 0] = 0x08
+    b = np.zeros((N, K), np.uint8)
+    b[:, 0] = 0x38
+    got = _run(a, b, "fp8", None, None, "f32").cpu().numpy()
+    assert (got[0] == 448.0).all(), got[0, :4]
+    assert (got[1] == 0.0).all(), got[1, :4]
+    assert np.isnan(got[2]).all(), got[2, :4]
+    assert (got[3] == 2.0 ** -9).all() and (got[4] == 2.0 ** -6).all()
+    assert (got[5:] == 0.0).all()
+
+
 def test_tiny_int8_case_end_to_end():
     """The tiny int8 case, every step on the GPU: per-tensor dynamic int8
     quantisation of A [16,128] and W [64,128], int32 accumulate, bf16 out."""
