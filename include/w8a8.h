@@ -142,16 +142,19 @@ w8a8_status w8a8_scaled_mm(void* out, w8a8_dtype ot, int64_t ldo, const void* a,
 /*
  * Bytes of device workspace with which w8a8_scaled_mm_ws splits K for an
  * M x N x K problem (0: it would not split, and needs none). Host-only.
- * Splitting pays for decode problems with 16 < M <= 64, K >= 8192 and
- * N < 16321: 4 splits of fp32 (int32 for int8) partial sums, 16*M*N bytes.
+ * Splitting pays for decode problems with 16 < M <= 64 on weights too
+ * narrow to occupy the GPU: K >= 8192 and N < 16321, or K >= 4096 and
+ * N <= 1024. Up to 4 splits of fp32 (int32 for int8) partial sums, at most
+ * 16*M*N bytes.
  */
 int64_t w8a8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*
  * w8a8_scaled_mm with an optional caller workspace [P1: the same operation].
  * When workspace_bytes >= w8a8_scaled_mm_workspace_size(M, N, K) > 0, two to
- * four workgroups (as many as fill one round of the GPU's workgroup slots)
- * share each 64-column tile along K, write their partial sums to
+ * four workgroups share each column block along K (four per 16 columns on
+ * weights of at most 2048 rows; on wider ones as many per 64 columns as
+ * fill one round of the GPU's workgroup slots), write their partial sums to
  * the workspace, and a second kernel adds them in a fixed split order and
  * applies the scales: results are deterministic, and equal to
  * w8a8_scaled_mm's up to the fp8 summation order (bit-identical for int8).

@@ -55,6 +55,7 @@ struct GemmArgs {
     // [splits][M][N] to part; a second kernel adds them
     void* part;
     int splits, stages_per_split;
+    int split_config;  // the decode configuration that runs split
     // asymmetric int8 activations: zero points (1 or M entries) and the
     // weights' code sums; NULL azp: symmetric
     const int32_t* azp;
@@ -1062,8 +1063,7 @@ Config select_config(int64_t M, int64_t N, int64_t K) {
 
 template <int QT, int OT>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
-    if (a.splits > 1) return run_decode<QT, OT, 64, 4, 256, 2>(a, st);
-    switch (select_config(a.M, a.N, a.K)) {
+    switch (a.splits > 1 ? static_cast<Config>(a.split_config) : select_config(a.M, a.N, a.K)) {
         case kDecode64x16: return run_decode<QT, OT, 64, 1, 512, 2>(a, st);
         case kDecode64x16R: return run_decode<QT, OT, 64, 1, 256, 4>(a, st);
         case kDecode64x64: return run_decode<QT, OT, 64, 4, 256, 2>(a, st);
@@ -1098,26 +1098,46 @@ hipError_t dispatch_ot(int ot, const GemmArgs& a, hipStream_t st) {
 
 }  // namespace
 
-// Split-K for decode problems above 16 rows with a long K on weights too
-// narrow for 64-column blocks to occupy the GPU: the 64-column kernel with K
-// split so that each activation tile is read once per 64 columns instead of
-// once per 16. The split count fills one round of the kernel's workgroup
-// slots (two 64 KB workgroups per CU on 256 CUs), at most 4: measured on
-// MI355X at 64 rows, Llama-3-70B QKV (160 column blocks) 33.6 us with 4
-// splits (640 workgroups, a second partial round) against 27.0 us with 3,
-// and Llama-3-8B down 26.4 us on the long-stage 16-column kernel against
-// 24.0 us with 4 splits (24.4 us with 8). Shorter K does not repay the
-// extra pass (Llama-3-8B QKV and O at 64 rows: 14.2 -> 17.3 us, 11.6 ->
-// 14.7 us), nor do problems of at most 16 rows.
+// Split K for decode problems above 16 rows whose weights are too narrow to
+// occupy the GPU, given a workspace:
+//  - Narrow weights (at most 2048 rows, 128 sixteen-column groups) with
+//    K >= 8192, or at most 1024 rows with K >= 4096: the 16-column kernel,
+//    K split 4 ways (the 3-slot ring where each split walks at least 6 of
+//    its 512-byte stages, or at K < 8192). Measured on MI355X (one process,
+//    rotating weights), against the previous plans: 64 x 1280 x 8192 14.1
+//    -> 11.4 us, 32 x 1280 x 8192 13.1 -> 10.2, 64 x 1024 x 14336 19.4 ->
+//    11.6, 64 x 2048 x 8192 14.7 -> 12.2, 64 x 768 x 4096 8.8 -> 7.7; at K
+//    = 4096 on 1280 to 3072 rows, and at 16 rows or fewer, no split was
+//    faster.
+//  - Wider weights with K >= 8192 that still give fewer than 256 64-column
+//    blocks: the 64-column kernel, K split so that each activation tile is
+//    read once per 64 columns instead of once per 16. The split count fills
+//    one round of the kernel's workgroup slots (two 64 KB workgroups per CU
+//    on 256 CUs), at most 4: Llama-3-70B QKV at 64 rows (160 column blocks)
+//    33.6 us with 4 splits (640 workgroups, a second partial round) against
+//    27.0 us with 3, and Llama-3-8B down 26.4 us on the long-stage 16-column
+//    kernel against 24.0 us with 4 splits (24.4 us with 8). Shorter K does
+//    not repay the extra pass there (Llama-3-8B QKV and O at 64 rows: 14.2
+//    -> 17.3 us, 11.6 -> 14.7 us).
 SplitPlan plan_splitk(int64_t M, int64_t N, int64_t K) {
-    SplitPlan d{1, 0, 0};
-    const int64_t blocks = (N + 63) / 64;
-    if (M <= 16 || M > 64 || K < 8192 || blocks >= 256) return d;
-    constexpr int64_t kSlots = 512;   // resident 64-column workgroups
-    constexpr int kStageBytes = 256;  // the 64-column kernel's K stage
-    const int64_t stages = (K + kStageBytes - 1) / kStageBytes;
-    d.splits = static_cast<int>(std::min<int64_t>(kMaxSplitsK, std::max<int64_t>(2, kSlots / blocks)));
-    d.stages_per_split = static_cast<int>((stages + d.splits - 1) / d.splits);
+    SplitPlan d{1, 0, 0, kDecode64x64};
+    if (M <= 16 || M > 64) return d;
+    const int64_t groups = (N + 15) / 16, blocks = (N + 63) / 64;
+    if ((groups <= 128 && K >= 8192) || (groups <= 64 && K >= 4096)) {
+        constexpr int kStageBytes = 512;  // the 16-column kernels' K stage at up to 64 rows
+        const int64_t stages = (K + kStageBytes - 1) / kStageBytes;
+        d.splits = 4;
+        d.stages_per_split = static_cast<int>((stages + d.splits - 1) / d.splits);
+        d.config = (d.stages_per_split >= 6 || K < 8192) ? kDecode16x64R : kDecode16x64;
+    } else if (K >= 8192 && blocks < 256) {
+        constexpr int64_t kSlots = 512;   // resident 64-column workgroups
+        constexpr int kStageBytes = 256;  // the 64-column kernel's K stage
+        const int64_t stages = (K + kStageBytes - 1) / kStageBytes;
+        d.splits = static_cast<int>(std::min<int64_t>(kMaxSplitsK, std::max<int64_t>(2, kSlots / blocks)));
+        d.stages_per_split = static_cast<int>((stages + d.splits - 1) / d.splits);
+    } else {
+        return d;
+    }
     d.workspace_bytes = static_cast<int64_t>(d.splits) * M * N * 4;
     return d;
 }
@@ -1145,6 +1165,7 @@ hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st) {
     a.part = nullptr;
     a.splits = 1;
     a.stages_per_split = 0;
+    a.split_config = 0;
     a.azp = p.azp;
     a.azp_per_row = p.azp_per_row ? 1 : 0;
     a.colsum = p.colsum;
@@ -1154,6 +1175,7 @@ hipError_t launch_scaled_mm(const GemmProblem& p, hipStream_t st) {
             a.part = p.workspace;
             a.splits = d.splits;
             a.stages_per_split = d.stages_per_split;
+            a.split_config = d.config;
         }
     }
     if (p.qt == Q_FP8) return dispatch_ot<Q_FP8>(p.ot, a, st);
@@ -1282,6 +1304,7 @@ hipError_t launch_quant_scaled_mm(const GemmProblem& p, int xt, const void* x, i
     a.part = nullptr;
     a.splits = 1;
     a.stages_per_split = 0;
+    a.split_config = 0;
     const dim3 grid((p.N + 15) / 16), block(256);
 #define W8A8_DYNQ(XT_, QT_, OT_) \
     hipLaunchKernelGGL((gemm_dynq_kernel<XT_, QT_, OT_>), grid, block, 0, st, a, x, q, a_scales)
@@ -1305,7 +1328,16 @@ hipError_t launch_quant_scaled_mm(const GemmProblem& p, int xt, const void* x, i
 }
 
 const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K, bool workspace) {
-    if (workspace && plan_splitk(M, N, K).splits > 1) return "gemm_decode_kernel<64x64>+splitk_reduce_kernel";
+    if (workspace) {
+        const SplitPlan d = plan_splitk(M, N, K);
+        if (d.splits > 1) {
+            switch (d.config) {
+                case kDecode16x64: return "gemm_decode_kernel<16x64>+splitk_reduce_kernel";
+                case kDecode16x64R: return "gemm_decode_kernel<16x64,3x512>+splitk_reduce_kernel";
+                default: return "gemm_decode_kernel<64x64>+splitk_reduce_kernel";
+            }
+        }
+    }
     switch (select_config(M, N, K)) {
         case kDecode64x16: return "gemm_decode_kernel<64x16>";
         case kDecode64x16R: return "gemm_decode_kernel<64x16,4x256>";

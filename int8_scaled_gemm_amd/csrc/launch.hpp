@@ -66,11 +66,14 @@ struct GemmProblem {
     const int32_t* colsum = nullptr;
 };
 
-// How a decode problem splits K when given a workspace (splits == 1: no split).
+// How a decode problem splits K when given a workspace (splits == 1: no
+// split): the split count, the K stages each split walks, the bytes of the
+// partial sums, and the decode kernel configuration that runs split.
 struct SplitPlan {
     int splits;
     int stages_per_split;
     int64_t workspace_bytes;
+    int config;
 };
 SplitPlan plan_splitk(int64_t M, int64_t N, int64_t K);
 

@@ -210,6 +210,10 @@ def test_split_k_workspace_plan(lib):
     assert size(64, 8192, 14336) == 4 * 64 * 8192 * 4     # 128 column blocks: 4 splits
     assert size(17, 8192, 8192) == 4 * 17 * 8192 * 4
     assert size(40, 1000, 8192) == 4 * 40 * 1000 * 4      # few column blocks: at most 4 splits
+    assert size(64, 1280, 8192) == 4 * 64 * 1280 * 4      # narrow: 16-column blocks split 4 ways
+    assert size(64, 768, 4096) == 4 * 64 * 768 * 4        # at most 1024 rows: from K = 4096
+    assert size(64, 1280, 4096) == 0                       # 1280 rows at K = 4096: no split
+    assert size(16, 1280, 8192) == 0                       # at most 16 rows: no split
     assert size(64, 10240, 8192) == 3 * 64 * 10240 * 4    # 160 column blocks: 3 splits fill 512
     assert size(64, 16320, 8192) == 2 * 64 * 16320 * 4    # 255 column blocks: 2 splits
     assert size(64, 4096, 14336) == 4 * 64 * 4096 * 4     # Llama-3-8B down
@@ -222,6 +226,9 @@ def test_split_k_workspace_plan(lib):
     assert name(64, 8192, 14336) == "gemm_decode_kernel<64x64>+splitk_reduce_kernel"
     assert name(64, 4096, 4096) == lib.w8a8_scaled_mm_kernel(64, 4096, 4096).decode()
     assert name(64, 4096, 14336) == "gemm_decode_kernel<64x64>+splitk_reduce_kernel"
+    assert name(64, 1280, 8192) == "gemm_decode_kernel<16x64>+splitk_reduce_kernel"          # 4 stages each
+    assert name(64, 1024, 14336) == "gemm_decode_kernel<16x64,3x512>+splitk_reduce_kernel"   # 7 stages each
+    assert name(64, 768, 4096) == "gemm_decode_kernel<16x64,3x512>+splitk_reduce_kernel"
     assert lib.w8a8_scaled_mm_kernel(64, 4096, 14336).decode() == "gemm_decode_kernel<16x64,1K>"
     ws = lib.w8a8_scaled_mm_ws
     args = (FAKE, 0, 64, FAKE, 128, FAKE, 128, 1, 16, 64, 128, None, 1, None, 1)

@@ -111,6 +111,19 @@ def test_int8_70b_full(M, name, N, K):
     _check_layer(M, N, K, "int8", "per_token", seed=13 * M + N % 83)
 
 
+@pytest.mark.parametrize("qtype", ["int8", "fp8"])
+@pytest.mark.parametrize("name,N,K", workloads.LLAMA3_70B_TP8_LAYERS)
+@pytest.mark.parametrize("M", workloads.INT8_70B_M)
+def test_70b_tp8_shard_full(M, name, N, K, qtype):
+    """One GPU's share of the Llama-3-70B layers under 8-way tensor
+    parallelism (QKV and gate_up split along N, O and down along K, the
+    sharding of "Add async tensor parallelism for scaled mm"): the same calls
+    at the shard's shapes, where narrow weights take the split-K plans."""
+    print(f"{qtype} 70B TP8 shard M={M} {name} {N}x{K} "
+          f"{w8.w8a8_scaled_mm_kernel(M, N, K, workspace=True)}", flush=True)
+    _check_layer(M, N, K, qtype, "per_token", seed=17 * M + N % 79)
+
+
 @pytest.mark.parametrize("name,N,K", workloads.LLAMA3_70B_LAYERS)
 @pytest.mark.parametrize("M", workloads.INT8_70B_M)
 def test_int8_azp_70b_full(M, name, N, K):

@@ -332,11 +332,15 @@ def test_decode_configs_are_the_ones_named():
 
 
 # Split-K through a caller workspace: decode problems above 16 rows with a
-# long K on narrow weights (the Llama-3-8B down projection at 64 tokens,
-# ragged N and K, the widest N that still splits).
+# long K on weights too narrow to occupy the GPU. The 64-column kernel split
+# (the Llama-3-8B down projection at 64 tokens, the widest N that still
+# splits) and the 16-column ones on narrow weights (Llama-3-70B QKV on one of
+# eight GPUs, 1280 rows; 2- and 3-slot rings; K of 4096 on at most 1024
+# rows), with ragged N and K.
 SPLITK_SHAPES = [(64, 4608, 14336), (40, 1000, 8192 + 16), (17, 300, 16384), (64, 16320, 8192),
                  (64, 10240, 8192), (64, 4096, 14336),
-                 (33, 48, 9000 - 9000 % 16)]
+                 (33, 48, 9000 - 9000 % 16), (64, 1280, 8192), (33, 2000, 8192 + 16),
+                 (64, 1024, 14336), (17, 768 + 16, 4096 + 16)]
 
 
 @pytest.mark.parametrize("qtype", ["fp8", "int8"])

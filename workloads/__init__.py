@@ -33,6 +33,14 @@ LLAMA3_70B_LAYERS = (
     ("gate_up", 57344, 8192),
     ("down", 8192, 28672),
 )
+# One GPU's share of those under 8-way tensor parallelism: QKV and gate_up
+# split along N (column-parallel), O and down along K (row-parallel).
+LLAMA3_70B_TP8_LAYERS = (
+    ("qkv", 1280, 8192),
+    ("o", 8192, 1024),
+    ("gate_up", 7168, 8192),
+    ("down", 8192, 3584),
+)
 
 # The five workloads: the tiny int8 case, fp8 decode, fp8 prefill, int8 70B,
 # and the scaled fp8 KV cache plus a standalone per-token quantisation.
