@@ -1053,9 +1053,16 @@ Config select_config(int64_t M, int64_t N, int64_t K) {
     // tiles: 27.1 -> 30.5), and so they do below 192 (400 x 2048 x 8192, 128
     // tiles: 23.4 -> 27.7). Below 192 tiles of 128 x 128 there are at most
     // 768 of 64 x 64.
+    // With K >= 8192 the large tiles pay from 160 tiles (five eighths of the
+    // CUs): their longer main loops outweigh the idle CUs (measured on
+    // MI355X: 8192 x 1280 x 8192 on 256 x 256 tiles 101 us against 116 on
+    // 128 x 128; on 256 x 128, 4096 x 1280 x 8192 58 against 67, 4096 x 1280
+    // x 14336 99 against 123, 512 x 10240 x 8192 int8 59 against 74; at 120
+    // to 128 tiles 256 x 128 loses: 3072 x 1280 x 8192 56 against 41).
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (tiles(256, 256) >= 192) return kTile256x256;
-    if (tiles(256, 128) >= 256) return kTile256x128;
+    const bool long_k = K >= 8192;
+    if (tiles(256, 256) >= (long_k ? 160 : 192)) return kTile256x256;
+    if (tiles(256, 128) >= (long_k ? 160 : 256)) return kTile256x128;
     if (tiles(128, 128) >= 192) return tiles(128, 128) <= 256 ? kTile128x128R : kTile128x128;
     if (tiles(128, 64) >= 192 && tiles(128, 64) <= 256) return kTile128x64;
     return tiles(64, 64) <= 512 ? kTile64x64R4 : kTile64x64R3;
