@@ -14,8 +14,9 @@
 //  - gemm_decode_kernel (M <= 64, bound by the weight stream): 16 x 16 MFMAs
 //    (v_mfma_f32_16x16x128_f8f6f4, v_mfma_i32_16x16x64_i8) on a block of
 //    16 or 64 output columns, weights streamed once through an LDS ring;
-//    with a caller workspace and a long K, split along K, the partial sums
-//    added by splitk_reduce_kernel.
+//    above 16 rows, with a caller workspace, on weights too narrow to
+//    occupy the GPU, split along K, the partial sums added by
+//    splitk_reduce_kernel.
 //  - gemm_dynq_kernel (M == 1): the per-token quantisation of the one row
 //    and the product in one kernel.
 // Each MFMA lane holds a run of contiguous K bytes of one row of each
@@ -50,7 +51,7 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int vec_out;  // out and ldo allow 4-element vector stores
     int vec_row;  // out and ldo allow 16-byte stores
-    // split-K decode: splits > 1 workgroups per 64-column tile, each over
+    // split-K decode: splits > 1 workgroups per column block, each over
     // stages_per_split K stages, writing fp32 (int32 for int8) partial sums
     // [splits][M][N] to part; a second kernel adds them
     void* part;
