@@ -1040,30 +1040,30 @@ Config select_config(int64_t M, int64_t N, int64_t K) {
         if (M <= 16) return groups16 <= 384 ? kDecode16x16R : kDecode16x16;
         return groups16 <= 256 ? kDecode16x64R : kDecode16x64;
     }
-    // The largest tile that still gives every CU a block, else the smallest;
-    // 256 x 256 and 128 x 128 already from 192 tiles (three quarters of the
-    // CUs), where one round of the large tile beats two of the half-size one
-    // (measured on MI355X: 2048 x 6144 x 4096 52 us against 64, 512 x 28672
-    // x 4096 58 against 70, 512 x 6144 x 4096 on 128 x 128 tiles 23.2 against
-    // 28.2 on 64 x 64; at 128 tiles 64 x 64 still wins: 512 x 4096 x 4096
-    // 19.8 against 22.0). Between them, 128 x 64 tiles (eight 32 x 32 waves,
-    // a 96 KB ring: one workgroup per CU) where 192 to 256 of them fill one
-    // round: 512 x 4096 x 4096 20.2 -> 17.1 us, 512 x 4096 x 14336 63.0 ->
-    // 51.1, 300 x 4096 x 4096 18.5 -> 15.4, 128 x 16384 x 4096 27.2 -> 21.4
-    // against 64 x 64; past one round they lose (512 x 5120 x 4096, 320
-    // tiles: 27.1 -> 30.5), and so they do below 192 (400 x 2048 x 8192, 128
-    // tiles: 23.4 -> 27.7). Below 192 tiles of 128 x 128 there are at most
-    // 768 of 64 x 64.
-    // With K >= 8192 the large tiles pay from 160 tiles (five eighths of the
-    // CUs): their longer main loops outweigh the idle CUs (measured on
-    // MI355X: 8192 x 1280 x 8192 on 256 x 256 tiles 101 us against 116 on
-    // 128 x 128; on 256 x 128, 4096 x 1280 x 8192 58 against 67, 4096 x 1280
-    // x 14336 99 against 123, 512 x 10240 x 8192 int8 59 against 74; at 120
-    // to 128 tiles 256 x 128 loses: 3072 x 1280 x 8192 56 against 41).
+    // The largest tile that still gives most CUs a block (measured on
+    // MI355X, A/B in one process):
+    //  - 256 x 256, else 256 x 128, from 160 tiles (five eighths of the
+    //    CUs): one round of them beats more rounds of the next smaller tile,
+    //    their longer main loops outweighing the idle CUs. 256 x 256: 2048 x
+    //    5120 x 4096 51 us against 63 on 256 x 128, 3072 x 3584 x 4096 52
+    //    against 61, 8192 x 1280 x 8192 101 against 115. 256 x 128: 4096 x
+    //    1280 x 4096 31 against 37 on 128 x 128, 2048 x 3072 x 4096 31
+    //    against 36, 4096 x 1280 x 14336 100 against 123, 512 x 10240 x 8192
+    //    int8 59 against 73; at 120 to 128 tiles it loses (3072 x 1280 x
+    //    8192 56 against 41).
+    //  - 128 x 128 from 192 tiles (three quarters of the CUs): 512 x 6144 x
+    //    4096 23.2 us against 28.2 on 64 x 64; at 128 tiles 64 x 64 still
+    //    wins (512 x 4096 x 4096 19.8 against 22.0).
+    //  - 128 x 64 tiles (eight 32 x 32 waves, a 96 KB ring: one workgroup per
+    //    CU) where 192 to 256 of them fill one round: 512 x 4096 x 4096 20.2
+    //    -> 17.1 us, 512 x 4096 x 14336 63.0 -> 51.1, 300 x 4096 x 4096 18.5
+    //    -> 15.4, 128 x 16384 x 4096 27.2 -> 21.4 against 64 x 64; past one
+    //    round they lose (512 x 5120 x 4096, 320 tiles: 27.1 -> 30.5), and so
+    //    they do below 192 (400 x 2048 x 8192, 128 tiles: 23.4 -> 27.7).
+    //  - Else 64 x 64 (below 192 tiles of 128 x 128 there are at most 768).
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    const bool long_k = K >= 8192;
-    if (tiles(256, 256) >= (long_k ? 160 : 192)) return kTile256x256;
-    if (tiles(256, 128) >= (long_k ? 160 : 256)) return kTile256x128;
+    if (tiles(256, 256) >= 160) return kTile256x256;
+    if (tiles(256, 128) >= 160) return kTile256x128;
     if (tiles(128, 128) >= 192) return tiles(128, 128) <= 256 ? kTile128x128R : kTile128x128;
     if (tiles(128, 64) >= 192 && tiles(128, 64) <= 256) return kTile128x64;
     return tiles(64, 64) <= 512 ? kTile64x64R4 : kTile64x64R3;

@@ -173,18 +173,17 @@ def test_kernel_configuration_names(lib):
     assert name(512, 5120, 4096) == "gemm_tile_kernel<64x64,3x128>"      # 320 of 128 x 64; 640
     assert name(512, 6144, 4096) == "gemm_tile_kernel<128x128,3x128>"    # 192 of 128 x 128
     assert name(512, 7168, 4096) == "gemm_tile_kernel<128x128,3x128>"    # 224
-    # 256 x 256 from 192 tiles: one round of large tiles beats two of 256 x 128
+    # the large tiles from 160 tiles: one round of them beats more of smaller ones
     assert name(2048, 6144, 4096) == "gemm_tile_kernel<256x256>"   # 8 x 24 = 192 tiles
     assert name(512, 28672, 4096) == "gemm_tile_kernel<256x256>"   # 2 x 112 = 224 tiles
-    assert name(2048, 5888, 4096) == "gemm_tile_kernel<256x128>"   # 8 x 23 = 184 tiles
-    assert name(1024, 4096, 4096) == "gemm_tile_kernel<128x128,3x128>"   # 256 tiles
-    # K >= 8192: the large tiles from 160 tiles
+    assert name(2048, 5888, 4096) == "gemm_tile_kernel<256x256>"   # 8 x 23 = 184 tiles
     assert name(8192, 1280, 8192) == "gemm_tile_kernel<256x256>"   # 32 x 5 = 160 tiles
-    assert name(4096, 1280, 8192) == "gemm_tile_kernel<256x128>"   # 16 x 10 = 160 tiles
+    assert name(4096, 1280, 4096) == "gemm_tile_kernel<256x128>"   # 80 of 256 x 256; 160
     assert name(512, 10240, 8192) == "gemm_tile_kernel<256x128>"   # 2 x 80 = 160 tiles
-    assert name(4096, 1280, 4096) == "gemm_tile_kernel<128x128>"   # K = 4096: 160 is too few
-    assert name(3072, 1280, 8192) == "gemm_tile_kernel<128x128,3x128>"   # 120 of 256 x 128
-    assert name(1024 + 128, 4096, 4096) == "gemm_tile_kernel<128x128>"   # 288
+    assert name(1024 + 128, 4096, 4096) == "gemm_tile_kernel<256x128>"   # 5 x 32 = 160
+    assert name(1024, 4096, 4096) == "gemm_tile_kernel<128x128,3x128>"   # 128 of 256 x 128; 256
+    assert name(3072, 1280, 8192) == "gemm_tile_kernel<128x128,3x128>"   # 120 of 256 x 128; 240
+    assert name(640, 6656, 4096) == "gemm_tile_kernel<128x128>"    # 156 of 256 x 128; 260
     assert name(-1, 4, 4) == ""
 
 
