@@ -1051,20 +1051,26 @@ Config select_config(int64_t M, int64_t N, int64_t K) {
     //    against 36, 4096 x 1280 x 14336 100 against 123, 512 x 10240 x 8192
     //    int8 59 against 73; at 120 to 128 tiles it loses (3072 x 1280 x
     //    8192 56 against 41).
-    //  - 128 x 128 from 192 tiles (three quarters of the CUs): 512 x 6144 x
-    //    4096 23.2 us against 28.2 on 64 x 64; at 128 tiles 64 x 64 still
-    //    wins (512 x 4096 x 4096 19.8 against 22.0).
+    //  - Past 256 tiles of 128 x 128 (more than one round of its 3-slot
+    //    ring), 256 x 128 from 144 tiles (640 x 6656 x 4096 30.3 us against
+    //    33.3, 1152 x 3840 x 4096 30.1 against 32.4 on the 2-slot 128 x 128),
+    //    else the 2-slot 128 x 128.
+    //  - 128 x 128 (eight waves, 3 slots) from 144 tiles: 512 x 5120 x 4096
+    //    21.4 us against 27.8 on 64 x 64, 640 x 4096 x 14336 66.7 against
+    //    86.1, 512 x 4608 x 4096 21.0 against 27.1; at 120 to 128 tiles 128
+    //    x 64 wins (512 x 4096 x 4096 17.4 against 20.9).
     //  - 128 x 64 tiles (eight 32 x 32 waves, a 96 KB ring: one workgroup per
     //    CU) where 192 to 256 of them fill one round: 512 x 4096 x 4096 20.2
     //    -> 17.1 us, 512 x 4096 x 14336 63.0 -> 51.1, 300 x 4096 x 4096 18.5
     //    -> 15.4, 128 x 16384 x 4096 27.2 -> 21.4 against 64 x 64; past one
     //    round they lose (512 x 5120 x 4096, 320 tiles: 27.1 -> 30.5), and so
     //    they do below 192 (400 x 2048 x 8192, 128 tiles: 23.4 -> 27.7).
-    //  - Else 64 x 64 (below 192 tiles of 128 x 128 there are at most 768).
+    //  - Else 64 x 64 (below 144 tiles of 128 x 128 there are at most 576).
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (tiles(256, 256) >= 160) return kTile256x256;
     if (tiles(256, 128) >= 160) return kTile256x128;
-    if (tiles(128, 128) >= 192) return tiles(128, 128) <= 256 ? kTile128x128R : kTile128x128;
+    if (tiles(128, 128) > 256) return tiles(256, 128) >= 144 ? kTile256x128 : kTile128x128;
+    if (tiles(128, 128) >= 144) return kTile128x128R;
     if (tiles(128, 64) >= 192 && tiles(128, 64) <= 256) return kTile128x64;
     return tiles(64, 64) <= 512 ? kTile64x64R4 : kTile64x64R3;
 }

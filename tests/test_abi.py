@@ -170,8 +170,10 @@ def test_kernel_configuration_names(lib):
     assert name(300, 4096, 4096) == "gemm_tile_kernel<128x64,4x128>"     # 192
     assert name(128, 16384, 4096) == "gemm_tile_kernel<128x64,4x128>"    # 256
     assert name(400, 2048, 8192) == "gemm_tile_kernel<64x64,4x128>"      # 128 of 128 x 64; 224
-    assert name(512, 5120, 4096) == "gemm_tile_kernel<64x64,3x128>"      # 320 of 128 x 64; 640
+    assert name(512, 4352, 4096) == "gemm_tile_kernel<64x64,3x128>"      # 136 of 128 x 128; 272 of 128 x 64; 544
     assert name(512, 6144, 4096) == "gemm_tile_kernel<128x128,3x128>"    # 192 of 128 x 128
+    assert name(512, 5120, 4096) == "gemm_tile_kernel<128x128,3x128>"    # 160
+    assert name(512, 4608, 4096) == "gemm_tile_kernel<128x128,3x128>"    # 144
     assert name(512, 7168, 4096) == "gemm_tile_kernel<128x128,3x128>"    # 224
     # the large tiles from 160 tiles: one round of them beats more of smaller ones
     assert name(2048, 6144, 4096) == "gemm_tile_kernel<256x256>"   # 8 x 24 = 192 tiles
@@ -183,7 +185,8 @@ def test_kernel_configuration_names(lib):
     assert name(1024 + 128, 4096, 4096) == "gemm_tile_kernel<256x128>"   # 5 x 32 = 160
     assert name(1024, 4096, 4096) == "gemm_tile_kernel<128x128,3x128>"   # 128 of 256 x 128; 256
     assert name(3072, 1280, 8192) == "gemm_tile_kernel<128x128,3x128>"   # 120 of 256 x 128; 240
-    assert name(640, 6656, 4096) == "gemm_tile_kernel<128x128>"    # 156 of 256 x 128; 260
+    assert name(640, 6656, 4096) == "gemm_tile_kernel<256x128>"    # 156 of 256 x 128; 260 of 128 x 128
+    assert name(512, 8320, 4096) == "gemm_tile_kernel<128x128>"    # 130 of 256 x 128; 260 of 128 x 128
     assert name(-1, 4, 4) == ""
 
 

@@ -59,8 +59,8 @@ def test_scaled_mm_parity(qtype, M, N, K):
 # Shapes that select each block tile of the tiled kernel (256x256, 256x128,
 # 128x128 with 2 and 3 ring stages, 128x64, 64x64 with 4 and 3), with ragged
 # M, N and K tails; checked on sampled rows.
-TILE_SHAPES = [(4096 + 37, 4096 + 48, 384 + 16), (2048, 4096 + 16, 272), (640 - 3, 6656 - 16, 144),
-               (200, 300, 1040), (1024 - 3, 4096, 144), (512, 5120 + 16, 400), (512 + 3, 6144 + 16, 272),
+TILE_SHAPES = [(4096 + 37, 4096 + 48, 384 + 16), (2048, 4096 + 16, 272), (512 - 5, 8320 - 16, 144),
+               (200, 300, 1040), (1024 - 3, 4096, 144), (512, 4352 - 16, 400), (512 + 3, 6144 + 16, 272),
                (400 + 7, 3072 + 16, 1040)]
 
 
