@@ -1009,10 +1009,14 @@ enum Config {
 // twice as long (the ring then fills a CU's LDS) keeps twice the bytes in
 // flight. Measured on MI355X at 4096 x 14336: 16 -> 14.8 us (16 rows) and
 // 28.8 -> 23.6 us (64 rows); with more workgroups than CUs the lost second
-// workgroup per CU costs more than it gains.
-bool long_k_16(int64_t N, int64_t K) {
+// workgroup per CU costs more than it gains. At up to 16 rows it pays on
+// narrower weights too (A/B in one process: 1 x 1280 x 8192 7.4 -> 6.7 us,
+// 1 x 2048 x 8192 8.9 -> 7.3, 1 x 1024 x 14336 10.3 -> 9.0, 16 x 2048 x
+// 8192 9.3 -> 8.8); above 16 rows, 128 groups or fewer keep the 3-slot
+// ring of 512-byte stages (or split K, given a workspace).
+bool long_k_16(int64_t M, int64_t N, int64_t K) {
     const int64_t groups = (N + 15) / 16;
-    return K >= 8192 && groups > 128 && groups <= 256;
+    return K >= 8192 && groups <= 256 && (M <= 16 || groups > 128);
 }
 
 // Ring depth: the direct loads of later stages stay in flight across the
@@ -1036,7 +1040,7 @@ Config select_config(int64_t M, int64_t N, int64_t K) {
             if (M > 16) return kDecode64x64;
             return blocks64 <= 512 ? kDecode64x16R : kDecode64x16;
         }
-        if (long_k_16(N, K)) return M <= 16 ? kDecode16x16L : kDecode16x64L;
+        if (long_k_16(M, N, K)) return M <= 16 ? kDecode16x16L : kDecode16x64L;
         if (M <= 16) return groups16 <= 384 ? kDecode16x16R : kDecode16x16;
         return groups16 <= 256 ? kDecode16x64R : kDecode16x64;
     }

@@ -163,6 +163,10 @@ def test_kernel_configuration_names(lib):
     assert name(17, 28672, 4096) == "gemm_decode_kernel<64x64>"
     assert name(16, 4096, 14336) == "gemm_decode_kernel<16x16,4x1K>"
     assert name(16, 6144, 14336) == "gemm_decode_kernel<16x16,4x512>"  # more workgroups than CUs
+    assert name(1, 1280, 8192) == "gemm_decode_kernel<16x16,4x1K>"     # 80 groups, long K
+    assert name(16, 2048, 8192) == "gemm_decode_kernel<16x16,4x1K>"    # 128 groups
+    assert name(1, 768, 4096) == "gemm_decode_kernel<16x16,4x512>"     # K < 8192
+    assert name(64, 1280, 8192) == "gemm_decode_kernel<16x64,3x512>"   # above 16 rows: 80 groups keep it
     assert name(8192, 28672, 4096) == "gemm_tile_kernel<256x256>"
     assert name(2048, 4096, 4096) == "gemm_tile_kernel<256x128>"
     # 128 x 64 where 192 to 256 of them fill one round, else 64 x 64
