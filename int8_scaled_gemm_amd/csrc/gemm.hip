@@ -1001,8 +1001,7 @@ enum Config {
     kTile128x128,    // gemm_tile_kernel 128 x 128, 4 waves, 2 stages
     kTile128x128R,   // gemm_tile_kernel 128 x 128, 8 waves, 3 stages (4 waves: 5% slower)
     kTile128x64,     // gemm_tile_kernel 128 x 64, 8 waves, 4 stages
-    kTile64x64R3,    // gemm_tile_kernel 64 x 64, 4 waves, 3 stages
-    kTile64x64R4,    // the same, 4 stages
+    kTile64x64,      // gemm_tile_kernel 64 x 64, 4 waves, 4 stages
 };
 
 // 16-column workgroups on a long K that fill at most one per CU: a stage
@@ -1059,24 +1058,26 @@ Config select_config(int64_t M, int64_t N, int64_t K) {
     //    ring), 256 x 128 from 144 tiles (640 x 6656 x 4096 30.3 us against
     //    33.3, 1152 x 3840 x 4096 30.1 against 32.4 on the 2-slot 128 x 128),
     //    else the 2-slot 128 x 128.
-    //  - 128 x 128 (eight waves, 3 slots) from 144 tiles: 512 x 5120 x 4096
-    //    21.4 us against 27.8 on 64 x 64, 640 x 4096 x 14336 66.7 against
-    //    86.1, 512 x 4608 x 4096 21.0 against 27.1; at 120 to 128 tiles 128
-    //    x 64 wins (512 x 4096 x 4096 17.4 against 20.9).
     //  - 128 x 64 tiles (eight 32 x 32 waves, a 96 KB ring: one workgroup per
     //    CU) where 192 to 256 of them fill one round: 512 x 4096 x 4096 20.2
     //    -> 17.1 us, 512 x 4096 x 14336 63.0 -> 51.1, 300 x 4096 x 4096 18.5
-    //    -> 15.4, 128 x 16384 x 4096 27.2 -> 21.4 against 64 x 64; past one
-    //    round they lose (512 x 5120 x 4096, 320 tiles: 27.1 -> 30.5), and so
-    //    they do below 192 (400 x 2048 x 8192, 128 tiles: 23.4 -> 27.7).
-    //  - Else 64 x 64 (below 144 tiles of 128 x 128 there are at most 576).
+    //    -> 15.4, 128 x 16384 x 4096 27.2 -> 21.4 against 64 x 64, and 17.4
+    //    against 20.9 on 128 x 128 at 512 x 4096 x 4096; past one round they
+    //    lose (512 x 5120 x 4096, 320 tiles: 27.1 -> 30.5), and so they do
+    //    below 192 (400 x 2048 x 8192, 128 tiles: 23.4 -> 27.7).
+    //  - Else 128 x 128 (eight waves, 3 slots) from 128 tiles: against 64 x
+    //    64, 512 x 5120 x 4096 21.4 us against 27.8, 640 x 4096 x 14336 66.7
+    //    against 86.1, 512 x 4352 x 4096 (136 tiles) 21.1 against 24.6, 256 x
+    //    8704 x 4096 22.7 against 29.0.
+    //  - Else 64 x 64: below 128 tiles of 128 x 128 there are at most 508,
+    //    one round of the 4-slot ring's resident workgroups.
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (tiles(256, 256) >= 160) return kTile256x256;
     if (tiles(256, 128) >= 160) return kTile256x128;
     if (tiles(128, 128) > 256) return tiles(256, 128) >= 144 ? kTile256x128 : kTile128x128;
-    if (tiles(128, 128) >= 144) return kTile128x128R;
     if (tiles(128, 64) >= 192 && tiles(128, 64) <= 256) return kTile128x64;
-    return tiles(64, 64) <= 512 ? kTile64x64R4 : kTile64x64R3;
+    if (tiles(128, 128) >= 128) return kTile128x128R;
+    return kTile64x64;
 }
 
 template <int QT, int OT>
@@ -1096,8 +1097,7 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
         case kTile128x128: return run_tile<QT, OT, 128, 128, 2, 2, 2>(a, st);
         case kTile128x128R: return run_tile<QT, OT, 128, 128, 2, 4, 3>(a, st);
         case kTile128x64: return run_tile<QT, OT, 128, 64, 4, 2, 4>(a, st);
-        case kTile64x64R3: return run_tile<QT, OT, 64, 64, 2, 2, 3>(a, st);
-        case kTile64x64R4: return run_tile<QT, OT, 64, 64, 2, 2, 4>(a, st);
+        case kTile64x64: return run_tile<QT, OT, 64, 64, 2, 2, 4>(a, st);
     }
     return hipErrorInvalidValue;  // not reached: select_config returns one of the above
 }
@@ -1371,8 +1371,7 @@ const char* scaled_mm_kernel_name(int64_t M, int64_t N, int64_t K, bool workspac
         case kTile128x128: return "gemm_tile_kernel<128x128>";
         case kTile128x128R: return "gemm_tile_kernel<128x128,3x128>";
         case kTile128x64: return "gemm_tile_kernel<128x64,4x128>";
-        case kTile64x64R3: return "gemm_tile_kernel<64x64,3x128>";
-        case kTile64x64R4: return "gemm_tile_kernel<64x64,4x128>";
+        case kTile64x64: return "gemm_tile_kernel<64x64,4x128>";
     }
     return "";  // not reached
 }

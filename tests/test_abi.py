@@ -174,7 +174,7 @@ def test_kernel_configuration_names(lib):
     assert name(300, 4096, 4096) == "gemm_tile_kernel<128x64,4x128>"     # 192
     assert name(128, 16384, 4096) == "gemm_tile_kernel<128x64,4x128>"    # 256
     assert name(400, 2048, 8192) == "gemm_tile_kernel<64x64,4x128>"      # 128 of 128 x 64; 224
-    assert name(512, 4352, 4096) == "gemm_tile_kernel<64x64,3x128>"      # 136 of 128 x 128; 272 of 128 x 64; 544
+    assert name(512, 4352, 4096) == "gemm_tile_kernel<128x128,3x128>"    # 136 of 128 x 128; 272 of 128 x 64
     assert name(512, 6144, 4096) == "gemm_tile_kernel<128x128,3x128>"    # 192 of 128 x 128
     assert name(512, 5120, 4096) == "gemm_tile_kernel<128x128,3x128>"    # 160
     assert name(512, 4608, 4096) == "gemm_tile_kernel<128x128,3x128>"    # 144
